@@ -1,0 +1,338 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module serves both sides of every parity check (the fp64 oracle and the
+GPU library), so it holds none of the method's arithmetic: only seeded draws,
+16-bit casts (round to nearest even) and layout packing.  Every generator uses
+``numpy.random.Generator(PCG64(seed))`` with a fixed draw order, listed in its
+docstring.  Normal draws are ``standard_normal(dtype=float32)`` then scaled and
+cast.
+
+Workload shapes:
+  * ``dense_small``  -- batch 1, 8 query heads on 2 KV heads, context 1024.
+  * ``ragged_llama`` -- Llama3-8B decode layer (32 Qh / 8 KVh, D 128), batch 16,
+    lengths uniform in [16384, 32768], K with per-channel LogNormal(0, 0.5)
+    outlier scales, ragged packing with cu_seqlens.
+  * ``paged_mha``    -- Llama-2-7B MHA layer (32 heads), batch 1024, LogNormal
+    lengths (median 1024, sigma 1) clipped to [128, 4096], 16-token pages in a
+    shuffled pool with a per-sequence block table.
+  * ``clo_hybrid``   -- CLO head-wise cache at 128K (Llama3-8B 32/8 or
+    Qwen2.5-14B 40/8), batch 4: labels, queries near their labels, Beta(0.5, 2)
+    importances, 2 persistent heads, a 10% token selection per buffer head.
+  * ``kvpr_layer``   -- KVPR OPT-13B layer: h 5120, 40 heads, batch 32,
+    s' 1024, split l 256, bf16 X and W, fp16 resident cache rows.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+D_HEAD = 128
+_BLOCK = 1 << 24  # values per draw block (keeps float32 temporaries small)
+
+POISON_F16 = np.float16(1000.0)
+
+
+def rng_for(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal_f16(rng, shape, scale=None):
+    """N(0,1) draws (float32), optionally times a broadcast scale, cast to fp16.
+
+    Drawn block by block in C order; the stream is the same as one big draw.
+    ``scale`` must broadcast against the trailing dims of ``shape``.
+    """
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, np.float16)
+    period, sc_row = 1, None
+    if scale is not None:
+        sc = np.asarray(scale, np.float32)
+        # the scale covers the trailing dims: one row of `period` values
+        sc_row = np.broadcast_to(sc, shape[len(shape) - sc.ndim:]).reshape(-1)
+        period = sc_row.size
+    step = max(period, (_BLOCK // period) * period)
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        blk = rng.standard_normal(hi - lo, dtype=np.float32)
+        if sc_row is not None:
+            blk = (blk.reshape(-1, period) * sc_row[None, :]).reshape(-1)
+        out[lo:hi] = blk.astype(np.float16)
+    return out.reshape(shape)
+
+
+def f32_to_bf16_bits(a):
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounding = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng, shape, std=1.0):
+    """N(0, std^2) draws (float32) cast to bfloat16 bit patterns (uint16)."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16)
+    for lo in range(0, n, _BLOCK):
+        hi = min(n, lo + _BLOCK)
+        blk = rng.standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            blk = blk * np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(blk)
+    return out.reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# Decode attention workloads
+# ---------------------------------------------------------------------------
+
+def dense_small(seed=0, B=1, Hq=8, Hkv=2, S=1024, D=D_HEAD, seqlens=None):
+    """Dense KV [B, S, Hkv, D].  Draw order: q, K, V (all N(0,1) -> fp16)."""
+    rng = rng_for(seed)
+    q = normal_f16(rng, (B, Hq, D))
+    k = normal_f16(rng, (B, S, Hkv, D))
+    v = normal_f16(rng, (B, S, Hkv, D))
+    return dict(layout="dense", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, q=q, k=k, v=v,
+                seqlens=None if seqlens is None else np.asarray(seqlens, np.int32),
+                scale=1.0 / math.sqrt(D))
+
+
+def ragged_llama(seed=0, B=16, lo=16384, hi=32768, Hq=32, Hkv=8, D=D_HEAD, lens=None,
+                 outlier_sigma=0.5):
+    """Ragged KV [T, Hkv, D] + cu_seqlens.
+
+    Draw order: lengths ~ U{lo..hi} (unless given); per-(KV head, channel) K
+    outlier scale ~ LogNormal(0, outlier_sigma), shared by all tokens and
+    sequences; K = N(0,1) * scale; V ~ N(0,1); q ~ N(0,1).
+    """
+    rng = rng_for(seed)
+    if lens is None:
+        lens = rng.integers(lo, hi + 1, size=B)
+    lens = np.asarray(lens, np.int64)
+    B = int(lens.size)
+    sigma = rng.lognormal(0.0, outlier_sigma, size=(Hkv, D)).astype(np.float32)
+    T = int(lens.sum())
+    k = normal_f16(rng, (T, Hkv, D), scale=sigma)
+    v = normal_f16(rng, (T, Hkv, D))
+    q = normal_f16(rng, (B, Hq, D))
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    return dict(layout="ragged", B=B, Hq=Hq, Hkv=Hkv, D=D, q=q, k=k, v=v, cu_seqlens=cu,
+                seqlens=lens.astype(np.int32), max_seqlen=int(lens.max()) if B else 0,
+                scale=1.0 / math.sqrt(D))
+
+
+def lognormal_lengths(rng, B, median=1024, sigma=1.0, lo=128, hi=4096):
+    z = rng.standard_normal(B)
+    return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
+
+
+def paged_mha(seed=0, B=1024, H=32, Hkv=None, D=D_HEAD, page=16, max_pages=256, median=1024,
+              sigma=1.0, lo=128, hi=4096, lens=None):
+    """Paged KV pool [P, Hkv, page, D] + block_table [B, max_pages] (-1 padded).
+
+    Draw order: lengths (LogNormal, median/sigma, clipped) unless given; page
+    permutation of the P = sum ceil(len/page) pages; pool K; pool V; q.  Slots
+    past the end of a sequence's last page hold the poison value 1000.0.
+    """
+    rng = rng_for(seed)
+    Hkv = H if Hkv is None else Hkv
+    if lens is None:
+        lens = lognormal_lengths(rng, B, median, sigma, lo, hi)
+    lens = np.asarray(lens, np.int64)
+    B = int(lens.size)
+    npg = (lens + page - 1) // page
+    if int(npg.max(initial=0)) > max_pages:
+        raise ValueError("a sequence needs more pages than max_pages")
+    P = int(npg.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    bt = np.full((B, max_pages), -1, np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, : npg[b]] = perm[off: off + npg[b]]
+        off += int(npg[b])
+    k = normal_f16(rng, (P, Hkv, page, D))
+    v = normal_f16(rng, (P, Hkv, page, D))
+    q = normal_f16(rng, (B, H, D))
+    for b in range(B):
+        tail = int(lens[b] % page)
+        if tail and npg[b]:
+            last = bt[b, npg[b] - 1]
+            k[last, :, tail:, :] = POISON_F16
+            v[last, :, tail:, :] = POISON_F16
+    return dict(layout="paged", B=B, Hq=H, Hkv=Hkv, D=D, q=q, k=k, v=v, block_table=bt,
+                seqlens=lens.astype(np.int32), page=page, max_pages=max_pages,
+                max_seqlen=int(lens.max()) if B else 0, scale=1.0 / math.sqrt(D))
+
+
+# --- layout packing helpers (no arithmetic) --------------------------------
+
+def paged_to_ragged(d):
+    """Gather a paged workload into the ragged layout (same logical tokens)."""
+    page, bt, lens = d["page"], d["block_table"], d["seqlens"]
+    parts_k, parts_v = [], []
+    for b in range(d["B"]):
+        n = int(lens[b])
+        npg = (n + page - 1) // page
+        pk = d["k"][bt[b, :npg]].transpose(0, 2, 1, 3).reshape(npg * page, d["Hkv"], d["D"])
+        pv = d["v"][bt[b, :npg]].transpose(0, 2, 1, 3).reshape(npg * page, d["Hkv"], d["D"])
+        parts_k.append(pk[:n]); parts_v.append(pv[:n])
+    cu = np.zeros(d["B"] + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    return dict(d, layout="ragged", k=np.ascontiguousarray(np.concatenate(parts_k)),
+                v=np.ascontiguousarray(np.concatenate(parts_v)), cu_seqlens=cu)
+
+
+def ragged_to_dense(d, S=None):
+    """Scatter a ragged workload into dense [B, S, Hkv, D] (padding rows = poison)."""
+    lens = d["seqlens"]
+    S = int(lens.max()) if S is None else S
+    shape = (d["B"], S, d["Hkv"], d["D"])
+    k = np.full(shape, POISON_F16, np.float16)
+    v = np.full(shape, POISON_F16, np.float16)
+    cu = d["cu_seqlens"]
+    for b in range(d["B"]):
+        n = int(lens[b])
+        k[b, :n] = d["k"][cu[b]: cu[b] + n]
+        v[b, :n] = d["v"][cu[b]: cu[b] + n]
+    return dict(d, layout="dense", k=k, v=v, S=S)
+
+
+def ragged_to_paged(d, seed=0, page=16, max_pages=None):
+    """Scatter a ragged workload into a shuffled page pool (draw: permutation)."""
+    rng = rng_for(seed)
+    lens = np.asarray(d["seqlens"], np.int64)
+    npg = (lens + page - 1) // page
+    max_pages = int(npg.max(initial=1)) if max_pages is None else max_pages
+    P = int(npg.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    bt = np.full((d["B"], max_pages), -1, np.int32)
+    k = np.full((P, d["Hkv"], page, d["D"]), POISON_F16, np.float16)
+    v = np.full_like(k, POISON_F16)
+    off = 0
+    cu = d["cu_seqlens"]
+    for b in range(d["B"]):
+        bt[b, : npg[b]] = perm[off: off + npg[b]]
+        off += int(npg[b])
+        for t0 in range(0, int(lens[b]), page):
+            n = min(page, int(lens[b]) - t0)
+            p = bt[b, t0 // page]
+            k[p, :, :n] = d["k"][cu[b] + t0: cu[b] + t0 + n].transpose(1, 0, 2)
+            v[p, :, :n] = d["v"][cu[b] + t0: cu[b] + t0 + n].transpose(1, 0, 2)
+    return dict(d, layout="paged", k=k, v=v, block_table=bt, page=page, max_pages=max_pages)
+
+
+# ---------------------------------------------------------------------------
+# CLO head-wise cache workload
+# ---------------------------------------------------------------------------
+
+CLO_MODELS = {"llama3-8b": (32, 8), "qwen2.5-14b": (40, 8)}
+
+
+def clo_queries(seed=0, model="llama3-8b", B=4, D=D_HEAD):
+    """Labels, queries near them, and importances for the head-wise cache.
+
+    Draw order: importance s_j ~ Beta(0.5, 2) per query head; labels ~ N(0, I);
+    per-(b, j) noise scale ~ U[2.96, 6.75]; noise ~ N(0, I).  The query is
+    0.9 * label + 0.1 * scale * noise, normalised to unit length, cast to fp16.
+    The noise scale band puts the label/query cosines near 0.80-0.95.
+    """
+    Hq, Hkv = CLO_MODELS[model]
+    rng = rng_for(seed)
+    s = rng.beta(0.5, 2.0, size=Hq)
+    lab32 = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    sig = rng.uniform(2.96, 6.75, size=(B, Hq)).astype(np.float32)
+    noise = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    q32 = np.float32(0.9) * lab32 + np.float32(0.1) * sig[..., None] * noise
+    q32 /= np.linalg.norm(q32, axis=-1, keepdims=True)
+    return dict(model=model, B=B, Hq=Hq, Hkv=Hkv, D=D, s=s, weights=s.astype(np.float32),
+                labels=lab32.astype(np.float16), q=q32.astype(np.float16), eta=0.8, n_exp=3.0)
+
+
+def group_importance(s, Hkv):
+    """Per-KV-head importance: the largest importance among its query heads."""
+    s = np.asarray(s)
+    return s.reshape(Hkv, -1).max(axis=1)
+
+
+def persistent_heads(s, Hkv, n_pers=2):
+    """Head map: the n_pers KV heads of largest group importance (ties -> lower
+    index) get persistent slots 0.. in ascending head order; others -1."""
+    sg = group_importance(s, Hkv)
+    top = np.sort(np.argsort(-sg, kind="stable")[:n_pers])
+    hm = np.full(Hkv, -1, np.int32)
+    hm[top] = np.arange(len(top), dtype=np.int32)
+    return hm
+
+
+def clo_hybrid(seed=0, model="llama3-8b", B=4, S=131072, frac=0.1, n_pers=2, D=D_HEAD):
+    """CLO cache buffer + persistent cache inputs.
+
+    Draw order: the ``clo_queries`` draws (stream ``seed``); then, from a second
+    stream seeded ``seed + 1000003``, full K and V [B, Hkv, S, D] ~ N(0,1) and,
+    per (b, buffer head) in ascending order, a sorted random selection of
+    round(frac * S) token indices without replacement.
+    Persistent heads copy their full KV into slot arrays; buffer heads copy the
+    selected rows, compacted in ascending token order.
+    """
+    base = clo_queries(seed, model, B, D)
+    Hq, Hkv = base["Hq"], base["Hkv"]
+    rng = rng_for(seed + 1_000_003)
+    kf = normal_f16(rng, (B, Hkv, S, D))
+    vf = normal_f16(rng, (B, Hkv, S, D))
+    hm = persistent_heads(base["s"], Hkv, n_pers)
+    ksel = int(round(frac * S))
+    P_slots = int((hm >= 0).sum())
+    pers_k = np.zeros((B, max(P_slots, 1), S, D), np.float16)
+    pers_v = np.zeros_like(pers_k)
+    buf_k = np.zeros((B, Hkv, ksel, D), np.float16)
+    buf_v = np.zeros_like(buf_k)
+    buf_len = np.zeros(B * Hkv, np.int32)
+    sel = {}
+    for b in range(B):
+        for g in range(Hkv):
+            if hm[g] >= 0:
+                pers_k[b, hm[g]] = kf[b, g]
+                pers_v[b, hm[g]] = vf[b, g]
+            else:
+                idx = np.sort(rng.choice(S, size=ksel, replace=False))
+                sel[(b, g)] = idx
+                buf_k[b, g] = kf[b, g, idx]
+                buf_v[b, g] = vf[b, g, idx]
+                buf_len[b * Hkv + g] = ksel
+    return dict(base, S=S, k_full=kf, v_full=vf, head_map=hm, pers_k=pers_k, pers_v=pers_v,
+                pers_len=np.full(B, S, np.int32), buf_k=buf_k, buf_v=buf_v, buf_len=buf_len,
+                selection=sel, ksel=ksel, scale=1.0 / math.sqrt(D))
+
+
+# ---------------------------------------------------------------------------
+# KVPR partial-recompute workload
+# ---------------------------------------------------------------------------
+
+def kvpr_layer(seed=0, b=32, h=5120, H=40, s=1024, l=256):
+    """OPT-13B-shaped layer for partial recompute + attention.
+
+    Draw order: X [b, l, h] ~ N(0,1) (bf16); W_K, W_V [h, h] ~ N(0, 1/h) (bf16);
+    resident cache rows K[:, l:s], V[:, l:s] ~ N(0,1) (fp16); q [b, H, h/H] (fp16).
+    Cache rows [0, l) start as the poison value 1000.0 (the recompute fills them).
+    """
+    D = h // H
+    rng = rng_for(seed)
+    x = normal_bf16(rng, (b, l, h))
+    std = 1.0 / math.sqrt(h)
+    wk = normal_bf16(rng, (h, h), std)
+    wv = normal_bf16(rng, (h, h), std)
+    kc = np.empty((b, s, H, D), np.float16)
+    vc = np.empty((b, s, H, D), np.float16)
+    kc[:, :l] = POISON_F16
+    vc[:, :l] = POISON_F16
+    kc[:, l:] = normal_f16(rng, (b, s - l, H, D))
+    vc[:, l:] = normal_f16(rng, (b, s - l, H, D))
+    q = normal_f16(rng, (b, H, D))
+    return dict(b=b, h=h, H=H, D=D, s=s, l=l, x=x, w_k=wk, w_v=wv, k_cache=kc, v_cache=vc,
+                q=q, scale=1.0 / math.sqrt(D))
