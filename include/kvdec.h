@@ -1,0 +1,207 @@
+/*
+ * kvdec.h -- libkvdec, long-KV-cache decode kernels for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every pointer is a DEVICE pointer
+ * unless its comment says (host).  Every compute call is asynchronous on the
+ * given HIP stream and returns after enqueueing.
+ *
+ * Ownership: the caller owns and allocates every buffer, including the
+ * workspaces whose sizes the *_workspace queries return.  Compute calls never
+ * allocate, free, synchronise or create streams.  Buffers documented as
+ * in/out (labels, k_cache, v_cache) are updated in place.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued.  On
+ * a bad argument nothing is launched, the call returns a non-zero status and
+ * kvdec_last_error() describes it (thread-local).  A failed launch returns
+ * KVDEC_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  No call throws.
+ *
+ * Thread safety: calls may be made from several threads.  Two calls that share
+ * a workspace must not run concurrently (they use it as scratch).
+ *
+ * Element types: KVDEC_F16 = IEEE binary16, KVDEC_BF16 = bfloat16.  All
+ * accumulation is fp32; 16-bit outputs are rounded to nearest even once.
+ */
+#ifndef KVDEC_H
+#define KVDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVDEC_ABI_VERSION 1
+
+typedef enum {
+  KVDEC_OK = 0,
+  KVDEC_ERR_INVALID = 1,     /* a null pointer, a negative size, inconsistent shapes */
+  KVDEC_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim != 128) */
+  KVDEC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query said */
+  KVDEC_ERR_HIP = 4          /* a HIP runtime call failed */
+} kvdec_status;
+
+typedef enum { KVDEC_F16 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
+typedef enum { KVDEC_DENSE = 0, KVDEC_RAGGED = 1, KVDEC_PAGED = 2 } kvdec_layout;
+
+/*
+ * Decode attention descriptor.
+ *
+ * The operation (KVPR page, section A3, MHA equation, at the decode step where
+ * each sequence contributes one query token; Neo page, method details, for the
+ * paged pool and the split-then-aggregate parallelisation of one request):
+ *
+ *   for every sequence b and query head j, with KV head g = j / (Hq / Hkv):
+ *     s_t   = softmax_scale * q[b, j, :] . K_g[b, t, :]      t < len_b
+ *     out[b, j, :] = sum_t softmax(s)_t * V_g[b, t, :]
+ *     lse[b, j]    = ln sum_t exp(s_t)          (natural log; -inf if len_b = 0)
+ *
+ * An empty sequence (len_b = 0) gives out = 0 and lse = -inf.
+ *
+ * Fields:
+ *   batch          B >= 0
+ *   num_q_heads    Hq >= 1; num_kv_heads Hkv >= 1; Hq % Hkv == 0; Hq / Hkv <= 8
+ *   head_dim       must be 128
+ *   softmax_scale  any finite value (1/sqrt(head_dim) in the usual case)
+ *   dtype          kvdec_dtype of q, K, V and out
+ *   layout         kvdec_layout (below)
+ *   max_seqlen     DENSE: the allocated token count S of each sequence (the
+ *                  row stride); RAGGED / PAGED: an upper bound on every len_b.
+ *                  It sizes the grid and the workspace; lengths above it are
+ *                  an error the kernel cannot report (they are clamped).
+ *   page_size      PAGED only: tokens per page, a multiple of 16
+ *   max_pages_per_seq PAGED only: row stride of block_table
+ *   split_tokens   0 = the library chooses how many tokens one work item
+ *                  covers; otherwise that count (a multiple of 64).
+ *   kv_rows        RAGGED: the token rows T in k and v; PAGED: the pages P in
+ *                  the pool; DENSE: ignored.  The kernel clamps cu_seqlens into
+ *                  [0, T] and page ids into [0, P), so malformed metadata reads
+ *                  wrong rows instead of faulting.
+ */
+typedef struct {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  float softmax_scale;
+  int32_t dtype;
+  int32_t layout;
+  int32_t max_seqlen;
+  int32_t page_size, max_pages_per_seq;
+  int32_t split_tokens;
+  int64_t kv_rows;
+} kvdec_attn_desc;
+
+/* Workspace bytes kvdec_decode_attn needs for this descriptor (0 when every
+ * sequence fits one work item).  The workspace holds the per-call partial
+ * results of the split work items; its contents need no initialisation and
+ * are dead after the call's kernels finish. */
+kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* desc, size_t* bytes /*(host)*/);
+
+/*
+ * Decode attention.
+ *   q   [B, Hq, 128]; out [B, Hq, 128] (dtype); lse [B, Hq] fp32 (may be NULL)
+ *   DENSE : k, v [B, max_seqlen, Hkv, 128]; seqlens [B] int32 (NULL => all max_seqlen)
+ *   RAGGED: k, v [T, Hkv, 128] packed by sequence; cu_seqlens [B+1] int32,
+ *           cu_seqlens[0] = 0, nondecreasing; seqlens ignored
+ *   PAGED : k, v [P, Hkv, page_size, 128]; block_table [B, max_pages_per_seq]
+ *           int32 page ids in [0, P); seqlens [B] int32 (required).  Token t of
+ *           sequence b is slot t % page_size of page block_table[b][t / page_size].
+ *           Slots past a sequence's end and table entries past its last page
+ *           are never read.
+ *   workspace / ws_bytes: see kvdec_decode_attn_workspace.
+ */
+kvdec_status kvdec_decode_attn(const kvdec_attn_desc* desc, const void* q, const void* k,
+                               const void* v, const int32_t* seqlens, const int32_t* cu_seqlens,
+                               const int32_t* block_table, void* out, float* lse,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * CLO cache buffer + persistent cache attention (CLO page, section 7: the
+ * hybrid attention kernel reads both buffers in place, with no gather into one
+ * buffer; section 2: hard-to-reuse heads keep their full KV resident).
+ *
+ * base: batch, heads, head_dim, softmax_scale, dtype, split_tokens as for
+ * kvdec_attn_desc (layout, max_seqlen, page fields are ignored).
+ *   pers_k, pers_v [B, num_pers_slots, pers_cap, 128]; pers_len [B] int32
+ *   buf_k,  buf_v  [B, Hkv, buf_cap, 128];             buf_len [B * Hkv] int32
+ *   head_map [Hkv] int32: slot >= 0 reads persistent slot `slot` (rows
+ *   0..pers_len[b]-1), -1 reads the cache buffer of that KV head (rows
+ *   0..buf_len[b*Hkv+g]-1, the selected tokens compacted in any order).
+ * The result for each KV head equals kvdec_decode_attn over the rows it reads.
+ */
+typedef struct {
+  kvdec_attn_desc base;
+  int32_t num_pers_slots, pers_cap, buf_cap;
+} kvdec_hybrid_desc;
+
+kvdec_status kvdec_sparse_hybrid_attn_workspace(const kvdec_hybrid_desc* desc,
+                                                size_t* bytes /*(host)*/);
+kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* desc, const void* q,
+                                      const void* pers_k, const void* pers_v,
+                                      const int32_t* pers_len, const void* buf_k,
+                                      const void* buf_v, const int32_t* buf_len,
+                                      const int32_t* head_map, void* out, float* lse,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * CLO head-wise approximate cache lookup fused with the query-label update
+ * (CLO page, section 2: one query label per head, hit iff the cosine to the
+ * label reaches tau, else the whole head is replaced; Eq. 10: a KV head's
+ * cosine is the importance-weighted mean over its query heads; section 7: the
+ * lookup and the label update share one read of q and the labels).
+ *
+ * For each sequence b and KV head g (query heads j = g*G .. g*G+G-1):
+ *   c[b,j]   = q[b,j].label[b,j] / (|q[b,j]| |label[b,j]|)           (fp32)
+ *   agg[b,g] = sum_j w[j] c[b,j] / sum_j w[j]    (unweighted mean if sum w = 0)
+ *   hit[b,g] = agg[b,g] >= tau[g]; a group holding a zero-norm q or label misses
+ *   on a miss: label[b,j] <- q[b,j] (bit copy) for every j of the group
+ *   miss_list: the b*Hkv+g of every miss in ascending order; miss_count: their number
+ *
+ *   q, labels [B, Hq, D] (dtype; labels in/out); weights [Hq] fp32; tau [Hkv] fp32
+ *   hit [B*Hkv] uint8; agg [B*Hkv] fp32, cos [B*Hq] fp32, miss_list [B*Hkv]
+ *   int32, miss_count [1] int32 -- all four may be NULL (miss_list and
+ *   miss_count together).  D must be 128.  Hq % Hkv == 0, Hq / Hkv <= 16.
+ */
+kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                    const void* q, void* labels, const float* weights,
+                                    const float* tau, uint8_t* hit, float* agg, float* cos,
+                                    int32_t* miss_list, int32_t* miss_count, hipStream_t stream);
+
+/*
+ * CLO threshold chain, Eqs. 7-9 (host only, fp64, rounded to fp32 once):
+ *   theta* = arccos(eta); lambda_i = s_i^n_exp;
+ *   tau_i = cos(lambda_i theta* + (1 - lambda_i) pi).
+ * s: n importance scores in [0, 1] (host); tau: n outputs (host).
+ * eta in [-1, 1]; n_exp > 0.
+ */
+kvdec_status kvdec_headcache_thresholds(int32_t n, const float* s /*(host)*/, double eta,
+                                        double n_exp, float* tau /*(host)*/);
+
+/*
+ * KVPR partial recompute (KVPR page, section A2: K[0:l] = X[0:l] W_K,
+ * V[0:l] = X[0:l] W_V with W in R^{h x h}; the recomputed rows join the rows
+ * already resident before attention runs over [0, s')).
+ *
+ *   x        [b, *, h] bf16, row t of batch i at x + i*x_batch_stride + t*h (elements)
+ *   w_k, w_v [h, h] bf16 row-major, input index first (the product is x . W)
+ *   k_cache, v_cache [b, s_cap, H, head_dim] fp16 with h = H * head_dim; batch i
+ *            starts cache_batch_stride elements after batch i-1.  Rows [0, l)
+ *            are overwritten with fp16(x . W) (fp32 accumulation, one rounding);
+ *            every other byte is left untouched.
+ *   Requires l >= 0, b >= 0, head_dim == 128, h % 256 == 0 (covers the 40-head
+ *   OPT-13B width 5120), x_batch_stride >= l*h, cache_batch_stride >= l*h.
+ */
+kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_heads,
+                                int32_t head_dim, const void* x, int64_t x_batch_stride,
+                                const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                                int64_t cache_batch_stride, hipStream_t stream);
+
+const char* kvdec_status_string(kvdec_status status);
+const char* kvdec_last_error(void);
+int kvdec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVDEC_H */

@@ -2,10 +2,10 @@
 
 This module serves both sides of every parity check (the fp64 oracle and the
 GPU library), so it holds none of the method's arithmetic: only seeded draws,
-16-bit casts (round to nearest even) and layout packing.  Every generator uses
-``numpy.random.Generator(PCG64(seed))`` with a fixed draw order, listed in its
-docstring.  Normal draws are ``standard_normal(dtype=float32)`` then scaled and
-cast.
+16-bit casts (round to nearest even) and layout packing.  Every workload draws
+from a ``Draws(seed)`` source (numpy PCG64 streams, see its docstring) in the
+order its docstring lists.  Normal draws are ``standard_normal(dtype=float32)``
+then scaled and cast.
 
 Workload shapes:
   * ``dense_small``  -- batch 1, 8 query heads on 2 KV heads, context 1024.
@@ -23,43 +23,73 @@ Workload shapes:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 
 import numpy as np
 
 D_HEAD = 128
-_BLOCK = 1 << 24  # values per draw block (keeps float32 temporaries small)
+BLOCK = 1 << 22  # values per independently seeded block of a large draw
 
 POISON_F16 = np.float16(1000.0)
 
-
-def rng_for(seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(seed))
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def normal_f16(rng, shape, scale=None):
-    """N(0,1) draws (float32), optionally times a broadcast scale, cast to fp16.
+class Draws:
+    """Seeded source of every random value of one workload.
 
-    Drawn block by block in C order; the stream is the same as one big draw.
-    ``scale`` must broadcast against the trailing dims of ``shape``.
+    Small draws (lengths, scales, importances, permutations) come, in order,
+    from ``ctl`` = PCG64(SeedSequence([seed, 0])).  The k-th large array
+    (k = 1, 2, ...) is drawn block by block: its block i of BLOCK values is
+    ``standard_normal(float32)`` from PCG64(SeedSequence([seed, k])).jumped(i).
+    Blocks are filled in parallel threads; the values do not depend on the
+    thread count.
     """
-    shape = tuple(int(s) for s in shape)
-    n = int(np.prod(shape)) if shape else 1
-    out = np.empty(n, np.float16)
-    period, sc_row = 1, None
-    if scale is not None:
-        sc = np.asarray(scale, np.float32)
-        # the scale covers the trailing dims: one row of `period` values
-        sc_row = np.broadcast_to(sc, shape[len(shape) - sc.ndim:]).reshape(-1)
-        period = sc_row.size
-    step = max(period, (_BLOCK // period) * period)
-    for lo in range(0, n, step):
-        hi = min(n, lo + step)
-        blk = rng.standard_normal(hi - lo, dtype=np.float32)
-        if sc_row is not None:
-            blk = (blk.reshape(-1, period) * sc_row[None, :]).reshape(-1)
-        out[lo:hi] = blk.astype(np.float16)
-    return out.reshape(shape)
+
+    def __init__(self, seed: int):
+        self.seed = int(seed)
+        self.ctl = np.random.Generator(np.random.PCG64(np.random.SeedSequence([self.seed, 0])))
+        self._k = 0
+
+    def _next_bitgen(self):
+        self._k += 1
+        return np.random.PCG64(np.random.SeedSequence([self.seed, self._k]))
+
+    def normal(self, shape, scale=None, out_dtype=np.float16, std=1.0):
+        """Array of N(0,1) float32 draws, times ``std`` and an optional scale
+        broadcast over the trailing dims, cast to ``out_dtype`` (float16, or
+        uint16 meaning bfloat16 bit patterns); casts round to nearest even."""
+        shape = tuple(int(s) for s in shape)
+        n = int(np.prod(shape)) if shape else 1
+        out = np.empty(n, out_dtype)
+        sc_row = None
+        if scale is not None:
+            sc = np.asarray(scale, np.float32)
+            sc_row = np.broadcast_to(sc, shape[len(shape) - sc.ndim:]).reshape(-1)
+            if BLOCK % sc_row.size:
+                raise ValueError("scale period must divide the block size")
+        base = self._next_bitgen()
+
+        def fill(i):
+            lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+            g = np.random.Generator(base.jumped(i))
+            blk = g.standard_normal(hi - lo, dtype=np.float32)
+            if std != 1.0:
+                blk *= np.float32(std)
+            if sc_row is not None:
+                blk = (blk.reshape(-1, sc_row.size) * sc_row[None, :]).reshape(-1)
+            out[lo:hi] = blk.astype(np.float16) if out_dtype == np.float16 else f32_to_bf16_bits(blk)
+
+        nblk = (n + BLOCK - 1) // BLOCK
+        if nblk <= 1:
+            for i in range(nblk):
+                fill(i)
+        else:
+            with cf.ThreadPoolExecutor(min(_THREADS, nblk)) as ex:
+                list(ex.map(fill, range(nblk)))
+        return out.reshape(shape)
 
 
 def f32_to_bf16_bits(a):
@@ -73,30 +103,16 @@ def bf16_bits_to_f32(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def normal_bf16(rng, shape, std=1.0):
-    """N(0, std^2) draws (float32) cast to bfloat16 bit patterns (uint16)."""
-    shape = tuple(int(s) for s in shape)
-    n = int(np.prod(shape))
-    out = np.empty(n, np.uint16)
-    for lo in range(0, n, _BLOCK):
-        hi = min(n, lo + _BLOCK)
-        blk = rng.standard_normal(hi - lo, dtype=np.float32)
-        if std != 1.0:
-            blk = blk * np.float32(std)
-        out[lo:hi] = f32_to_bf16_bits(blk)
-    return out.reshape(shape)
-
-
 # ---------------------------------------------------------------------------
 # Decode attention workloads
 # ---------------------------------------------------------------------------
 
 def dense_small(seed=0, B=1, Hq=8, Hkv=2, S=1024, D=D_HEAD, seqlens=None):
     """Dense KV [B, S, Hkv, D].  Draw order: q, K, V (all N(0,1) -> fp16)."""
-    rng = rng_for(seed)
-    q = normal_f16(rng, (B, Hq, D))
-    k = normal_f16(rng, (B, S, Hkv, D))
-    v = normal_f16(rng, (B, S, Hkv, D))
+    dr = Draws(seed)
+    q = dr.normal((B, Hq, D))
+    k = dr.normal((B, S, Hkv, D))
+    v = dr.normal((B, S, Hkv, D))
     return dict(layout="dense", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, q=q, k=k, v=v,
                 seqlens=None if seqlens is None else np.asarray(seqlens, np.int32),
                 scale=1.0 / math.sqrt(D))
@@ -110,16 +126,16 @@ def ragged_llama(seed=0, B=16, lo=16384, hi=32768, Hq=32, Hkv=8, D=D_HEAD, lens=
     outlier scale ~ LogNormal(0, outlier_sigma), shared by all tokens and
     sequences; K = N(0,1) * scale; V ~ N(0,1); q ~ N(0,1).
     """
-    rng = rng_for(seed)
+    dr = Draws(seed)
     if lens is None:
-        lens = rng.integers(lo, hi + 1, size=B)
+        lens = dr.ctl.integers(lo, hi + 1, size=B)
     lens = np.asarray(lens, np.int64)
     B = int(lens.size)
-    sigma = rng.lognormal(0.0, outlier_sigma, size=(Hkv, D)).astype(np.float32)
+    sigma = dr.ctl.lognormal(0.0, outlier_sigma, size=(Hkv, D)).astype(np.float32)
     T = int(lens.sum())
-    k = normal_f16(rng, (T, Hkv, D), scale=sigma)
-    v = normal_f16(rng, (T, Hkv, D))
-    q = normal_f16(rng, (B, Hq, D))
+    k = dr.normal((T, Hkv, D), scale=sigma)
+    v = dr.normal((T, Hkv, D))
+    q = dr.normal((B, Hq, D))
     cu = np.zeros(B + 1, np.int32)
     cu[1:] = np.cumsum(lens)
     return dict(layout="ragged", B=B, Hq=Hq, Hkv=Hkv, D=D, q=q, k=k, v=v, cu_seqlens=cu,
@@ -140,7 +156,8 @@ def paged_mha(seed=0, B=1024, H=32, Hkv=None, D=D_HEAD, page=16, max_pages=256, 
     permutation of the P = sum ceil(len/page) pages; pool K; pool V; q.  Slots
     past the end of a sequence's last page hold the poison value 1000.0.
     """
-    rng = rng_for(seed)
+    dr = Draws(seed)
+    rng = dr.ctl
     Hkv = H if Hkv is None else Hkv
     if lens is None:
         lens = lognormal_lengths(rng, B, median, sigma, lo, hi)
@@ -156,9 +173,9 @@ def paged_mha(seed=0, B=1024, H=32, Hkv=None, D=D_HEAD, page=16, max_pages=256, 
     for b in range(B):
         bt[b, : npg[b]] = perm[off: off + npg[b]]
         off += int(npg[b])
-    k = normal_f16(rng, (P, Hkv, page, D))
-    v = normal_f16(rng, (P, Hkv, page, D))
-    q = normal_f16(rng, (B, H, D))
+    k = dr.normal((P, Hkv, page, D))
+    v = dr.normal((P, Hkv, page, D))
+    q = dr.normal((B, H, D))
     for b in range(B):
         tail = int(lens[b] % page)
         if tail and npg[b]:
@@ -205,7 +222,7 @@ def ragged_to_dense(d, S=None):
 
 def ragged_to_paged(d, seed=0, page=16, max_pages=None):
     """Scatter a ragged workload into a shuffled page pool (draw: permutation)."""
-    rng = rng_for(seed)
+    rng = Draws(seed).ctl
     lens = np.asarray(d["seqlens"], np.int64)
     npg = (lens + page - 1) // page
     max_pages = int(npg.max(initial=1)) if max_pages is None else max_pages
@@ -243,7 +260,7 @@ def clo_queries(seed=0, model="llama3-8b", B=4, D=D_HEAD):
     The noise scale band puts the label/query cosines near 0.80-0.95.
     """
     Hq, Hkv = CLO_MODELS[model]
-    rng = rng_for(seed)
+    rng = Draws(seed).ctl
     s = rng.beta(0.5, 2.0, size=Hq)
     lab32 = rng.standard_normal((B, Hq, D), dtype=np.float32)
     sig = rng.uniform(2.96, 6.75, size=(B, Hq)).astype(np.float32)
@@ -273,18 +290,19 @@ def persistent_heads(s, Hkv, n_pers=2):
 def clo_hybrid(seed=0, model="llama3-8b", B=4, S=131072, frac=0.1, n_pers=2, D=D_HEAD):
     """CLO cache buffer + persistent cache inputs.
 
-    Draw order: the ``clo_queries`` draws (stream ``seed``); then, from a second
-    stream seeded ``seed + 1000003``, full K and V [B, Hkv, S, D] ~ N(0,1) and,
-    per (b, buffer head) in ascending order, a sorted random selection of
-    round(frac * S) token indices without replacement.
+    Draw order: the ``clo_queries`` draws (``Draws(seed)``); then, from
+    ``Draws(seed + 1000003)``, full K and V [B, Hkv, S, D] ~ N(0,1) and, per
+    (b, buffer head) in ascending order, a sorted random selection of
+    round(frac * S) token indices without replacement (from its ``ctl``).
     Persistent heads copy their full KV into slot arrays; buffer heads copy the
     selected rows, compacted in ascending token order.
     """
     base = clo_queries(seed, model, B, D)
     Hq, Hkv = base["Hq"], base["Hkv"]
-    rng = rng_for(seed + 1_000_003)
-    kf = normal_f16(rng, (B, Hkv, S, D))
-    vf = normal_f16(rng, (B, Hkv, S, D))
+    dr = Draws(seed + 1_000_003)
+    rng = dr.ctl
+    kf = dr.normal((B, Hkv, S, D))
+    vf = dr.normal((B, Hkv, S, D))
     hm = persistent_heads(base["s"], Hkv, n_pers)
     ksel = int(round(frac * S))
     P_slots = int((hm >= 0).sum())
@@ -322,17 +340,17 @@ def kvpr_layer(seed=0, b=32, h=5120, H=40, s=1024, l=256):
     Cache rows [0, l) start as the poison value 1000.0 (the recompute fills them).
     """
     D = h // H
-    rng = rng_for(seed)
-    x = normal_bf16(rng, (b, l, h))
+    dr = Draws(seed)
+    x = dr.normal((b, l, h), out_dtype=np.uint16)
     std = 1.0 / math.sqrt(h)
-    wk = normal_bf16(rng, (h, h), std)
-    wv = normal_bf16(rng, (h, h), std)
+    wk = dr.normal((h, h), out_dtype=np.uint16, std=std)
+    wv = dr.normal((h, h), out_dtype=np.uint16, std=std)
     kc = np.empty((b, s, H, D), np.float16)
     vc = np.empty((b, s, H, D), np.float16)
     kc[:, :l] = POISON_F16
     vc[:, :l] = POISON_F16
-    kc[:, l:] = normal_f16(rng, (b, s - l, H, D))
-    vc[:, l:] = normal_f16(rng, (b, s - l, H, D))
-    q = normal_f16(rng, (b, H, D))
+    kc[:, l:] = dr.normal((b, s - l, H, D))
+    vc[:, l:] = dr.normal((b, s - l, H, D))
+    q = dr.normal((b, H, D))
     return dict(b=b, h=h, H=H, D=D, s=s, l=l, x=x, w_k=wk, w_v=wv, k_cache=kc, v_cache=vc,
                 q=q, scale=1.0 / math.sqrt(D))

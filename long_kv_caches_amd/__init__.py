@@ -1,0 +1,12 @@
+"""libkvdec: long-KV-cache decode kernels for AMD MI355X (gfx950).
+
+The compute lives in the HIP library ``libkvdec.so`` (C ABI in include/kvdec.h);
+this package is its thin ctypes binding (``_lib``) and build script (``build``).
+"""
+from ._lib import (  # noqa: F401
+    KVDEC_BF16, KVDEC_DENSE, KVDEC_F16, KVDEC_PAGED, KVDEC_RAGGED, AttnDesc, HybridDesc,
+    KvdecError, alloc_workspace, attn_desc, hybrid_desc, kvdec_decode_attn,
+    kvdec_decode_attn_workspace, kvdec_headcache_lookup, kvdec_headcache_thresholds,
+    kvdec_kv_recompute, kvdec_sparse_hybrid_attn, kvdec_sparse_hybrid_attn_workspace,
+    last_error, status_string,
+)

@@ -1,0 +1,186 @@
+"""ctypes binding of libkvdec (include/kvdec.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a non-OK status raises KvdecError with the
+library's message.  Every computation runs in the library's HIP kernels; if
+libkvdec.so is missing this module raises at import (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvdec.so")
+
+KVDEC_OK, KVDEC_ERR_INVALID, KVDEC_ERR_UNSUPPORTED, KVDEC_ERR_WORKSPACE, KVDEC_ERR_HIP = range(5)
+KVDEC_F16, KVDEC_BF16 = 0, 1
+KVDEC_DENSE, KVDEC_RAGGED, KVDEC_PAGED = 0, 1, 2
+
+_DTYPES = {torch.float16: KVDEC_F16, torch.bfloat16: KVDEC_BF16}
+
+
+class KvdecError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{status_string(status)}: {msg}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32), ("kv_rows", ctypes.c_int64),
+    ]
+
+
+class HybridDesc(ctypes.Structure):
+    _fields_ = [("base", AttnDesc), ("num_pers_slots", ctypes.c_int32),
+                ("pers_cap", ctypes.c_int32), ("buf_cap", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m long_kv_caches_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "kvdec_decode_attn_workspace": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)], st),
+        "kvdec_decode_attn": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, sz, P], st),
+        "kvdec_sparse_hybrid_attn_workspace": ([ctypes.POINTER(HybridDesc), ctypes.POINTER(sz)], st),
+        "kvdec_sparse_hybrid_attn": ([ctypes.POINTER(HybridDesc), P, P, P, P, P, P, P, P, P, P, P,
+                                      sz, P], st),
+        "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
+        "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
+        "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, P, P, i64, P], st),
+        "kvdec_status_string": ([st], ctypes.c_char_p),
+        "kvdec_last_error": ([], ctypes.c_char_p),
+        "kvdec_abi_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
+            "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_thresholds",
+            "kvdec_kv_recompute", "kvdec_status_string",
+            "kvdec_last_error", "kvdec_abi_version")
+
+
+def status_string(status: int) -> str:
+    return lib.kvdec_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib.kvdec_last_error().decode()
+
+
+def _check(status):
+    if status != KVDEC_OK:
+        raise KvdecError(status, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_desc(*, batch, num_q_heads, num_kv_heads, dtype, layout, max_seqlen, head_dim=128,
+              softmax_scale=None, page_size=0, max_pages_per_seq=0, split_tokens=0, kv_rows=0):
+    if softmax_scale is None:
+        softmax_scale = head_dim ** -0.5
+    return AttnDesc(batch, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+                    _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype), layout,
+                    max_seqlen, page_size, max_pages_per_seq, split_tokens, kv_rows)
+
+
+def hybrid_desc(*, num_pers_slots, pers_cap, buf_cap, **kw):
+    kw.setdefault("layout", KVDEC_DENSE)
+    kw.setdefault("max_seqlen", 0)
+    return HybridDesc(attn_desc(**kw), num_pers_slots, pers_cap, buf_cap)
+
+
+def kvdec_decode_attn_workspace(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvdec_decode_attn_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def kvdec_sparse_hybrid_attn_workspace(desc: HybridDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvdec_sparse_hybrid_attn_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """Workspace buffer (uint8, contents irrelevant); None when nbytes is 0."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def kvdec_decode_attn(desc, q, k, v, seqlens, cu_seqlens, block_table, out, lse, workspace,
+                      stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kvdec_decode_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
+                                 _ptr(cu_seqlens), _ptr(block_table), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kvdec_sparse_hybrid_attn(desc, q, pers_k, pers_v, pers_len, buf_k, buf_v, buf_len, head_map,
+                             out, lse, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kvdec_sparse_hybrid_attn(ctypes.byref(desc), _ptr(q), _ptr(pers_k), _ptr(pers_v),
+                                        _ptr(pers_len), _ptr(buf_k), _ptr(buf_v), _ptr(buf_len),
+                                        _ptr(head_map), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        ws_bytes, _stream(stream)))
+    return out
+
+
+def kvdec_headcache_lookup(q, labels, weights, tau, hit, agg=None, cos=None, miss_list=None,
+                           miss_count=None, stream=None):
+    B, Hq, D = q.shape
+    Hkv = tau.numel()
+    _check(lib.kvdec_headcache_lookup(B, Hq, Hkv, D, _DTYPES[q.dtype], _ptr(q), _ptr(labels),
+                                      _ptr(weights), _ptr(tau), _ptr(hit), _ptr(agg), _ptr(cos),
+                                      _ptr(miss_list), _ptr(miss_count), _stream(stream)))
+    return hit
+
+
+def kvdec_headcache_thresholds(s, eta=0.8, n_exp=3.0):
+    """Host-side Eqs. 7-9; s is a CPU float32 tensor, returns a CPU float32 tensor."""
+    s = torch.as_tensor(s, dtype=torch.float32).contiguous()
+    tau = torch.empty_like(s)
+    _check(lib.kvdec_headcache_thresholds(s.numel(), ctypes.c_void_p(s.data_ptr()), float(eta),
+                                          float(n_exp), ctypes.c_void_p(tau.data_ptr())))
+    return tau
+
+
+def kvdec_kv_recompute(x, w_k, w_v, k_cache, v_cache, l, stream=None):
+    """x [b, s_x, h] bf16; k_cache, v_cache [b, s_cap, H, 128] fp16 (rows [0, l) written)."""
+    b, s_x, h = x.shape
+    H, hd = k_cache.shape[2], k_cache.shape[3]
+    _check(lib.kvdec_kv_recompute(b, l, h, H, hd, _ptr(x), s_x * h, _ptr(w_k), _ptr(w_v),
+                                  _ptr(k_cache), _ptr(v_cache), k_cache.shape[1] * H * hd,
+                                  _stream(stream)))

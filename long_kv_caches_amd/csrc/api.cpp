@@ -1,0 +1,341 @@
+// api.cpp -- the libkvdec C ABI: argument validation, work planning and
+// launches.  Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace kvdec {
+
+static thread_local char g_err[512] = "";
+
+kvdec_status fail(kvdec_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static kvdec_status ok() {
+  g_err[0] = '\0';
+  return KVDEC_OK;
+}
+
+static kvdec_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVDEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Work items of the attention kernels, one workgroup each.  `est_tokens` is
+// the host's estimate of all tokens over all (sequence, KV head) pairs and
+// `max_len` bounds one pair's length.  Aim for about kTargetItems items so
+// that the 256 CUs see several waves of workgroups, never split below
+// kMinChunk tokens, and never beyond one item per pair when that is enough.
+struct Plan {
+  int chunk;
+  int n_chunks;
+};
+
+static constexpr int64_t kTargetItems = 2048;
+static constexpr int kMinChunk = 128;
+static constexpr int kChunkQuantum = kTile * kWaves;  // 64
+
+static int round_up(int64_t x, int q) { return (int)(((x + q - 1) / q) * q); }
+
+static Plan plan_chunks(int64_t est_tokens, int max_len, int split_tokens) {
+  Plan p;
+  const int full = std::max(kChunkQuantum, round_up(std::max(max_len, 1), kChunkQuantum));
+  if (split_tokens > 0) {
+    p.chunk = std::min(split_tokens, full);
+  } else {
+    int64_t c = (est_tokens + kTargetItems - 1) / kTargetItems;
+    c = std::max<int64_t>(c, kMinChunk);
+    p.chunk = std::min(round_up(c, kChunkQuantum), full);
+  }
+  // the merge kernel keeps every chunk's (max, sum) in LDS
+  const int min_chunk = round_up((std::max(max_len, 1) + kMaxChunks - 1) / kMaxChunks, kChunkQuantum);
+  p.chunk = std::max(p.chunk, min_chunk);
+  p.n_chunks = (std::max(max_len, 1) + p.chunk - 1) / p.chunk;
+  return p;
+}
+
+static kvdec_status check_common(const kvdec_attn_desc* d, bool check_layout) {
+  if (!d) return fail(KVDEC_ERR_INVALID, "desc is NULL");
+  if (d->batch < 0) return fail(KVDEC_ERR_INVALID, "batch < 0");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(KVDEC_ERR_INVALID, "num_q_heads and num_kv_heads must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(KVDEC_ERR_INVALID, "num_q_heads %% num_kv_heads != 0");
+  if (d->num_q_heads / d->num_kv_heads > kMaxGroup)
+    return fail(KVDEC_ERR_UNSUPPORTED, "query heads per KV head > %d", kMaxGroup);
+  if (d->head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->dtype != KVDEC_F16 && d->dtype != KVDEC_BF16)
+    return fail(KVDEC_ERR_UNSUPPORTED, "dtype must be KVDEC_F16 or KVDEC_BF16");
+  if (!isfinite(d->softmax_scale)) return fail(KVDEC_ERR_INVALID, "softmax_scale not finite");
+  if (d->split_tokens < 0 || d->split_tokens % kChunkQuantum != 0)
+    return fail(KVDEC_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 64");
+  if (check_layout) {
+    if (d->layout != KVDEC_DENSE && d->layout != KVDEC_RAGGED && d->layout != KVDEC_PAGED)
+      return fail(KVDEC_ERR_INVALID, "unknown layout %d", d->layout);
+    if (d->max_seqlen < 0) return fail(KVDEC_ERR_INVALID, "max_seqlen < 0");
+    if (d->layout == KVDEC_PAGED) {
+      if (d->page_size < 16 || d->page_size % 16 != 0)
+        return fail(KVDEC_ERR_UNSUPPORTED, "page_size must be a positive multiple of 16");
+      if (d->max_pages_per_seq < 1) return fail(KVDEC_ERR_INVALID, "max_pages_per_seq < 1");
+      if ((int64_t)d->max_pages_per_seq * d->page_size < d->max_seqlen)
+        return fail(KVDEC_ERR_INVALID, "max_pages_per_seq * page_size < max_seqlen");
+      if (d->kv_rows < 1 || d->kv_rows > INT32_MAX)
+        return fail(KVDEC_ERR_INVALID, "kv_rows (pages in the pool) must be in [1, 2^31)");
+    }
+    if (d->layout == KVDEC_RAGGED && (d->kv_rows < 0 || d->kv_rows > INT32_MAX))
+      return fail(KVDEC_ERR_INVALID, "kv_rows (token rows) must be in [0, 2^31)");
+  }
+  return ok();
+}
+
+static Plan plan_decode(const kvdec_attn_desc* d) {
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
+  return plan_chunks(pairs * (int64_t)d->max_seqlen, d->max_seqlen, d->split_tokens);
+}
+
+static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
+  const kvdec_attn_desc* d = &h->base;
+  const int64_t est = (int64_t)d->batch *
+                      ((int64_t)h->num_pers_slots * h->pers_cap + (int64_t)d->num_kv_heads * h->buf_cap);
+  return plan_chunks(est, std::max(h->pers_cap, h->buf_cap), d->split_tokens);
+}
+
+static size_t attn_ws(const kvdec_attn_desc* d, const Plan& p) {
+  if (p.n_chunks <= 1 || d->batch == 0) return 0;
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
+  return attn_workspace_bytes(pairs * p.n_chunks, d->num_q_heads / d->num_kv_heads);
+}
+
+static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
+  a->B = d->batch;
+  a->Hq = d->num_q_heads;
+  a->Hkv = d->num_kv_heads;
+  a->G = d->num_q_heads / d->num_kv_heads;
+  a->chunk = p.chunk;
+  a->n_chunks = p.n_chunks;
+  a->scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
+  a->dtype = d->dtype;
+}
+
+static kvdec_status run_attn(const kvdec_attn_desc* d, const Plan& p, AttnArgs& a, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (p.n_chunks > 1) {
+    const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
+    if (!attn_workspace_carve(ws, ws_bytes, pairs * p.n_chunks, a.G, &a))
+      return fail(KVDEC_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", attn_ws(d, p),
+                  ws_bytes, ws ? "" : " (NULL)");
+  }
+  const int64_t blocks = (int64_t)d->batch * p.n_chunks * d->num_kv_heads;
+  if (blocks > INT32_MAX) return fail(KVDEC_ERR_UNSUPPORTED, "grid too large");
+  if (blocks == 0) return ok();
+  return hip_status(launch_decode_attn(a, stream), "decode attention launch");
+}
+
+}  // namespace kvdec
+
+using namespace kvdec;
+
+extern "C" {
+
+int kvdec_abi_version(void) { return KVDEC_ABI_VERSION; }
+
+const char* kvdec_last_error(void) { return g_err; }
+
+const char* kvdec_status_string(kvdec_status s) {
+  switch (s) {
+    case KVDEC_OK: return "KVDEC_OK";
+    case KVDEC_ERR_INVALID: return "KVDEC_ERR_INVALID";
+    case KVDEC_ERR_UNSUPPORTED: return "KVDEC_ERR_UNSUPPORTED";
+    case KVDEC_ERR_WORKSPACE: return "KVDEC_ERR_WORKSPACE";
+    case KVDEC_ERR_HIP: return "KVDEC_ERR_HIP";
+  }
+  return "unknown kvdec_status";
+}
+
+kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* d, size_t* bytes) {
+  if (!bytes) return fail(KVDEC_ERR_INVALID, "bytes is NULL");
+  kvdec_status st = check_common(d, true);
+  if (st != KVDEC_OK) return st;
+  *bytes = attn_ws(d, plan_decode(d));
+  return ok();
+}
+
+kvdec_status kvdec_decode_attn(const kvdec_attn_desc* d, const void* q, const void* k,
+                               const void* v, const int32_t* seqlens, const int32_t* cu_seqlens,
+                               const int32_t* block_table, void* out, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  kvdec_status st = check_common(d, true);
+  if (st != KVDEC_OK) return st;
+  if (d->batch == 0) return ok();
+  if (!q || !k || !v || !out) return fail(KVDEC_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (d->layout == KVDEC_RAGGED && !cu_seqlens)
+    return fail(KVDEC_ERR_INVALID, "RAGGED needs cu_seqlens");
+  if (d->layout == KVDEC_PAGED && (!seqlens || !block_table))
+    return fail(KVDEC_ERR_INVALID, "PAGED needs seqlens and block_table");
+  const Plan p = plan_decode(d);
+  AttnArgs a = {};
+  fill_common(d, p, &a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.seqlens = seqlens;
+  a.cu_seqlens = cu_seqlens;
+  a.block_table = block_table;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  if (d->layout == KVDEC_DENSE) {
+    a.src = SRC_DENSE;
+    a.S = d->max_seqlen;
+  } else if (d->layout == KVDEC_RAGGED) {
+    a.src = SRC_RAGGED;
+    a.S = (int)d->kv_rows;
+  } else {
+    a.src = SRC_PAGED;
+    a.S = (int)d->kv_rows;
+    a.page = d->page_size;
+    a.max_pages = d->max_pages_per_seq;
+  }
+  return run_attn(d, p, a, ws, ws_bytes, stream);
+}
+
+static kvdec_status check_hybrid(const kvdec_hybrid_desc* h) {
+  if (!h) return fail(KVDEC_ERR_INVALID, "desc is NULL");
+  kvdec_status st = check_common(&h->base, false);
+  if (st != KVDEC_OK) return st;
+  if (h->num_pers_slots < 0 || h->pers_cap < 0 || h->buf_cap < 0)
+    return fail(KVDEC_ERR_INVALID, "negative hybrid capacity");
+  return ok();
+}
+
+kvdec_status kvdec_sparse_hybrid_attn_workspace(const kvdec_hybrid_desc* h, size_t* bytes) {
+  if (!bytes) return fail(KVDEC_ERR_INVALID, "bytes is NULL");
+  kvdec_status st = check_hybrid(h);
+  if (st != KVDEC_OK) return st;
+  *bytes = attn_ws(&h->base, plan_hybrid(h));
+  return ok();
+}
+
+kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* h, const void* q,
+                                      const void* pers_k, const void* pers_v,
+                                      const int32_t* pers_len, const void* buf_k,
+                                      const void* buf_v, const int32_t* buf_len,
+                                      const int32_t* head_map, void* out, float* lse, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  kvdec_status st = check_hybrid(h);
+  if (st != KVDEC_OK) return st;
+  const kvdec_attn_desc* d = &h->base;
+  if (d->batch == 0) return ok();
+  if (!q || !out || !head_map) return fail(KVDEC_ERR_INVALID, "q, out and head_map must be non-NULL");
+  if (h->num_pers_slots > 0 && (!pers_k || !pers_v || !pers_len))
+    return fail(KVDEC_ERR_INVALID, "persistent slots need pers_k, pers_v and pers_len");
+  if (!buf_k || !buf_v || !buf_len)
+    return fail(KVDEC_ERR_INVALID, "buf_k, buf_v and buf_len must be non-NULL");
+  const Plan p = plan_hybrid(h);
+  AttnArgs a = {};
+  fill_common(d, p, &a);
+  a.src = SRC_HYBRID;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(pers_k);
+  a.v = static_cast<const uint16_t*>(pers_v);
+  a.k2 = static_cast<const uint16_t*>(buf_k);
+  a.v2 = static_cast<const uint16_t*>(buf_v);
+  a.pers_len = pers_len;
+  a.buf_len = buf_len;
+  a.head_map = head_map;
+  a.P_slots = h->num_pers_slots;
+  a.pers_cap = h->pers_cap;
+  a.buf_cap = h->buf_cap;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return run_attn(d, p, a, ws, ws_bytes, stream);
+}
+
+kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                    const void* q, void* labels, const float* weights,
+                                    const float* tau, uint8_t* hit, float* agg, float* cos,
+                                    int32_t* miss_list, int32_t* miss_count, hipStream_t stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1) return fail(KVDEC_ERR_INVALID, "bad B / Hq / Hkv");
+  if (Hq % Hkv != 0) return fail(KVDEC_ERR_INVALID, "Hq %% Hkv != 0");
+  if (Hq / Hkv > 16) return fail(KVDEC_ERR_UNSUPPORTED, "query heads per KV head > 16");
+  if (D != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "D must be 128");
+  if (dtype != KVDEC_F16 && dtype != KVDEC_BF16) return fail(KVDEC_ERR_UNSUPPORTED, "bad dtype");
+  if ((int64_t)B * Hkv > INT32_MAX / 4) return fail(KVDEC_ERR_UNSUPPORTED, "B * Hkv too large");
+  if (B == 0) return ok();
+  if (!q || !labels || !weights || !tau || !hit)
+    return fail(KVDEC_ERR_INVALID, "q, labels, weights, tau and hit must be non-NULL");
+  if ((miss_list == nullptr) != (miss_count == nullptr))
+    return fail(KVDEC_ERR_INVALID, "miss_list and miss_count go together");
+  LookupArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.labels = static_cast<uint16_t*>(labels);
+  a.w = weights;
+  a.tau = tau;
+  a.hit = hit;
+  a.agg = agg;
+  a.cos = cos;
+  a.miss_list = miss_list;
+  a.miss_count = miss_count;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.dtype = dtype;
+  return hip_status(launch_headcache_lookup(a, stream), "head-cache lookup launch");
+}
+
+kvdec_status kvdec_headcache_thresholds(int32_t n, const float* s, double eta, double n_exp,
+                                        float* tau) {
+  if (n < 0) return fail(KVDEC_ERR_INVALID, "n < 0");
+  if (n > 0 && (!s || !tau)) return fail(KVDEC_ERR_INVALID, "s and tau must be non-NULL");
+  if (!(eta >= -1.0 && eta <= 1.0)) return fail(KVDEC_ERR_INVALID, "eta outside [-1, 1]");
+  if (!(n_exp > 0.0) || !isfinite(n_exp)) return fail(KVDEC_ERR_INVALID, "n_exp must be > 0");
+  const double pi = 3.14159265358979323846;
+  const double theta_star = acos(eta);  // Eq. 7
+  for (int32_t i = 0; i < n; ++i) {
+    const double si = (double)s[i];
+    if (!(si >= 0.0 && si <= 1.0)) return fail(KVDEC_ERR_INVALID, "s[%d] outside [0, 1]", i);
+    const double lambda = pow(si, n_exp);                          // Eq. 8
+    tau[i] = (float)cos(lambda * theta_star + (1.0 - lambda) * pi);  // Eq. 9
+  }
+  return ok();
+}
+
+kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_heads,
+                                int32_t head_dim, const void* x, int64_t x_batch_stride,
+                                const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                                int64_t cache_batch_stride, hipStream_t stream) {
+  if (b < 0 || l < 0 || h < 1 || num_heads < 1) return fail(KVDEC_ERR_INVALID, "bad sizes");
+  if (head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
+  if ((int64_t)num_heads * head_dim != h) return fail(KVDEC_ERR_INVALID, "h != num_heads * head_dim");
+  if (h % 256 != 0) return fail(KVDEC_ERR_UNSUPPORTED, "h must be a multiple of 256");
+  if (x_batch_stride < (int64_t)l * h || cache_batch_stride < (int64_t)l * h)
+    return fail(KVDEC_ERR_INVALID, "batch strides smaller than l * h");
+  if (b == 0 || l == 0) return ok();
+  if (!x || !w_k || !w_v || !k_cache || !v_cache)
+    return fail(KVDEC_ERR_INVALID, "x, w_k, w_v, k_cache and v_cache must be non-NULL");
+  RecomputeArgs a = {};
+  a.x = static_cast<const uint16_t*>(x);
+  a.wk = static_cast<const uint16_t*>(w_k);
+  a.wv = static_cast<const uint16_t*>(w_v);
+  a.kc = static_cast<uint16_t*>(k_cache);
+  a.vc = static_cast<uint16_t*>(v_cache);
+  a.x_bstride = x_batch_stride;
+  a.c_bstride = cache_batch_stride;
+  a.b = b;
+  a.l = l;
+  a.h = h;
+  return hip_status(launch_kv_recompute(a, stream), "kv recompute launch");
+}
+
+
+}  // extern "C"

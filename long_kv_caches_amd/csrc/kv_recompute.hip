@@ -1,0 +1,152 @@
+// kv_recompute.hip -- KVPR partial K/V recompute as an MFMA GEMM for gfx950.
+//
+// KVPR page, section A2: the first l tokens' keys and values are recomputed on
+// the GPU from the saved activations, K[0:l] = X[0:l] W_K and V[0:l] = X[0:l]
+// W_V with W in R^{h x h}, and then join the resident rows [l, s') before
+// attention.  Here both products form one GEMM
+//     C[M = b*l, N = 2h] = X[M, K = h] . [W_K | W_V][K, N]
+// with bf16 inputs, fp32 MFMA accumulation and an epilogue that rounds to
+// fp16 and writes row (batch i, token t) straight into k_cache / v_cache
+// [b, s_cap, H, 128] at rows t < l (every other byte untouched).
+//
+// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C; its four
+// waves each own a 64 x 64 quarter as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
+// K advances 32 at a time through double-buffered LDS.  X rows are already
+// K-contiguous; W is N-contiguous, so each thread transposes a 4 x 4 block of
+// W in registers (byte permutes) before storing it K-contiguous in LDS, where
+// every MFMA operand is one 16-byte LDS read.
+#include "device_common.h"
+#include "internal.h"
+
+namespace kvdec {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (80 bytes: spreads banks)
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  // (a.lo, b.lo) -> low half from a, high half from b
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void kv_recompute_kernel(RecomputeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = a.b * a.l, N = 2 * a.h, K = a.h;
+  const int n_tiles_n = N / BN;
+  const int tile_m = blockIdx.x / n_tiles_n, tile_n = blockIdx.x % n_tiles_n;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  // W source for this N tile (never straddles the K|V boundary: h % BN == 0).
+  const bool is_v = n0 >= a.h;
+  const uint16_t* W = is_v ? a.wv : a.wk;
+  const int wn0 = is_v ? n0 - a.h : n0;
+
+  // A loads: thread -> (row am, 16-byte piece ak) for two rows am, am + 64.
+  const int am = tid >> 2, ak = (tid & 3) * 8;
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = min(m0 + am + 64 * i, M - 1);
+    const int bi = r / a.l, t = r - bi * a.l;
+    xrow[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
+  }
+  // B loads: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns (bn .. bn+3).
+  const int bn = (tid & 31) * 4, bk = (tid >> 5) * 4;
+  const uint16_t* wcol = W + (int64_t)bk * a.h + wn0 + bn;
+
+  u32x4 ra[2];
+  u32x2 rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ra[i] = load_b128(xrow[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rb[i] = *reinterpret_cast<const u32x2*>(wcol + (int64_t)(k0 + i) * a.h);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      store_b128(&As[buf][(am + 64 * i) * LDS_STRIDE + ak], ra[i]);
+    // rb[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
+    u32x2 col[4];
+    col[0] = u32x2{pack_lo(rb[0].x, rb[1].x), pack_lo(rb[2].x, rb[3].x)};
+    col[1] = u32x2{pack_hi(rb[0].x, rb[1].x), pack_hi(rb[2].x, rb[3].x)};
+    col[2] = u32x2{pack_lo(rb[0].y, rb[1].y), pack_lo(rb[2].y, rb[3].y)};
+    col[3] = u32x2{pack_hi(rb[0].y, rb[1].y), pack_hi(rb[2].y, rb[3].y)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
+  };
+
+  // Wave quarter: rows wm .. wm+63, cols wn .. wn+63.
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      u32x4 fa[2], fb[2];
+      const int kk = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * i + (lane & 31)) * LDS_STRIDE + kk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: acc[i][j][e] = C[row wm + 32i + 8*(e/4) + 4*(lane/32) + e%4][col wn + 32j + lane%32]
+  uint16_t* C = is_v ? a.vc : a.kc;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (r >= M) continue;
+      const int bi = r / a.l, t = r - bi * a.l;
+      uint16_t* crow = C + (int64_t)bi * a.c_bstride + (int64_t)t * a.h + wn0 + wn + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) crow[32 * j] = to_bits<KIND_F16>(acc[i][j][e]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
+  const int M = a.b * a.l, N = 2 * a.h;
+  const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
+  kv_recompute_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvdec

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: every declared symbol is exported, and every
+validation error returns its status before any HIP call (fake device pointers
+are never dereferenced on the host)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_kv_caches_amd as K
+from long_kv_caches_amd import _lib
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvdec.h")
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvdec_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(_lib.lib, n), n
+    assert set(names) == set(_lib.EXPORTED)
+    assert _lib.lib.kvdec_abi_version() == 1
+
+
+def test_status_strings():
+    assert K.status_string(0) == "KVDEC_OK"
+    assert K.status_string(3) == "KVDEC_ERR_WORKSPACE"
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, dtype=0, layout=K.KVDEC_RAGGED,
+                max_seqlen=100, kv_rows=200)
+    base.update(kw)
+    return K.attn_desc(**base)
+
+
+def _decode(desc, ws=None, ws_bytes=0, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, seqlens=FAKE, cu=FAKE, bt=FAKE, out=FAKE, lse=None)
+    p.update(ptrs)
+    return _lib.lib.kvdec_decode_attn(ctypes.byref(desc) if desc is not None else None, p["q"],
+                                      p["k"], p["v"], p["seqlens"], p["cu"], p["bt"], p["out"],
+                                      p["lse"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(head_dim=64), K._lib.KVDEC_ERR_UNSUPPORTED, "head_dim"),
+    (dict(num_q_heads=7), K._lib.KVDEC_ERR_INVALID, "num_q_heads"),
+    (dict(num_q_heads=32, num_kv_heads=2), K._lib.KVDEC_ERR_UNSUPPORTED, "per KV head"),
+    (dict(dtype=7), K._lib.KVDEC_ERR_UNSUPPORTED, "dtype"),
+    (dict(layout=9), K._lib.KVDEC_ERR_INVALID, "layout"),
+    (dict(batch=-1), K._lib.KVDEC_ERR_INVALID, "batch"),
+    (dict(split_tokens=100), K._lib.KVDEC_ERR_INVALID, "split_tokens"),
+    (dict(max_seqlen=-5), K._lib.KVDEC_ERR_INVALID, "max_seqlen"),
+    (dict(layout=K.KVDEC_PAGED, page_size=8, max_pages_per_seq=20), K._lib.KVDEC_ERR_UNSUPPORTED,
+     "page_size"),
+    (dict(layout=K.KVDEC_PAGED, page_size=16, max_pages_per_seq=2), K._lib.KVDEC_ERR_INVALID,
+     "max_pages_per_seq"),
+    (dict(layout=K.KVDEC_PAGED, page_size=16, max_pages_per_seq=8, kv_rows=0),
+     K._lib.KVDEC_ERR_INVALID, "kv_rows"),
+    (dict(softmax_scale=float("inf")), K._lib.KVDEC_ERR_INVALID, "softmax_scale"),
+])
+def test_decode_desc_validation(kw, status, needle):
+    d = _desc(**kw)
+    assert _decode(d) == status
+    assert needle in K.last_error()
+    with pytest.raises(K.KvdecError):
+        K.kvdec_decode_attn_workspace(d)
+
+
+def test_decode_pointer_and_workspace_validation():
+    assert _decode(None) == K._lib.KVDEC_ERR_INVALID
+    assert _decode(_desc(), q=None) == K._lib.KVDEC_ERR_INVALID
+    assert _decode(_desc(), cu=None) == K._lib.KVDEC_ERR_INVALID
+    assert "cu_seqlens" in K.last_error()
+    pd = _desc(layout=K.KVDEC_PAGED, page_size=16, max_pages_per_seq=8, kv_rows=10)
+    assert _decode(pd, bt=None) == K._lib.KVDEC_ERR_INVALID
+    # a long split problem needs a workspace
+    big = _desc(batch=4, max_seqlen=40000, kv_rows=160000)
+    need = K.kvdec_decode_attn_workspace(big)
+    assert need > 0
+    assert _decode(big, ws=None, ws_bytes=0) == K._lib.KVDEC_ERR_WORKSPACE
+    assert _decode(big, ws=FAKE, ws_bytes=need - 1) == K._lib.KVDEC_ERR_WORKSPACE
+    assert str(need) in K.last_error()
+    # empty batch is a no-op success
+    assert _decode(_desc(batch=0)) == K._lib.KVDEC_OK
+
+
+def test_workspace_sizes():
+    small = _desc(max_seqlen=100)
+    assert K.kvdec_decode_attn_workspace(small) == 0  # one item per (b, g): no partials
+    d = _desc(batch=16, num_q_heads=32, num_kv_heads=8, max_seqlen=32768, kv_rows=393216,
+              split_tokens=512)
+    items = 16 * 8 * (32768 // 512)
+    up = lambda x: (x + 255) // 256 * 256
+    assert K.kvdec_decode_attn_workspace(d) == up(items * 4 * 128 * 4) + up(items * 4 * 2 * 4)
+
+
+def test_hybrid_validation():
+    h = K.hybrid_desc(batch=1, num_q_heads=8, num_kv_heads=2, dtype=0, num_pers_slots=-1,
+                      pers_cap=10, buf_cap=10)
+    n = ctypes.c_size_t()
+    assert _lib.lib.kvdec_sparse_hybrid_attn_workspace(ctypes.byref(h), ctypes.byref(n)) == 1
+    h.num_pers_slots = 1
+    rc = _lib.lib.kvdec_sparse_hybrid_attn(ctypes.byref(h), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, None, FAKE, None, None, 0, None)
+    assert rc == K._lib.KVDEC_ERR_INVALID and "head_map" in K.last_error()
+
+
+def test_lookup_validation():
+    L = _lib.lib.kvdec_headcache_lookup
+    args = [FAKE] * 5
+    assert L(2, 8, 3, 128, 0, *args, None, None, None, None, None) == K._lib.KVDEC_ERR_INVALID
+    assert L(2, 8, 2, 64, 0, *args, None, None, None, None, None) == K._lib.KVDEC_ERR_UNSUPPORTED
+    assert L(2, 64, 2, 128, 0, *args, None, None, None, None, None) == K._lib.KVDEC_ERR_UNSUPPORTED
+    assert L(2, 8, 2, 128, 0, *args, None, None, FAKE, None, None) == K._lib.KVDEC_ERR_INVALID
+    assert "miss_list" in K.last_error()
+    assert L(0, 8, 2, 128, 0, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_recompute_validation():
+    R = _lib.lib.kvdec_kv_recompute
+    assert R(2, 4, 5000, 40, 128, FAKE, 4 * 5000, FAKE, FAKE, FAKE, FAKE, 8 * 5000, None) == 1
+    assert R(2, 4, 5120, 40, 64, FAKE, 4 * 5120, FAKE, FAKE, FAKE, FAKE, 8 * 5120, None) == 2
+    assert R(2, 4, 384, 3, 128, FAKE, 4 * 384, FAKE, FAKE, FAKE, FAKE, 8 * 384, None) == 2
+    assert R(2, 4, 5120, 40, 128, FAKE, 3 * 5120, FAKE, FAKE, FAKE, FAKE, 8 * 5120, None) == 1
+    assert R(2, 0, 5120, 40, 128, None, 0, None, None, None, None, 0, None) == 0
+
+
+def test_thresholds_host_helper_matches_oracle_bitwise():
+    s = np.concatenate([[0.0, 1.0, 0.5], np.random.default_rng(0).beta(0.5, 2, 200)]).astype(np.float32)
+    for eta, n in ((0.8, 3.0), (0.5, 1.0), (-1.0, 3.0), (0.95, 7.0)):
+        ours = K.kvdec_headcache_thresholds(s, eta, n).numpy()
+        ref = oracle.thresholds(s.astype(np.float64), eta, n).astype(np.float32)
+        assert np.array_equal(ours, ref)
+    with pytest.raises(K.KvdecError):
+        K.kvdec_headcache_thresholds([1.5])
+    with pytest.raises(K.KvdecError):
+        K.kvdec_headcache_thresholds([0.5], eta=1.5)

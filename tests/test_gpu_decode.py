@@ -1,0 +1,123 @@
+"""GPU parity of kvdec_decode_attn (dense, ragged, paged) against the fp64 oracle.
+
+Every case is seeded; shapes span several 16-token tiles, several 64-token
+waves of a work item, several work items per sequence and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvgen
+import oracle
+from gpu_util import (bits, check_close, check_lse, decode_on_gpu, dev, host_f64, say,
+                      to_bf16_bits)
+
+pytestmark = pytest.mark.gpu
+
+ORC_LAYOUT = {"dense": oracle.DENSE, "ragged": oracle.RAGGED, "paged": oracle.PAGED}
+
+
+def oracle_ref(d, bf16=False):
+    conv = to_bf16_bits if bf16 else (lambda x: x)
+    return oracle.decode_attn(conv(d["q"]), conv(d["k"]), conv(d["v"]), num_kv_heads=d["Hkv"],
+                              layout=ORC_LAYOUT[d["layout"]], scale=d["scale"],
+                              kind=oracle.BF16 if bf16 else oracle.F16,
+                              seqlens=d.get("seqlens"), cu_seqlens=d.get("cu_seqlens"),
+                              block_table=d.get("block_table"))
+
+
+def _parity(d, what, split_tokens=0, bf16=False):
+    say(f"[decode] {what} split={split_tokens} bf16={bf16}")
+    out, lse = decode_on_gpu(d, split_tokens=split_tokens, bf16=bf16)
+    ref_o, ref_l = oracle_ref(d, bf16)
+    check_close(host_f64(out), ref_o, what, bf16_out=bf16)
+    check_lse(lse, ref_l, what + " lse")
+    return out
+
+
+def test_dense_small_config():
+    d = kvgen.dense_small(seed=0)
+    _parity(d, "dense 1x8/2x1024")
+    _parity(d, "dense 1x8/2x1024", split_tokens=64)
+
+
+def test_single_key_returns_v_bit_exact():
+    for layout in ("dense", "ragged"):
+        d = kvgen.dense_small(seed=1, B=3, Hq=8, Hkv=2, S=1)
+        if layout == "ragged":
+            d = dict(d, layout="ragged", k=d["k"].reshape(3, 2, 128), v=d["v"].reshape(3, 2, 128),
+                     cu_seqlens=np.arange(4, dtype=np.int32), seqlens=np.ones(3, np.int32))
+        say(f"[decode] single key {layout}")
+        out, lse = decode_on_gpu(d)
+        got = bits(out)
+        v = d["v"].reshape(3, 2, 128).view(np.uint16)
+        for j in range(8):
+            assert np.array_equal(got[:, j], v[:, j // 4]), (layout, j)
+
+
+@pytest.mark.parametrize("split", [0, 64, 128, 512])
+def test_ragged_tiles_and_tails(split):
+    lens = [1, 15, 16, 17, 63, 64, 65, 127, 700, 1000, 3001, 64 * 37 + 5]
+    d = kvgen.ragged_llama(seed=2, lens=lens, Hq=32, Hkv=8)
+    _parity(d, f"ragged lens={lens}", split_tokens=split)
+
+
+def test_deterministic_repeats():
+    d = kvgen.ragged_llama(seed=3, lens=[5000, 333, 4097], Hq=32, Hkv=8)
+    say("[decode] determinism x3")
+    outs, _ = decode_on_gpu(d, split_tokens=256, repeat=3)
+    b0 = bits(outs[0])
+    for o in outs[1:]:
+        assert np.array_equal(bits(o), b0)
+
+
+def test_empty_sequences():
+    d = kvgen.ragged_llama(seed=4, lens=[0, 5, 0, 300, 0], Hq=8, Hkv=2)
+    out = _parity(d, "ragged with empty sequences", split_tokens=64)
+    got = host_f64(out)
+    assert np.all(got[[0, 2, 4]] == 0.0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (12, 4), (40, 8), (48, 8), (56, 8), (64, 8)])
+def test_group_sizes(hq, hkv):
+    d = kvgen.ragged_llama(seed=5, lens=[1, 77, 1500, 2049], Hq=hq, Hkv=hkv)
+    _parity(d, f"G={hq // hkv}", split_tokens=256)
+
+
+def test_dense_with_seqlens():
+    d = kvgen.dense_small(seed=6, B=4, Hq=16, Hkv=4, S=2000, seqlens=[2000, 1, 999, 0])
+    _parity(d, "dense with seqlens", split_tokens=128)
+
+
+def test_bf16():
+    d = kvgen.ragged_llama(seed=7, lens=[100, 2000, 4321], Hq=32, Hkv=8)
+    _parity(d, "ragged bf16", split_tokens=256, bf16=True)
+
+
+def test_paged_bitwise_equals_ragged():
+    d = kvgen.ragged_llama(seed=8, lens=[16, 17, 1000, 2047, 5000], Hq=32, Hkv=8)
+    p = kvgen.ragged_to_paged(d, seed=9)
+    say("[decode] paged vs ragged bitwise")
+    for split in (64, 512):
+        out_r, lse_r = decode_on_gpu(d, split_tokens=split)
+        out_p, lse_p = decode_on_gpu(p, split_tokens=split)
+        assert np.array_equal(bits(out_r), bits(out_p))
+        assert np.array_equal(lse_r.view(np.uint32), lse_p.view(np.uint32))
+    _parity(p, "paged (from ragged)", split_tokens=512)
+
+
+def test_paged_mha_reduced_batch():
+    d = kvgen.paged_mha(seed=10, B=96)
+    _parity(d, "paged Llama-2-7B MHA, B=96")
+
+
+def test_page_size_32():
+    d = kvgen.ragged_llama(seed=11, lens=[31, 32, 33, 900], Hq=8, Hkv=8)
+    p = kvgen.ragged_to_paged(d, seed=12, page=32)
+    _parity(p, "paged page_size=32", split_tokens=128)
+
+
+def test_headline_full_size():
+    """Llama3-8B 32K ragged batch at full size, default plan (as the bench runs it)."""
+    d = kvgen.ragged_llama(seed=0)
+    _parity(d, "Llama3-8B ragged B=16 16K-32K (full)")

@@ -1,0 +1,102 @@
+"""GPU parity of kvdec_kv_recompute (KVPR partial recompute, MFMA GEMM) and of
+attention over the merged cache [0, s')."""
+import numpy as np
+import pytest
+import torch
+
+import kvgen
+import long_kv_caches_amd as K
+import oracle
+from gpu_util import bits, check_close, decode_on_gpu, dev, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def recompute_on_gpu(d):
+    x = dev(d["x"], bf16=True)
+    wk = dev(d["w_k"], bf16=True)
+    wv = dev(d["w_v"], bf16=True)
+    kc = dev(d["k_cache"])
+    vc = dev(d["v_cache"])
+    K.kvdec_kv_recompute(x, wk, wv, kc, vc, d["l"])
+    torch.cuda.synchronize()
+    return kc, vc
+
+
+def _check_rows(d, kc, vc, rows=None):
+    b, l, h = d["b"], d["l"], d["h"]
+    ko, vo = oracle.kv_recompute(d["x"], d["w_k"], d["w_v"], l=l, rows=rows)
+    kg = host_f64(kc).reshape(b, -1, h)[:, :l].reshape(b * l, h)
+    vg = host_f64(vc).reshape(b, -1, h)[:, :l].reshape(b * l, h)
+    if rows is not None:
+        kg, vg = kg[rows], vg[rows]
+    check_close(kg, ko, "K rows")
+    check_close(vg, vo, "V rows")
+    # rows [l, s') untouched, bit for bit
+    s = d["k_cache"].shape[1]
+    assert np.array_equal(bits(kc)[:, l:], d["k_cache"][:, l:].view(np.uint16))
+    assert np.array_equal(bits(vc)[:, l:], d["v_cache"][:, l:].view(np.uint16))
+
+
+@pytest.mark.parametrize("b,l,h,H", [(3, 17, 256, 2), (2, 150, 512, 4), (1, 1, 256, 2),
+                                     (4, 128, 1024, 8)])
+def test_small_shapes(b, l, h, H):
+    d = kvgen.kvpr_layer(seed=1, b=b, h=h, H=H, s=l + 40, l=l)
+    say(f"[recompute] b={b} l={l} h={h}")
+    kc, vc = recompute_on_gpu(d)
+    _check_rows(d, kc, vc)
+
+
+def test_unit_vector_rows_bit_exact():
+    rng = np.random.default_rng(2)
+    d = kvgen.kvpr_layer(seed=2, b=2, h=512, H=4, s=40, l=33)
+    idx = rng.integers(0, 512, size=(2, 33))
+    x = np.zeros((2, 33, 512), np.float32)
+    for i in range(2):
+        for t in range(33):
+            x[i, t, idx[i, t]] = 1.0
+    d["x"] = kvgen.f32_to_bf16_bits(x)
+    say("[recompute] unit-vector rows")
+    kc, vc = recompute_on_gpu(d)
+    kg = bits(kc).reshape(2, 40, 512)
+    vg = bits(vc).reshape(2, 40, 512)
+    wk16 = kvgen.bf16_bits_to_f32(d["w_k"]).astype(np.float16).view(np.uint16)
+    wv16 = kvgen.bf16_bits_to_f32(d["w_v"]).astype(np.float16).view(np.uint16)
+    for i in range(2):
+        for t in range(33):
+            assert np.array_equal(kg[i, t], wk16[idx[i, t]])
+            assert np.array_equal(vg[i, t], wv16[idx[i, t]])
+
+
+def test_opt13b_full_size_sampled_rows_then_attention():
+    d = kvgen.kvpr_layer(seed=0)
+    say("[recompute] OPT-13B b=32 l=256 h=5120 (sampled rows)")
+    kc, vc = recompute_on_gpu(d)
+    rows = np.sort(np.random.default_rng(3).choice(d["b"] * d["l"], 40, replace=False)).astype(np.int32)
+    _check_rows(d, kc, vc, rows=rows)
+    # attention over [0, s'): first with the GPU's own recomputed rows (isolates attention)
+    w = dict(layout="dense", B=d["b"], Hq=d["H"], Hkv=d["H"], D=128, S=d["s"], q=d["q"],
+             k=bits(kc).view(np.float16), v=bits(vc).view(np.float16), seqlens=None,
+             scale=d["scale"])
+    say("[recompute] attention over the merged cache")
+    out, _ = decode_on_gpu(w, dev_inputs=dict(q=dev(d["q"]), k=kc, v=vc))
+    ro, _ = oracle.decode_attn(w["q"], w["k"], w["v"], num_kv_heads=d["H"], layout=oracle.DENSE,
+                               scale=d["scale"])
+    check_close(host_f64(out), ro, "attention (GPU rows)")
+
+
+def test_end_to_end_against_fp64_recompute():
+    d = kvgen.kvpr_layer(seed=4, b=2, h=1024, H=8, s=200, l=120)
+    say("[recompute] end to end vs fp64 X.W")
+    kc, vc = recompute_on_gpu(d)
+    ko, vo = oracle.kv_recompute(d["x"], d["w_k"], d["w_v"], l=d["l"])
+    kref = d["k_cache"].copy()
+    vref = d["v_cache"].copy()
+    kref[:, :d["l"]] = ko.reshape(2, d["l"], 8, 128).astype(np.float16)
+    vref[:, :d["l"]] = vo.reshape(2, d["l"], 8, 128).astype(np.float16)
+    w = dict(layout="dense", B=2, Hq=8, Hkv=8, D=128, S=200, q=d["q"], k=kref, v=vref,
+             seqlens=None, scale=d["scale"])
+    out, _ = decode_on_gpu(w, dev_inputs=dict(q=dev(d["q"]), k=kc, v=vc))
+    ro, _ = oracle.decode_attn(d["q"], kref, vref, num_kv_heads=8, layout=oracle.DENSE,
+                               scale=d["scale"])
+    check_close(host_f64(out), ro, "end to end")

@@ -13,13 +13,20 @@ def test_deterministic_per_seed():
     assert not np.array_equal(a["q"], c["q"])
 
 
-def test_block_draws_equal_one_draw():
-    # drawing in blocks must give the same stream as one draw
-    rng1, rng2 = kvgen.rng_for(5), kvgen.rng_for(5)
-    n = (1 << 24) + 1000
-    big = kvgen.normal_f16(rng1, (n,))
-    ref = rng2.standard_normal(n, dtype=np.float32).astype(np.float16)
-    assert np.array_equal(big, ref)
+def test_draws_independent_of_thread_count():
+    n = 3 * kvgen.BLOCK + 1000
+    a = kvgen.Draws(5).normal((n,))
+    saved = kvgen._THREADS
+    try:
+        kvgen._THREADS = 1
+        b = kvgen.Draws(5).normal((n,))
+    finally:
+        kvgen._THREADS = saved
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    # block 1 is stream (seed, 1) jumped once
+    bg = np.random.PCG64(np.random.SeedSequence([5, 1])).jumped(1)
+    ref = np.random.Generator(bg).standard_normal(kvgen.BLOCK, dtype=np.float32)
+    assert np.array_equal(a[kvgen.BLOCK:2 * kvgen.BLOCK], ref.astype(np.float16))
 
 
 def test_ragged_shapes_and_ranges():
@@ -44,7 +51,7 @@ def test_paged_structure():
 
 
 def test_lognormal_lengths_median_and_clip():
-    rng = kvgen.rng_for(0)
+    rng = kvgen.Draws(0).ctl
     lens = kvgen.lognormal_lengths(rng, 20000)
     assert lens.min() >= 128 and lens.max() <= 4096
     assert 950 < np.median(lens) < 1100
