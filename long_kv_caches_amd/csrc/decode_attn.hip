@@ -13,13 +13,18 @@
 //   Each wave walks 16-token tiles c*chunk + 16*(wave + 4i) of the item and
 //   keeps its own online-softmax state (running max m, sum l, output o) for
 //   the G query heads of KV head g.
-//   Per tile:
-//     K tile -> registers in the MFMA A layout (lane l holds token l%16 and
-//               four 16-byte pieces of its 256-byte row), Q^T in the B layout;
-//               four v_mfma_f32_16x16x32 give the 16 x G score block.
-//     online softmax in log2 units (scores are pre-scaled by scale*log2 e).
-//     V tile -> registers (lane l holds 16 bytes of one of four tokens), the
-//               probabilities reach it by a DPP row broadcast, fp32 FMAs.
+//   Lane l owns the 16-byte piece n = l % 16 (8 of the 128 elements) of rows
+//   4*(l/16) .. 4*(l/16)+3 of a tile, so every load instruction reads four
+//   whole 256-byte rows (fully coalesced) for K and for V alike.  Per tile:
+//     scores  v_dot2_f32_f16 (or _bf16) partial dots of the lane's piece with
+//             q, summed over the 16 pieces of a row by four DPP row steps;
+//     softmax tile max across the four row groups by permlane16/32 swaps,
+//             exp2 in log2 units (scores are pre-scaled by scale*log2 e);
+//     P.V     the probabilities are already in the lanes that hold the V
+//             rows: fp32 FMAs on the lane's 8 V elements.
+//   This op is HBM-bound (4-8 flops per byte), so the score dots stay on the
+//   vector ALU, where they need no operand reshuffle; no LDS is touched in
+//   the loop.
 //   The 4 waves merge through LDS.  A sequence covered by one item writes the
 //   normalised output directly; otherwise each item writes its partial
 //   (o, m, l) to the workspace and a second, small kernel merges the partials
@@ -67,7 +72,7 @@ __device__ __forceinline__ SeqView locate(const AttnArgs& a, int b, int g) {
     s.kb = a.k;
     s.vb = a.v;
   } else {  // SRC_HYBRID
-    const int slot = a.head_map[g];
+    const int slot = __builtin_amdgcn_readfirstlane(a.head_map[g]);
     s.stride = kHeadDim;
     if (slot >= 0) {
       s.len = slot < a.P_slots ? min(a.pers_len[b], a.pers_cap) : 0;
@@ -81,7 +86,9 @@ __device__ __forceinline__ SeqView locate(const AttnArgs& a, int b, int g) {
       s.vb = a.v2 + base;
     }
   }
-  s.len = max(0, min(s.len, a.n_chunks * a.chunk));
+  // Values loaded from memory are the same for the whole workgroup; say so,
+  // so that buffer descriptors built from them stay in scalar registers.
+  s.len = __builtin_amdgcn_readfirstlane(max(0, min(s.len, a.n_chunks * a.chunk)));
   return s;
 }
 
@@ -89,7 +96,8 @@ template <int KIND, int G, int SRC>
 __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
   static_assert(G >= 1 && G <= kMaxGroup, "group size");
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int n = lane & 15, lg = lane >> 4;
 
   int bid = blockIdx.x;
@@ -114,85 +122,94 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
   }
   if (c >= n_c) return;
 
-  // Q^T fragment in the MFMA B layout: column n = query head, rows = the same
-  // 8-element d pieces the K fragment uses.  Heads n >= G are zero.
-  u32x4 qf[4];
+  // q piece n of each query head of the group (8 elements, 4 packed words).
+  u32x4 qf[G];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = u32x4{0u, 0u, 0u, 0u};
-    if (n < G) qf[s] = load_b128(a.q + (head0 + n) * kHeadDim + 32 * s + 8 * lg);
-  }
+  for (int j = 0; j < G; ++j) qf[j] = load_b128(a.q + (head0 + j) * kHeadDim + 8 * n);
 
   const int t_lo = c * a.chunk;
   const int t_hi = min(len, t_lo + a.chunk);
   const int n_tiles = (t_hi - t_lo + kTile - 1) / kTile;
 
-  // Element offsets of the K/V rows this lane reads for the tile at t0.
-  auto tile_rows = [&](int t0, int64_t& rk, int64_t (&rv)[4]) {
-    const int tk = min(t0 + n, len - 1);
+  // K/V rows of one 16-token tile come through buffer resources whose base is
+  // the tile's first row (scalar registers) and whose size covers only the
+  // rows below len: rows past the end of the sequence, and whole tiles past
+  // the wave's last one, read as zeros with no memory traffic.  Per-lane
+  // offsets are the same for every tile.
+  const uint32_t row_bytes = (SRC == SRC_PAGED) ? kHeadDim * 2 : (uint32_t)(sq.stride * 2);
+  uint32_t row_off[4];  // this lane's rows 4*lg + i, piece n
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row_off[i] = (4 * lg + i) * row_bytes + 16 * n;
+
+  auto load_tile = [&](int kt, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
+    const int t0 = t_lo + kTile * kt;
+    const int rows = kt < n_tiles ? min(len - t0, kTile) : 0;
+    int64_t row0;  // element offset of the tile's first row
     if constexpr (SRC == SRC_PAGED) {
-      int pg = a.block_table[(int64_t)b * a.max_pages + t0 / a.page];
-      pg = min(max(pg, 0), a.S - 1);  // a.S holds the pool's page count
-      const int64_t pbase = ((int64_t)pg * a.Hkv + g) * a.page;
-      const int in0 = t0 % a.page;  // tiles never straddle pages
-      rk = (pbase + in0 + (tk - t0)) * kHeadDim;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tv = min(t0 + 4 * lg + i, len - 1);
-        rv[i] = (pbase + in0 + (tv - t0)) * kHeadDim;
-      }
+      int pg = kt < n_tiles ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
+      pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
+      row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;  // tiles never straddle pages
     } else {
-      rk = (int64_t)tk * sq.stride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rv[i] = (int64_t)min(t0 + 4 * lg + i, len - 1) * sq.stride;
+      row0 = (int64_t)t0 * sq.stride;
     }
-  };
-  auto load_tile = [&](int t0, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
-    int64_t rk, rv[4];
-    tile_rows(t0, rk, rv);
+    const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(sq.kb + row0), nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(sq.vb + row0), nbytes);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[s] = load_b128<true>(sq.kb + rk + 32 * s + 8 * lg);
+    for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, row_off[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vf[i] = load_b128<true>(sq.vb + rv[i] + 8 * n);
+    for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, row_off[i]);
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float o[G][8];
+  // Online-softmax state; every lane holds the same m and l (per head).
+  float m_run[G], l_run[G], o[G][8];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int j = 0; j < G; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  }
 
-  // One 16-token tile: MFMA scores, online softmax, P.V accumulation.
+  // One 16-token tile: scores, online softmax, P.V accumulation.
   auto process = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4], int kt) {
-    // scores: acc[r] = S[token 4*lg + r][head n]
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma16x16x32<KIND>(kf[s], qf[s], acc);
-
     const int t0 = t_lo + kTile * kt;
-    float sc[4];
+    float sc[4][G];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      sc[r] = (t0 + 4 * lg + r < len) ? acc[r] * a.scale_log2 : -INFINITY;
-    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    tmax = fmaxf(tmax, xor_shfl(tmax, 16));
-    tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);  // finite: every tile has a valid token
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[4];
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = t0 + 4 * lg + i < len;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - m_new);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    const bool grew = (n < G) && (m_new > m_run);
-    m_run = m_new;
-
-    if (__ballot(grew)) {
-      static_for<0, G>([&](auto J) {
-        const float aj = row_bcast<decltype(J)::value>(alpha);
+      for (int j = 0; j < G; ++j) {
+        float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[J][e] *= aj;
-      });
+        for (int e = 0; e < 4; ++e) part = dot2<KIND>(kf[i][e], qf[j][e], part);
+        const float full = row_sum16(part);
+        sc[i][j] = valid ? full * a.scale_log2 : -INFINITY;
+      }
+    }
+    bool grew = false;
+    float alpha[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float tmax = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
+      tmax = rowgroup_max(tmax);
+      const float m_new = fmaxf(m_run[j], tmax);  // finite: every tile has a valid token
+      alpha[j] = fast_exp2(m_run[j] - m_new);
+      grew |= m_new > m_run[j];
+      m_run[j] = m_new;
+    }
+    float p[4][G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i][j] = fast_exp2(sc[i][j] - m_run[j]);
+      l_run[j] = l_run[j] * alpha[j] + ((p[0][j] + p[1][j]) + (p[2][j] + p[3][j]));
+    }
+    if (__builtin_amdgcn_readfirstlane((int)grew)) {  // the same in every lane
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] *= alpha[j];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -202,44 +219,37 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
         vv[2 * e] = lo_f32<KIND>(vf[i][e]);
         vv[2 * e + 1] = hi_f32<KIND>(vf[i][e]);
       }
-      static_for<0, G>([&](auto J) {
-        const float pj = row_bcast<decltype(J)::value>(p[i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[J][e] = __builtin_fmaf(pj, vv[e], o[J][e]);
-      });
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = __builtin_fmaf(p[i][j], vv[e], o[j][e]);
     }
   };
 
   // Two register buffers in ping-pong: the next tile's loads are in flight
-  // while the current one is processed.  Prefetch addresses are clamped to the
-  // wave's last tile, so loads are unconditional (no branch, no register copy
-  // that would force an early wait); a clamped repeat re-reads lines just
-  // fetched.
+  // while the current one is processed.  Loads are unconditional (a tile past
+  // the wave's last one reads nothing), so no branch or register copy forces
+  // an early wait.
   if (wave < n_tiles) {
-    const int last = wave + kWaves * ((n_tiles - 1 - wave) / kWaves);
-    auto tile_t0 = [&](int kt) { return t_lo + kTile * min(kt, last); };
     u32x4 ka[4], va[4], kb[4], vb[4];
-    load_tile(tile_t0(wave), ka, va);
+    load_tile(wave, ka, va);
     for (int kt = wave;; kt += 2 * kWaves) {
-      load_tile(tile_t0(kt + kWaves), kb, vb);
+      load_tile(kt + kWaves, kb, vb);
       process(ka, va, kt);
-      if (kt + kWaves > last) break;
-      load_tile(tile_t0(kt + 2 * kWaves), ka, va);
+      if (kt + kWaves >= n_tiles) break;
+      load_tile(kt + 2 * kWaves, ka, va);
       process(kb, vb, kt + kWaves);
-      if (kt + 2 * kWaves > last) break;
+      if (kt + 2 * kWaves >= n_tiles) break;
     }
   }
 
-  // Sum the four lane groups (they hold different tokens of the same heads).
-  l_run += xor_shfl(l_run, 16);
-  l_run += xor_shfl(l_run, 32);
+  // Sum the four row groups (they hold different rows of the same pieces).
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int j = 0; j < G; ++j) {
+    l_run[j] = rowgroup_sum(l_run[j]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[j][e] += xor_shfl(o[j][e], 16);
-      o[j][e] += xor_shfl(o[j][e], 32);
-    }
+    for (int e = 0; e < 8; ++e) o[j][e] = rowgroup_sum(o[j][e]);
+  }
 
   // Merge the four waves through LDS.
   __shared__ float sm_o[kWaves][G][kHeadDim];
@@ -249,9 +259,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
     for (int j = 0; j < G; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) sm_o[wave][j][8 * n + e] = o[j][e];
-    if (n < G) {
-      sm_m[wave][n] = m_run;
-      sm_l[wave][n] = l_run;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      sm_m[wave][j] = m_run[j];
+      sm_l[wave][j] = l_run[j];
     }
   }
   __syncthreads();

@@ -22,6 +22,28 @@ __device__ __forceinline__ u32x4 load_b128(const void* p) {
   else return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Values the caller knows are equal across the wave (kept in scalar registers).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uniform_u32((uint32_t)u), hi = uniform_u32((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(lo | (hi << 32));
+}
+
+// Raw buffer resource over [base, base + nbytes): loads at offsets >= nbytes
+// return zero and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+// 16-byte buffer load marked non-temporal (streamed once).
+__device__ __forceinline__ u32x4 buffer_load_b128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+
 __device__ __forceinline__ void store_b128(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
@@ -57,38 +79,66 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   }
 }
 
-// 16x16x32 MFMA on 8 packed 16-bit values per lane (fp32 accumulate).
+// acc + a.lo * b.lo + a.hi * b.hi on packed 16-bit pairs, fp32 accumulate.
 template <int KIND>
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   if constexpr (KIND == KIND_F16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc, false);
   } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), acc,
+                                           false);
   }
 }
 
-// Value of lane J of this lane's 16-lane row (DPP row broadcast).
-template <int J>
-__device__ __forceinline__ float row_bcast(float x) {
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
+// Sum over the 16 lanes of each row; every lane of the row gets the sum.
+// Steps: swap neighbours, swap pairs (quad permutes), then mirror within
+// half-rows and within the row.  Fixed order, so the result is deterministic.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
 }
 
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Row exchanges between two registers a and b holding the same per-lane
+// value: afterwards (a, b) hold (row r, row r^1) for permlane16 and (half h,
+// half h^1) for permlane32 in every lane, so a op b combines the partners.
+// Issued as inline assembly with both operands in/out: the compiler builtins
+// for these swaps hand back the first result for both outputs.  The s_nop
+// pads cover the VALU-write / permlane-read hazard on either side.
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// Combine the four 16-lane rows of the wave (every lane gets the result):
+// rows 0<->1 and 2<->3 by permlane16 swap, then halves by permlane32 swap.
+__device__ __forceinline__ float rowgroup_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = b = __builtin_bit_cast(uint32_t, x);
+  permlane32_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = b = __builtin_bit_cast(uint32_t, x);
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
 }  // namespace kvdec
