@@ -74,8 +74,12 @@ typedef enum { KVDEC_DENSE = 0, KVDEC_RAGGED = 1, KVDEC_PAGED = 2 } kvdec_layout
  *                  an error the kernel cannot report (they are clamped).
  *   page_size      PAGED only: tokens per page, a multiple of 16
  *   max_pages_per_seq PAGED only: row stride of block_table
- *   split_tokens   0 = the library chooses how many tokens one work item
- *                  covers; otherwise that count (a multiple of 64).
+ *   split_tokens   0 = balanced schedule: every tile of every sequence is
+ *                  spread evenly over a persistent grid sized to the device,
+ *                  so the length mix does not leave compute units idle;
+ *                  otherwise each work item covers split_tokens tokens (a
+ *                  multiple of 64) of one sequence, and a sequence's result
+ *                  does not depend on the other sequences of the batch.
  *   kv_rows        RAGGED: the token rows T in k and v; PAGED: the pages P in
  *                  the pool; DENSE: ignored.  The kernel clamps cu_seqlens into
  *                  [0, T] and page ids into [0, P), so malformed metadata reads
@@ -92,10 +96,12 @@ typedef struct {
   int64_t kv_rows;
 } kvdec_attn_desc;
 
-/* Workspace bytes kvdec_decode_attn needs for this descriptor (0 when every
- * sequence fits one work item).  The workspace holds the per-call partial
- * results of the split work items; its contents need no initialisation and
- * are dead after the call's kernels finish. */
+/* Workspace bytes kvdec_decode_attn needs for this descriptor on the current
+ * device (0 only with split_tokens > 0 when every sequence fits one work
+ * item).  The workspace holds the per-call partial results; its contents need
+ * no initialisation and are dead after the call's kernels finish.  The size
+ * depends on the device's compute-unit count: query it on the device that
+ * will run the call. */
 kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* desc, size_t* bytes /*(host)*/);
 
 /*

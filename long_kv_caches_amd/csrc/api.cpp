@@ -31,14 +31,20 @@ static kvdec_status hip_status(hipError_t e, const char* what) {
   return fail(KVDEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Work items of the attention kernels, one workgroup each.  `est_tokens` is
-// the host's estimate of all tokens over all (sequence, KV head) pairs and
-// `max_len` bounds one pair's length.  Aim for about kTargetItems items so
-// that the 256 CUs see several waves of workgroups, never split below
-// kMinChunk tokens, and never beyond one item per pair when that is enough.
+// Work plan of the attention kernels.  With split_tokens = 0 the balanced
+// schedule runs a persistent grid whose waves take items of the tile line
+// (all tiles of all pairs, laid out on the device from the actual lengths)
+// until none is left.  With split_tokens > 0, or when the tile line has more
+// units than the balanced kernel keeps in LDS or more tiles than an int
+// indexes, one workgroup handles each chunk of split_tokens tokens of a
+// (sequence, KV head) pair.
 struct Plan {
-  int chunk;
-  int n_chunks;
+  int mode;
+  int max_len;
+  int chunk, n_chunks;    // chunks
+  int n_blocks, n_units;  // balanced
+  int64_t max_items;      // balanced: columns of the line
+  int line_heads;         // balanced: heads run per line item
 };
 
 static constexpr int64_t kTargetItems = 2048;
@@ -47,8 +53,22 @@ static constexpr int kChunkQuantum = kTile * kWaves;  // 64
 
 static int round_up(int64_t x, int q) { return (int)(((x + q - 1) / q) * q); }
 
-static Plan plan_chunks(int64_t est_tokens, int max_len, int split_tokens) {
-  Plan p;
+static Plan plan_attn(int dtype, int G, int src, int64_t pairs, int64_t n_units, int64_t est_tokens,
+                      int max_len, int split_tokens) {
+  Plan p = {};
+  p.max_len = std::max(max_len, 0);
+  const int64_t est_tiles = pairs * ((std::max(max_len, 1) + kTile - 1) / kTile);
+  if (split_tokens == 0 && n_units <= kMaxUnits && est_tiles < (int64_t(1) << 30)) {
+    p.mode = MODE_BALANCED;
+    p.n_units = (int)n_units;
+    p.n_blocks = balanced_blocks(dtype, G, src, est_tiles);
+    // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
+    const int64_t LH = pairs / std::max<int64_t>(n_units, 1);
+    p.max_items = (int64_t)p.n_blocks * kWaves / std::max<int64_t>(LH, 1);
+    p.line_heads = (int)LH;
+    return p;
+  }
+  p.mode = MODE_CHUNKS;
   const int full = std::max(kChunkQuantum, round_up(std::max(max_len, 1), kChunkQuantum));
   if (split_tokens > 0) {
     p.chunk = std::min(split_tokens, full);
@@ -57,10 +77,8 @@ static Plan plan_chunks(int64_t est_tokens, int max_len, int split_tokens) {
     c = std::max<int64_t>(c, kMinChunk);
     p.chunk = std::min(round_up(c, kChunkQuantum), full);
   }
-  // the merge kernel keeps every chunk's (max, sum) in LDS
-  const int min_chunk = round_up((std::max(max_len, 1) + kMaxChunks - 1) / kMaxChunks, kChunkQuantum);
-  p.chunk = std::max(p.chunk, min_chunk);
   p.n_chunks = (std::max(max_len, 1) + p.chunk - 1) / p.chunk;
+  p.max_len = std::min<int64_t>((int64_t)p.n_chunks * p.chunk, std::max(max_len, 0));
   return p;
 }
 
@@ -100,20 +118,39 @@ static kvdec_status check_common(const kvdec_attn_desc* d, bool check_layout) {
 
 static Plan plan_decode(const kvdec_attn_desc* d) {
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
-  return plan_chunks(pairs * (int64_t)d->max_seqlen, d->max_seqlen, d->split_tokens);
+  const int src = d->layout == KVDEC_DENSE ? SRC_DENSE : d->layout == KVDEC_RAGGED ? SRC_RAGGED : SRC_PAGED;
+  return plan_attn(d->dtype, d->num_q_heads / d->num_kv_heads, src, pairs, d->batch,
+                   pairs * (int64_t)d->max_seqlen, d->max_seqlen, d->split_tokens);
 }
 
 static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
   const kvdec_attn_desc* d = &h->base;
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
   const int64_t est = (int64_t)d->batch *
                       ((int64_t)h->num_pers_slots * h->pers_cap + (int64_t)d->num_kv_heads * h->buf_cap);
-  return plan_chunks(est, std::max(h->pers_cap, h->buf_cap), d->split_tokens);
+  return plan_attn(d->dtype, d->num_q_heads / d->num_kv_heads, SRC_HYBRID, pairs, pairs, est,
+                   std::max(h->pers_cap, h->buf_cap), d->split_tokens);
+}
+
+// Partial slots and prefix entries the plan needs in the workspace.
+static void ws_shape(const kvdec_attn_desc* d, const Plan& p, int64_t* slots, int64_t* n_pref) {
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
+  if (p.mode == MODE_BALANCED) {
+    // slot (item + unit) * LH + h
+    *slots = (p.max_items + p.n_units) * p.line_heads;
+    *n_pref = (int64_t)p.n_units + 1;
+  } else {
+    *slots = p.n_chunks > 1 ? pairs * p.n_chunks : 0;
+    *n_pref = 0;
+  }
 }
 
 static size_t attn_ws(const kvdec_attn_desc* d, const Plan& p) {
-  if (p.n_chunks <= 1 || d->batch == 0) return 0;
-  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
-  return attn_workspace_bytes(pairs * p.n_chunks, d->num_q_heads / d->num_kv_heads);
+  if (d->batch == 0) return 0;
+  int64_t slots, n_pref;
+  ws_shape(d, p, &slots, &n_pref);
+  if (slots == 0 && n_pref == 0) return 0;
+  return attn_workspace_bytes(slots, d->num_q_heads / d->num_kv_heads, n_pref);
 }
 
 static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
@@ -121,23 +158,27 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->Hq = d->num_q_heads;
   a->Hkv = d->num_kv_heads;
   a->G = d->num_q_heads / d->num_kv_heads;
+  a->mode = p.mode;
+  a->max_len = p.max_len;
   a->chunk = p.chunk;
   a->n_chunks = p.n_chunks;
+  a->n_blocks = p.n_blocks;
+  a->n_units = p.n_units;
   a->scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
   a->dtype = d->dtype;
 }
 
 static kvdec_status run_attn(const kvdec_attn_desc* d, const Plan& p, AttnArgs& a, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-  if (p.n_chunks > 1) {
-    const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
-    if (!attn_workspace_carve(ws, ws_bytes, pairs * p.n_chunks, a.G, &a))
+  int64_t slots, n_pref;
+  ws_shape(d, p, &slots, &n_pref);
+  if (slots > 0 || n_pref > 0) {
+    if (!attn_workspace_carve(ws, ws_bytes, slots, a.G, n_pref, &a))
       return fail(KVDEC_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", attn_ws(d, p),
                   ws_bytes, ws ? "" : " (NULL)");
   }
-  const int64_t blocks = (int64_t)d->batch * p.n_chunks * d->num_kv_heads;
-  if (blocks > INT32_MAX) return fail(KVDEC_ERR_UNSUPPORTED, "grid too large");
-  if (blocks == 0) return ok();
+  if (p.mode == MODE_CHUNKS && (int64_t)d->batch * p.n_chunks * d->num_kv_heads > INT32_MAX)
+    return fail(KVDEC_ERR_UNSUPPORTED, "grid too large");
   return hip_status(launch_decode_attn(a, stream), "decode attention launch");
 }
 

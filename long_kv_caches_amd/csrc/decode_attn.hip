@@ -3,35 +3,48 @@
 //
 // Operation: for one query token per sequence, out = softmax(scale q K^T) V
 // with grouped KV heads (KVPR page, section A3, MHA equation at the decode
-// step).  One request's tokens are split into independent work items whose
+// step).  One request's tokens are split into independent pieces whose
 // partial results are aggregated afterwards (Neo page, method details: the
 // Flash-Decoding style split along a request, then aggregation of partial
 // outputs), and paged KV follows the page pool + block table of the same page.
 //
-// Work decomposition (one workgroup = 4 waves = one work item):
-//   item = (sequence b, KV head g, chunk c of `chunk` tokens).
-//   Each wave walks 16-token tiles c*chunk + 16*(wave + 4i) of the item and
-//   keeps its own online-softmax state (running max m, sum l, output o) for
-//   the G query heads of KV head g.
-//   Lane l owns the 16-byte piece n = l % 16 (8 of the 128 elements) of rows
-//   4*(l/16) .. 4*(l/16)+3 of a tile, so every load instruction reads four
-//   whole 256-byte rows (fully coalesced) for K and for V alike.  Per tile:
-//     scores  v_dot2_f32_f16 (or _bf16) partial dots of the lane's piece with
-//             q, summed over the 16 pieces of a row by four DPP row steps;
-//     softmax tile max across the four row groups by permlane16/32 swaps,
-//             exp2 in log2 units (scores are pre-scaled by scale*log2 e);
-//     P.V     the probabilities are already in the lanes that hold the V
-//             rows: fp32 FMAs on the lane's 8 V elements.
-//   This op is HBM-bound (4-8 flops per byte), so the score dots stay on the
-//   vector ALU, where they need no operand reshuffle; no LDS is touched in
-//   the loop.
-//   The 4 waves merge through LDS.  A sequence covered by one item writes the
-//   normalised output directly; otherwise each item writes its partial
-//   (o, m, l) to the workspace and a second, small kernel merges the partials
-//   of each (b, g) in chunk order (so the result does not depend on which item
-//   finished first).  The kernel boundary orders the partial writes before the
-//   merge reads; no grid-wide fence or atomic is needed.
-#include <type_traits>
+// The unit of work is a 16-token tile of one (sequence b, KV head g) pair.  A
+// wave streams a run of tiles of one pair and keeps an online-softmax state
+// (running max m, sum l, output o) for the G query heads of KV head g.
+// Lane l owns the 16-byte piece n = l % 16 (8 of the 128 elements) of rows
+// 4*(l/16) .. 4*(l/16)+3 of a tile, so every load instruction reads four whole
+// 256-byte rows (fully coalesced) for K and for V alike.  Per tile:
+//   scores  v_dot2_f32_f16 (or _bf16) partial dots of the lane's piece with q,
+//           summed over the 16 pieces of a row by four DPP row steps;
+//   softmax tile max across the four row groups by permlane16/32 swaps, exp2
+//           in log2 units (scores are pre-scaled by scale * log2 e);
+//   P.V     the probabilities are already in the lanes that hold the V rows:
+//           fp32 FMAs on the lane's 8 V elements.
+// This op is HBM-bound (4-8 flops per byte), so the score dots stay on the
+// vector ALU, where they need no operand reshuffle; no LDS is used in the
+// tile loop.  Two register buffers alternate so the next tile's loads are in
+// flight while the current one is processed.
+//
+// Two schedules distribute the tiles:
+//   balanced (default) -- a persistent grid of CUs x occupancy workgroups.
+//     The tile line (all pairs in (b, g) order) is cut into items of a fixed
+//     number of tiles; waves take items from an atomic counter in the
+//     workspace until none is left.  Measured on MI355X, equal static shares
+//     end far apart (waves of the second resident workgroup on a CU, and of
+//     some XCDs, run slower), and the hardware hands workgroups to XCDs in
+//     order, so a fast XCD can starve; taking items dynamically keeps every
+//     wave busy to the end.  An item may cover the end of one pair and the
+//     start of the next: it writes one partial per pair it touches (or the
+//     final output when it covers a whole pair).  Partials are indexed by
+//     item, so which wave ran an item does not change the result.
+//   fixed chunks (split_tokens > 0) -- one workgroup per (b, g, chunk of
+//     split_tokens tokens); its four waves interleave the chunk's tiles and
+//     merge through LDS.  The partition then depends only on each sequence's
+//     own length.
+// In both, a second small kernel merges the partials of each pair in a fixed
+// order (so results do not depend on timing); the kernel boundary orders the
+// partial writes before the merge reads, with no grid-wide fence or atomic.
+#include <atomic>
 
 #include "device_common.h"
 #include "internal.h"
@@ -50,55 +63,347 @@ struct SeqView {
   int64_t stride;
 };
 
+// Length of pair (b, g), per thread (no uniformity assumed).
+template <int SRC>
+__device__ __forceinline__ int pair_len(const AttnArgs& a, int b, int g) {
+  int len;
+  if constexpr (SRC == SRC_DENSE) {
+    len = a.seqlens ? min(a.seqlens[b], a.S) : a.S;
+  } else if constexpr (SRC == SRC_RAGGED) {
+    // a.S holds the number of token rows T; offsets are clamped into [0, T].
+    const int start = min(max(a.cu_seqlens[b], 0), a.S);
+    len = min(max(a.cu_seqlens[b + 1], start), a.S) - start;
+  } else if constexpr (SRC == SRC_PAGED) {
+    len = min(a.seqlens[b], a.max_pages * a.page);
+  } else {  // SRC_HYBRID
+    const int slot = a.head_map[g];
+    if (slot >= 0) len = slot < a.P_slots ? min(a.pers_len[b], a.pers_cap) : 0;
+    else len = min(a.buf_len[b * a.Hkv + g], a.buf_cap);
+  }
+  return max(0, min(len, a.max_len));
+}
+
+// Rows of pair (b, g), for a wave that handles this pair.
 template <int SRC>
 __device__ __forceinline__ SeqView locate(const AttnArgs& a, int b, int g) {
   SeqView s;
   s.stride = (int64_t)a.Hkv * kHeadDim;
+  // Values loaded from memory are the same for the whole wave; say so, so
+  // that buffer descriptors built from them stay in scalar registers.
+  s.len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
   if constexpr (SRC == SRC_DENSE) {
-    s.len = a.seqlens ? min(a.seqlens[b], a.S) : a.S;
     const int64_t base = ((int64_t)b * a.S * a.Hkv + g) * kHeadDim;
     s.kb = a.k + base;
     s.vb = a.v + base;
   } else if constexpr (SRC == SRC_RAGGED) {
-    // a.S holds the number of token rows T; offsets are clamped into [0, T].
-    const int start = min(max(a.cu_seqlens[b], 0), a.S);
-    const int end = min(max(a.cu_seqlens[b + 1], start), a.S);
-    s.len = end - start;
+    const int start = __builtin_amdgcn_readfirstlane(min(max(a.cu_seqlens[b], 0), a.S));
     const int64_t base = ((int64_t)start * a.Hkv + g) * kHeadDim;
     s.kb = a.k + base;
     s.vb = a.v + base;
   } else if constexpr (SRC == SRC_PAGED) {
-    s.len = min(a.seqlens[b], a.max_pages * a.page);
     s.kb = a.k;
     s.vb = a.v;
   } else {  // SRC_HYBRID
     const int slot = __builtin_amdgcn_readfirstlane(a.head_map[g]);
     s.stride = kHeadDim;
     if (slot >= 0) {
-      s.len = slot < a.P_slots ? min(a.pers_len[b], a.pers_cap) : 0;
-      const int64_t base = ((int64_t)b * a.P_slots + slot) * a.pers_cap * kHeadDim;
+      const int64_t base = ((int64_t)b * a.P_slots + min(slot, max(a.P_slots - 1, 0))) *
+                           a.pers_cap * kHeadDim;
       s.kb = a.k + base;
       s.vb = a.v + base;
     } else {
-      s.len = min(a.buf_len[b * a.Hkv + g], a.buf_cap);
       const int64_t base = ((int64_t)b * a.Hkv + g) * a.buf_cap * kHeadDim;
       s.kb = a.k2 + base;
       s.vb = a.v2 + base;
     }
   }
-  // Values loaded from memory are the same for the whole workgroup; say so,
-  // so that buffer descriptors built from them stay in scalar registers.
-  s.len = __builtin_amdgcn_readfirstlane(max(0, min(s.len, a.n_chunks * a.chunk)));
   return s;
 }
 
+// Online-softmax state of one wave for G query heads; every lane holds the
+// same m and l, and o for its own 8-element piece (per row group until
+// finish() sums the row groups).
+template <int G>
+struct WaveState {
+  float m[G], l[G], o[G][8];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+  }
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      l[j] = rowgroup_sum(l[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = rowgroup_sum(o[j][e]);
+    }
+  }
+};
+
+// q piece n of each query head of the group (8 elements, 4 packed words).
+template <int G>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int64_t head0, int n, u32x4 (&qf)[G]) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) qf[j] = load_b128(a.q + (head0 + j) * kHeadDim + 8 * n);
+}
+
+// Byte offsets, within a tile, of the four rows of this lane: rows 4*lg + i,
+// piece n.
+__device__ __forceinline__ void tile_row_offsets(uint32_t row_bytes, int lane, uint32_t (&row_off)[4]) {
+  const int n = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row_off[i] = (4 * lg + i) * row_bytes + 16 * n;
+}
+
+template <int SRC>
+__device__ __forceinline__ uint32_t tile_row_bytes(const AttnArgs& a) {
+  return SRC == SRC_PAGED ? kHeadDim * 2 : SRC == SRC_HYBRID ? kHeadDim * 2 : (uint32_t)a.Hkv * kHeadDim * 2;
+}
+
+// Loads K and V of the tile whose first row is t0 of pair (b, g) into kf, vf.
+// The rows come through buffer resources whose base is the tile's first row
+// (scalar registers) and whose size covers only rows below len, so rows past
+// the end of the sequence, and a tile with active == false, read as zeros with
+// no memory traffic.
+template <int SRC>
+__device__ __forceinline__ void load_kv_tile(const AttnArgs& a, int b, int g, const uint16_t* kb,
+                                             const uint16_t* vb, int len, int t0, bool active,
+                                             const uint32_t (&row_off)[4], u32x4 (&kf)[4],
+                                             u32x4 (&vf)[4]) {
+  const uint32_t row_bytes = tile_row_bytes<SRC>(a);
+  const int rows = active ? min(len - t0, kTile) : 0;
+  int64_t row0;  // element offset of the tile's first row
+  if constexpr (SRC == SRC_PAGED) {
+    int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
+    pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
+    row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;  // never straddles pages
+  } else {
+    row0 = (int64_t)t0 * (row_bytes / 2);
+  }
+  const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, row_off[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, row_off[i]);
+}
+
+// Online-softmax update of st with the tile whose first row is t0 (rows at or
+// past len are masked out; the tile holds at least one row below len).
+template <int KIND, int G>
+__device__ __forceinline__ void process_tile(const AttnArgs& a, const u32x4 (&qf)[G],
+                                             const u32x4 (&kf)[4], const u32x4 (&vf)[4], int t0,
+                                             int len, int lg, WaveState<G>& st) {
+  float sc[4][G];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool valid = t0 + 4 * lg + i < len;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part = dot2<KIND>(kf[i][e], qf[j][e], part);
+      const float full = row_sum16(part);
+      sc[i][j] = valid ? full * a.scale_log2 : -INFINITY;
+    }
+  }
+  bool grew = false;
+  float alpha[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float tmax = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
+    tmax = rowgroup_max(tmax);
+    const float m_new = fmaxf(st.m[j], tmax);  // finite: every tile has a valid token
+    alpha[j] = fast_exp2(st.m[j] - m_new);
+    grew |= m_new > st.m[j];
+    st.m[j] = m_new;
+  }
+  float p[4][G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i][j] = fast_exp2(sc[i][j] - st.m[j]);
+    st.l[j] = st.l[j] * alpha[j] + ((p[0][j] + p[1][j]) + (p[2][j] + p[3][j]));
+  }
+  if (__builtin_amdgcn_readfirstlane((int)grew)) {  // the same in every lane
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.o[j][e] *= alpha[j];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float vv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[2 * e] = lo_f32<KIND>(vf[i][e]);
+      vv[2 * e + 1] = hi_f32<KIND>(vf[i][e]);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.o[j][e] = __builtin_fmaf(p[i][j], vv[e], st.o[j][e]);
+  }
+}
+
+// Streams tiles tile_first + k * tile_step (k < count) of pair (b, g) into st.
 template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void run_tiles(const AttnArgs& a, int b, int g, const SeqView& sq,
+                                          const u32x4 (&qf)[G], int tile_first, int count,
+                                          int tile_step, WaveState<G>& st) {
+  const int lane = threadIdx.x & 63;
+  const int lg = lane >> 4;
+  uint32_t row_off[4];
+  tile_row_offsets(tile_row_bytes<SRC>(a), lane, row_off);
+  auto load = [&](int k, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
+    load_kv_tile<SRC>(a, b, g, sq.kb, sq.vb, sq.len, (tile_first + k * tile_step) * kTile, k < count,
+                      row_off, kf, vf);
+  };
+  auto process = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4], int k) {
+    process_tile<KIND, G>(a, qf, kf, vf, (tile_first + k * tile_step) * kTile, sq.len, lg, st);
+  };
+
+  // Ping-pong: loads are unconditional (a tile past the run reads nothing), so
+  // no branch or register copy forces an early wait on the prefetch.
+  if (count <= 0) return;
+  u32x4 ka[4], va[4], kb[4], vb[4];
+  load(0, ka, va);
+  for (int k = 0;; k += 2) {
+    load(k + 1, kb, vb);
+    process(ka, va, k);
+    if (k + 1 >= count) break;
+    load(k + 2, ka, va);
+    process(kb, vb, k + 1);
+    if (k + 2 >= count) break;
+  }
+}
+
+// Final output of G heads from a finished wave state (lanes of row group 0).
+template <int KIND, int G>
+__device__ __forceinline__ void store_output(const AttnArgs& a, int64_t head0, const WaveState<G>& st,
+                                             int lane) {
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float inv = 1.f / st.l[j];
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)to_bits<KIND>(st.o[j][2 * e] * inv) |
+               ((uint32_t)to_bits<KIND>(st.o[j][2 * e + 1] * inv) << 16);
+      store_b128(a.out + (head0 + j) * kHeadDim + 8 * lane, u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+  if (lane == 0 && a.lse) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) a.lse[head0 + j] = (st.m[j] + __builtin_log2f(st.l[j])) * kLn2;
+  }
+}
+
+// Unnormalised partial of G heads into workspace slot `slot`.
+template <int G>
+__device__ __forceinline__ void store_partial(const AttnArgs& a, int64_t slot, const WaveState<G>& st,
+                                              int lane) {
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float* dst = a.ws_o + (slot * G + j) * kHeadDim + 8 * lane;
+      store_b128(dst, u32x4{__builtin_bit_cast(uint32_t, st.o[j][0]), __builtin_bit_cast(uint32_t, st.o[j][1]),
+                            __builtin_bit_cast(uint32_t, st.o[j][2]), __builtin_bit_cast(uint32_t, st.o[j][3])});
+      store_b128(dst + 4, u32x4{__builtin_bit_cast(uint32_t, st.o[j][4]), __builtin_bit_cast(uint32_t, st.o[j][5]),
+                                __builtin_bit_cast(uint32_t, st.o[j][6]), __builtin_bit_cast(uint32_t, st.o[j][7])});
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      a.ws_ml[(slot * G + j) * 2] = st.m[j];
+      a.ws_ml[(slot * G + j) * 2 + 1] = st.l[j];
+    }
+  }
+}
+
+template <int KIND, int G>
+__device__ __forceinline__ void store_empty(const AttnArgs& a, int64_t head0) {
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
+    a.out[(head0 + (idx >> 7)) * kHeadDim + (idx & 127)] = 0;
+    if ((idx & 127) == 0 && a.lse) a.lse[head0 + (idx >> 7)] = -INFINITY;
+  }
+}
+
+// Merges n_p >= 1 partials of query head j of a group (slots slot0 +
+// i * slot_step, i < n_p) into the final output and lse of head head0 + j:
+// out = sum_i w_i o_i / sum_i w_i l_i with w_i = 2^(m_i - M), M = max_i m_i.
+// Thread (c, r) of the 256 takes elements 4c .. 4c+3 of the partials
+// i = r, r + 8, ... in order; the eight running sums are then added in the
+// order r = 0 .. 7, so the result does not depend on timing.
+template <int KIND, int G>
+__device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot0, int slot_step,
+                           int n_p) {
+  __shared__ float s_max[kWaves];
+  __shared__ f32x4 s_acc[8][32];
+  __shared__ float s_l[8];
+  const int tid = threadIdx.x, c = tid & 31, r = tid >> 5;
+  float m = -INFINITY;
+  for (int i = tid; i < n_p; i += 256) m = fmaxf(m, a.ws_ml[((slot0 + (int64_t)i * slot_step) * G + j) * 2]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if ((tid & 63) == 0) s_max[tid >> 6] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, lsum = 0.f;
+#pragma unroll 4
+  for (int i = r; i < n_p; i += 8) {
+    const int64_t sj = (slot0 + (int64_t)i * slot_step) * G + j;
+    const float mi = a.ws_ml[sj * 2], li = a.ws_ml[sj * 2 + 1];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + sj * kHeadDim + 4 * c);
+    const float w = fast_exp2(mi - M);
+    acc0 = __builtin_fmaf(w, o.x, acc0);
+    acc1 = __builtin_fmaf(w, o.y, acc1);
+    acc2 = __builtin_fmaf(w, o.z, acc2);
+    acc3 = __builtin_fmaf(w, o.w, acc3);
+    lsum = __builtin_fmaf(w, li, lsum);
+  }
+  s_acc[r][c] = f32x4{acc0, acc1, acc2, acc3};
+  if (c == 0) s_l[r] = lsum;
+  __syncthreads();
+  if (r == 0) {
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, L = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const f32x4 v = s_acc[rr][c];
+      o0 += v.x;
+      o1 += v.y;
+      o2 += v.z;
+      o3 += v.w;
+      L += s_l[rr];
+    }
+    const float inv = 1.f / L;
+    const uint32_t w0 = (uint32_t)to_bits<KIND>(o0 * inv) | ((uint32_t)to_bits<KIND>(o1 * inv) << 16);
+    const uint32_t w1 = (uint32_t)to_bits<KIND>(o2 * inv) | ((uint32_t)to_bits<KIND>(o3 * inv) << 16);
+    *reinterpret_cast<uint2*>(a.out + (head0 + j) * kHeadDim + 4 * c) = make_uint2(w0, w1);
+    if (c == 0 && a.lse) a.lse[head0 + j] = (M + __builtin_log2f(L)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-chunk schedule: one workgroup per (b, g, chunk).
+// ---------------------------------------------------------------------------
+
+template <int KIND, int G, int SRC>
+__global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
   static_assert(G >= 1 && G <= kMaxGroup, "group size");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int n = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
 
   int bid = blockIdx.x;
   const int g = bid % a.Hkv;
@@ -109,162 +414,37 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
   const SeqView sq = locate<SRC>(a, b, g);
   const int len = sq.len;
   const int n_c = (len + a.chunk - 1) / a.chunk;
-  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;  // first query head row
-
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
   if (len == 0) {
-    if (c == 0) {
-      for (int idx = tid; idx < G * kHeadDim; idx += 256) {
-        a.out[(head0 + (idx >> 7)) * kHeadDim + (idx & 127)] = 0;
-        if ((idx & 127) == 0 && a.lse) a.lse[head0 + (idx >> 7)] = -INFINITY;
-      }
-    }
+    if (c == 0) store_empty<KIND, G>(a, head0);
     return;
   }
   if (c >= n_c) return;
 
-  // q piece n of each query head of the group (8 elements, 4 packed words).
   u32x4 qf[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) qf[j] = load_b128(a.q + (head0 + j) * kHeadDim + 8 * n);
-
-  const int t_lo = c * a.chunk;
-  const int t_hi = min(len, t_lo + a.chunk);
-  const int n_tiles = (t_hi - t_lo + kTile - 1) / kTile;
-
-  // K/V rows of one 16-token tile come through buffer resources whose base is
-  // the tile's first row (scalar registers) and whose size covers only the
-  // rows below len: rows past the end of the sequence, and whole tiles past
-  // the wave's last one, read as zeros with no memory traffic.  Per-lane
-  // offsets are the same for every tile.
-  const uint32_t row_bytes = (SRC == SRC_PAGED) ? kHeadDim * 2 : (uint32_t)(sq.stride * 2);
-  uint32_t row_off[4];  // this lane's rows 4*lg + i, piece n
-#pragma unroll
-  for (int i = 0; i < 4; ++i) row_off[i] = (4 * lg + i) * row_bytes + 16 * n;
-
-  auto load_tile = [&](int kt, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
-    const int t0 = t_lo + kTile * kt;
-    const int rows = kt < n_tiles ? min(len - t0, kTile) : 0;
-    int64_t row0;  // element offset of the tile's first row
-    if constexpr (SRC == SRC_PAGED) {
-      int pg = kt < n_tiles ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
-      pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
-      row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;  // tiles never straddle pages
-    } else {
-      row0 = (int64_t)t0 * sq.stride;
-    }
-    const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(sq.kb + row0), nbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(sq.vb + row0), nbytes);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, row_off[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, row_off[i]);
-  };
-
-  // Online-softmax state; every lane holds the same m and l (per head).
-  float m_run[G], l_run[G], o[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-  }
-
-  // One 16-token tile: scores, online softmax, P.V accumulation.
-  auto process = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4], int kt) {
-    const int t0 = t_lo + kTile * kt;
-    float sc[4][G];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = t0 + 4 * lg + i < len;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part = dot2<KIND>(kf[i][e], qf[j][e], part);
-        const float full = row_sum16(part);
-        sc[i][j] = valid ? full * a.scale_log2 : -INFINITY;
-      }
-    }
-    bool grew = false;
-    float alpha[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float tmax = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
-      tmax = rowgroup_max(tmax);
-      const float m_new = fmaxf(m_run[j], tmax);  // finite: every tile has a valid token
-      alpha[j] = fast_exp2(m_run[j] - m_new);
-      grew |= m_new > m_run[j];
-      m_run[j] = m_new;
-    }
-    float p[4][G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i][j] = fast_exp2(sc[i][j] - m_run[j]);
-      l_run[j] = l_run[j] * alpha[j] + ((p[0][j] + p[1][j]) + (p[2][j] + p[3][j]));
-    }
-    if (__builtin_amdgcn_readfirstlane((int)grew)) {  // the same in every lane
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] *= alpha[j];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vv[2 * e] = lo_f32<KIND>(vf[i][e]);
-        vv[2 * e + 1] = hi_f32<KIND>(vf[i][e]);
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = __builtin_fmaf(p[i][j], vv[e], o[j][e]);
-    }
-  };
-
-  // Two register buffers in ping-pong: the next tile's loads are in flight
-  // while the current one is processed.  Loads are unconditional (a tile past
-  // the wave's last one reads nothing), so no branch or register copy forces
-  // an early wait.
-  if (wave < n_tiles) {
-    u32x4 ka[4], va[4], kb[4], vb[4];
-    load_tile(wave, ka, va);
-    for (int kt = wave;; kt += 2 * kWaves) {
-      load_tile(kt + kWaves, kb, vb);
-      process(ka, va, kt);
-      if (kt + kWaves >= n_tiles) break;
-      load_tile(kt + 2 * kWaves, ka, va);
-      process(kb, vb, kt + kWaves);
-      if (kt + 2 * kWaves >= n_tiles) break;
-    }
-  }
-
-  // Sum the four row groups (they hold different rows of the same pieces).
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    l_run[j] = rowgroup_sum(l_run[j]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = rowgroup_sum(o[j][e]);
-  }
+  load_q<G>(a, head0, n, qf);
+  const int tile0 = c * (a.chunk / kTile);
+  const int n_tiles = (min(len, (c + 1) * a.chunk) - c * a.chunk + kTile - 1) / kTile;
+  const int mine = n_tiles > wave ? (n_tiles - 1 - wave) / kWaves + 1 : 0;
+  WaveState<G> st;
+  st.init();
+  run_tiles<KIND, G, SRC>(a, b, g, sq, qf, tile0 + wave, mine, kWaves, st);
+  st.finish();
 
   // Merge the four waves through LDS.
   __shared__ float sm_o[kWaves][G][kHeadDim];
   __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
-  if (lg == 0) {
+  if (lane < 16) {
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][j][8 * n + e] = o[j][e];
+      for (int e = 0; e < 8; ++e) sm_o[wave][j][8 * n + e] = st.o[j][e];
   }
   if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      sm_m[wave][j] = m_run[j];
-      sm_l[wave][j] = l_run[j];
+      sm_m[wave][j] = st.m[j];
+      sm_l[wave][j] = st.l[j];
     }
   }
   __syncthreads();
@@ -278,7 +458,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sm_m[w][j] - M);
+      const float wt = fast_exp2(sm_m[w][j] - M);  // 0 for a wave with no tiles
       num = __builtin_fmaf(wt, sm_o[w][j][d], num);
       den = __builtin_fmaf(wt, sm_l[w][j], den);
     }
@@ -293,62 +473,330 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(AttnArgs a) {
       }
     }
   }
-  if (n_c == 1) return;
 }
 
-// Merges the partials of one (sequence, KV head) pair: out = sum_c w_c o_c /
-// sum_c w_c l_c with w_c = 2^(m_c - M), M = max_c m_c, chunks in order.
+// One workgroup per (pair, query head of the group).
 template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
-  __shared__ float s_w[kMaxChunks * G];  // m_c, then the weights 2^(m_c - M)
-  __shared__ float s_l[kMaxChunks * G];
-  __shared__ float s_M[G], s_L[G];
-  const int tid = threadIdx.x;
-  const int g = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
-  const int len = locate<SRC>(a, b, g).len;
+__global__ __launch_bounds__(256) void decode_chunk_merge_kernel(AttnArgs a) {
+  const int j = blockIdx.x % G, p = blockIdx.x / G;
+  const int g = p % a.Hkv, b = p / a.Hkv;
+  const int len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
   const int n_c = (len + a.chunk - 1) / a.chunk;
-  if (n_c <= 1) return;  // written by the split kernel
-  const int64_t item0 = ((int64_t)b * a.Hkv + g) * a.n_chunks;
-  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  if (n_c <= 1) return;  // written by the chunk kernel
+  merge_head<KIND, G>(a, (int64_t)b * a.Hq + (int64_t)g * G, j, (int64_t)p * a.n_chunks, 1, n_c);
+}
 
-  for (int i = tid; i < n_c * G; i += 256) {
-    s_w[i] = a.ws_ml[(item0 * G + i) * 2];
-    s_l[i] = a.ws_ml[(item0 * G + i) * 2 + 1];
+// ---------------------------------------------------------------------------
+// Balanced schedule: persistent waves taking items of the tile line.
+// ---------------------------------------------------------------------------
+
+// Tile line: the tiles of one KV head of every unit, units in order; unit
+// u = sequence b, whose Hkv heads share one length, or, for the hybrid
+// source, pair u (lengths differ per KV head).  Item k of the line is run
+// for every line head h < LH (LH = Hkv, or 1 for the hybrid source) as item
+// k * LH + h, so waves that run at the same time read all heads of the same
+// token rows: each 2 KB row of the [tokens, Hkv, 128] cache is then read
+// whole within a short time, where one head's 256 B pieces read alone leave
+// most of each DRAM row unused (measured on MI355X: a line of whole pairs
+// was about 20% slower).  The first tile of unit u is pref[u], pref[n_units]
+// is the line length; the unit's length and, for the ragged source, its
+// first token row (for the hybrid source, its persistent slot) are kept
+// beside it, so that finding a unit needs no global load.
+template <int SRC>
+__device__ __forceinline__ int line_heads(const AttnArgs& a) {
+  return SRC == SRC_HYBRID ? 1 : a.Hkv;
+}
+
+struct UnitTable {
+  int* pref;  // [n_units + 1]
+  int* len;   // [n_units]
+  int* aux;   // [n_units]
+};
+
+template <int SRC>
+__device__ void build_units(const AttnArgs& a, const UnitTable& ut) {
+  __shared__ int s_wave[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nu = a.n_units;
+  const int per = (nu + 255) / 256;
+  const int u0 = min(nu, tid * per), u1 = min(nu, u0 + per);
+  int local = 0;
+  for (int u = u0; u < u1; ++u) {
+    const int b = SRC == SRC_HYBRID ? u / a.Hkv : u;
+    const int g = SRC == SRC_HYBRID ? u % a.Hkv : 0;
+    const int len = pair_len<SRC>(a, b, g);
+    ut.len[u] = len;
+    if constexpr (SRC == SRC_RAGGED) ut.aux[u] = min(max(a.cu_seqlens[b], 0), a.S);
+    else if constexpr (SRC == SRC_HYBRID) ut.aux[u] = a.head_map[g];
+    else ut.aux[u] = 0;
+    local += (len + kTile - 1) / kTile;
   }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int c = 0; c < n_c; ++c) M = fmaxf(M, s_w[c * G + tid]);
-    s_M[tid] = M;
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
+  if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
-  for (int i = tid; i < n_c * G; i += 256) s_w[i] = fast_exp2(s_w[i] - s_M[i % G]);
-  __syncthreads();
-  if (tid < G) {
-    float L = 0.f;
-    for (int c = 0; c < n_c; ++c) L = __builtin_fmaf(s_w[c * G + tid], s_l[c * G + tid], L);
-    s_L[tid] = L;
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  int run = base + incl - local;
+  for (int u = u0; u < u1; ++u) {
+    ut.pref[u] = run;
+    run += (ut.len[u] + kTile - 1) / kTile;
   }
+  if (tid == 255) ut.pref[nu] = base + incl;
   __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
-    const int j = idx >> 7, d = idx & 127;
-    const float* po = a.ws_o + (item0 * G + j) * kHeadDim + d;
-    float num = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < n_c; ++c) num = __builtin_fmaf(s_w[c * G + j], po[(int64_t)c * G * kHeadDim], num);
-    a.out[(head0 + j) * kHeadDim + d] = to_bits<KIND>(num / s_L[j]);
-    if (d == 0 && a.lse) a.lse[head0 + j] = (s_M[j] + __builtin_log2f(s_L[j])) * kLn2;
+}
+
+// Items of the line: column k < Wc <= (persistent waves) / LH holds line
+// tiles [k N / Wc, (k + 1) N / Wc), and item k * LH + h (column k, line
+// head h) belongs to persistent wave k * LH + h.  The main and the merge
+// kernel cut the line the same way from its length N.
+struct ItemLine {
+  int N, Wc;
+  __device__ int first(int k) const { return (int)((int64_t)k * N / Wc); }
+  // the column that holds tile x (x < N)
+  __device__ int of_tile(int x) const { return (int)(((int64_t)(x + 1) * Wc - 1) / N); }
+};
+
+// At most N columns, so that none is empty.
+__device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) {
+  return ItemLine{N, min(a.n_blocks * kWaves / LH, N)};
+}
+
+// Waves of the workgroups that reach a CU first win most arbitration
+// (oldest first), so with equal shares they end far ahead of the others
+// (measured on MI355X: mean end 238 vs 265 us on the 16 x 16K-32K ragged
+// batch even with the steps below, 199 vs 261 us without).  A wave starts its
+// share at the highest priority and steps down a level at each quarter done,
+// so the waves that are behind get served first.
+__device__ __forceinline__ void set_progress_priority(int level) {
+  switch (level) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
   }
 }
+
+// A run of tiles of one pair inside one item: tiles [x0, x1) of the line,
+// the first of them tile t of the pair.  All fields are wave-uniform.
+struct Seg {
+  int x0, x1, t;
+  int b, g, len;
+  int slot;    // partial slot: (column + unit) * LH + line head
+  bool whole;  // the run is the whole pair
+  const uint16_t* kb;
+  const uint16_t* vb;
+};
+
+// The run that starts at line tile x of column `item` (ending at hi), head h.
+template <int SRC>
+__device__ __forceinline__ Seg seg_at(const AttnArgs& a, const UnitTable& ut, int x, int item, int hi,
+                                      int h) {
+  int lo_u = 0, hi_u = a.n_units;  // largest u with pref[u] <= x
+  while (hi_u - lo_u > 1) {
+    const int mid = (lo_u + hi_u) >> 1;
+    if (uniform_i32(ut.pref[mid]) <= x) lo_u = mid;
+    else hi_u = mid;
+  }
+  const int u = uniform_i32(lo_u);
+  const int ubase = uniform_i32(ut.pref[u]);
+  const int uend = uniform_i32(ut.pref[u + 1]);
+  const int LH = line_heads<SRC>(a);
+  Seg sg;
+  sg.x0 = x;
+  sg.x1 = uniform_i32(min(hi, uend));
+  sg.t = x - ubase;
+  sg.b = SRC == SRC_HYBRID ? u / a.Hkv : u;
+  sg.g = SRC == SRC_HYBRID ? u % a.Hkv : h;
+  sg.len = uniform_i32(ut.len[u]);
+  sg.slot = (item + u) * LH + h;
+  sg.whole = x == ubase && sg.x1 == uend;
+  const int aux = uniform_i32(ut.aux[u]);
+  if constexpr (SRC == SRC_DENSE) {
+    const int64_t base = ((int64_t)sg.b * a.S * a.Hkv + sg.g) * kHeadDim;
+    sg.kb = a.k + base;
+    sg.vb = a.v + base;
+  } else if constexpr (SRC == SRC_RAGGED) {
+    const int64_t base = ((int64_t)aux * a.Hkv + sg.g) * kHeadDim;
+    sg.kb = a.k + base;
+    sg.vb = a.v + base;
+  } else if constexpr (SRC == SRC_PAGED) {
+    sg.kb = a.k;
+    sg.vb = a.v;
+  } else {  // SRC_HYBRID: aux is the persistent slot, or < 0 for the cache buffer
+    if (aux >= 0) {
+      const int64_t base = ((int64_t)sg.b * a.P_slots + min(aux, max(a.P_slots - 1, 0))) *
+                           a.pers_cap * kHeadDim;
+      sg.kb = a.k + base;
+      sg.vb = a.v + base;
+    } else {
+      const int64_t base = ((int64_t)sg.b * a.Hkv + sg.g) * a.buf_cap * kHeadDim;
+      sg.kb = a.k2 + base;
+      sg.vb = a.v2 + base;
+    }
+  }
+  return sg;
+}
+
+// Persistent waves stream the tiles of their items as one sequence: the
+// loads for the next tile are issued while the current one is processed,
+// also where the next tile starts another pair or another item, so a wave's
+// loads stay in flight across item boundaries.  When the processed tile ends
+// its run, the state goes out (as the pair's output when the run is the whole
+// pair, else as the partial of slot item + pair) and the next run begins.
+template <int KIND, int G, int SRC>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
+  extern __shared__ int s_units[];
+  const UnitTable ut{s_units, s_units + a.n_units + 1, s_units + 2 * a.n_units + 1};
+  build_units<SRC>(a, ut);
+  if (blockIdx.x == 0)
+    for (int u = threadIdx.x; u <= a.n_units; u += 256) a.ws_pref[u] = ut.pref[u];
+
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const int LH = line_heads<SRC>(a);
+  const ItemLine L = item_line(a, uniform_i32(ut.pref[a.n_units]), LH);
+  const int gw = uniform_i32((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6));
+  const int lk = gw / LH, lh = gw - (gw / LH) * LH;
+  if (lk >= L.Wc) return;
+  const int x_end = uniform_i32(L.first(lk + 1));
+  const int share = x_end - uniform_i32(L.first(lk));
+  if (share <= 0) return;
+  int done = 0;
+  set_progress_priority(3);
+
+  uint32_t row_off[4];
+  tile_row_offsets(tile_row_bytes<SRC>(a), lane, row_off);
+
+  // Load side: run ls, next tile to load lx; `more` is false once the share
+  // is loaded.
+  Seg ls = seg_at<SRC>(a, ut, L.first(lk), lk, x_end, lh);
+  int lx = ls.x0;
+  bool more = true;
+  // Process side: run ps, next tile to process px.
+  Seg ps = ls;
+  int px = lx;
+  u32x4 qf[G], qn[G];
+  load_q<G>(a, (int64_t)ps.b * a.Hq + (int64_t)ps.g * G, lane & 15, qf);
+  WaveState<G> st;
+  st.init();
+
+  auto advance = [&]() {
+    if (!more) return;
+    if (++lx < ls.x1) return;
+    if (lx >= x_end) {
+      more = false;
+      return;
+    }
+    ls = seg_at<SRC>(a, ut, lx, lk, x_end, lh);  // the next unit
+    load_q<G>(a, (int64_t)ls.b * a.Hq + (int64_t)ls.g * G, lane & 15, qn);
+  };
+  auto load = [&](u32x4 (&kf)[4], u32x4 (&vf)[4]) {
+    load_kv_tile<SRC>(a, ls.b, ls.g, ls.kb, ls.vb, ls.len, (ls.t + lx - ls.x0) * kTile, more, row_off,
+                      kf, vf);
+  };
+  // Processes tile px; returns false when nothing is left to process.
+  auto step = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4]) -> bool {
+    process_tile<KIND, G>(a, qf, kf, vf, (ps.t + px - ps.x0) * kTile, ps.len, lg, st);
+    ++done;
+    if ((4 * done) / share != (4 * (done - 1)) / share) set_progress_priority(3 - (4 * done) / share);
+    if (++px < ps.x1) return true;
+    st.finish();
+    // A fresh copy of the lane index: address arithmetic that depends on it
+    // is then done here, instead of being hoisted and kept live in the loop.
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
+    const int64_t head0 = (int64_t)ps.b * a.Hq + (int64_t)ps.g * G;
+    if (ps.whole) store_output<KIND, G>(a, head0, st, lane_s);
+    else store_partial<G>(a, ps.slot, st, lane_s);
+    st.init();
+    if (!more) return false;
+    // The loaded tile after the finished run starts run ls.
+    ps = ls;
+    px = ps.x0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) qf[j] = qn[j];
+    return true;
+  };
+
+  u32x4 ka[4], va[4], kb[4], vb[4];
+  load(ka, va);
+  for (;;) {
+    advance();
+    load(kb, vb);
+    if (!step(ka, va)) break;
+    advance();
+    load(ka, va);
+    if (!step(kb, vb)) break;
+  }
+}
+
+// One workgroup per (pair, query head of the group).  The partial of item k
+// and unit u for line head h is slot (k + u) * LH + h: items grow along the
+// line and units follow it, so no two runs share a slot, and the slots of
+// one pair are LH apart.
+template <int KIND, int G, int SRC>
+__global__ __launch_bounds__(256) void decode_balanced_merge_kernel(AttnArgs a) {
+  const int j = blockIdx.x % G, p = blockIdx.x / G;
+  const int b = p / a.Hkv, g = p % a.Hkv;
+  const int LH = line_heads<SRC>(a);
+  const int u = SRC == SRC_HYBRID ? p : b, h = SRC == SRC_HYBRID ? 0 : g;
+  const int ubase = a.ws_pref[u], uend = a.ws_pref[u + 1];
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  if (uend == ubase) {
+    if (threadIdx.x < kHeadDim) a.out[(head0 + j) * kHeadDim + threadIdx.x] = 0;
+    if (threadIdx.x == 0 && a.lse) a.lse[head0 + j] = -INFINITY;
+    return;
+  }
+  const ItemLine L = item_line(a, a.ws_pref[a.n_units], LH);
+  const int k0 = L.of_tile(ubase), k1 = L.of_tile(uend - 1);  // columns, each non-empty
+  if (k0 == k1) return;  // one item covered the pair and wrote the output
+  merge_head<KIND, G>(a, head0, j, (int64_t)(k0 + u) * LH + h, LH, k1 - k0 + 1);
+}
+
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
 
 template <int KIND, int G, int SRC>
 hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv)), block(256);
-  decode_attn_kernel<KIND, G, SRC><<<grid, block, 0, stream>>>(a);
+  const dim3 block(256);
+  if (a.mode == MODE_BALANCED) {
+    const size_t lds = (size_t)(3 * a.n_units + 1) * sizeof(int);
+    decode_balanced_kernel<KIND, G, SRC><<<dim3((unsigned)a.n_blocks), block, lds, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv));
+  decode_chunk_kernel<KIND, G, SRC><<<grid, block, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
-  decode_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv)), block, 0, stream>>>(a);
+  decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int KIND, int G, int SRC>
+int balanced_occupancy() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int occ = 0;
+  const size_t lds = (size_t)(3 * kMaxUnits + 1) * sizeof(int);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &occ, reinterpret_cast<const void*>(decode_balanced_kernel<KIND, G, SRC>), 256, lds) !=
+          hipSuccess ||
+      occ < 1) {
+    (void)hipGetLastError();
+    occ = 2;
+  }
+  cached.store(occ, std::memory_order_relaxed);
+  return occ;
 }
 
 template <int KIND, int G>
@@ -361,39 +809,91 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   }
 }
 
-template <int KIND>
-hipError_t launch_kind(const AttnArgs& a, hipStream_t stream) {
-  switch (a.G) {
-    case 1: return launch_g<KIND, 1>(a, stream);
-    case 2: return launch_g<KIND, 2>(a, stream);
-    case 3: return launch_g<KIND, 3>(a, stream);
-    case 4: return launch_g<KIND, 4>(a, stream);
-    case 5: return launch_g<KIND, 5>(a, stream);
-    case 6: return launch_g<KIND, 6>(a, stream);
-    case 7: return launch_g<KIND, 7>(a, stream);
-    case 8: return launch_g<KIND, 8>(a, stream);
-    default: return hipErrorInvalidValue;
+template <int KIND, int G>
+int occupancy_g(int src) {
+  switch (src) {
+    case SRC_DENSE: return balanced_occupancy<KIND, G, SRC_DENSE>();
+    case SRC_RAGGED: return balanced_occupancy<KIND, G, SRC_RAGGED>();
+    case SRC_PAGED: return balanced_occupancy<KIND, G, SRC_PAGED>();
+    default: return balanced_occupancy<KIND, G, SRC_HYBRID>();
   }
+}
+
+template <int KIND, template <int, int> class F, typename... Args>
+auto dispatch_g(int G, Args... args) {
+  switch (G) {
+    case 1: return F<KIND, 1>::run(args...);
+    case 2: return F<KIND, 2>::run(args...);
+    case 3: return F<KIND, 3>::run(args...);
+    case 4: return F<KIND, 4>::run(args...);
+    case 5: return F<KIND, 5>::run(args...);
+    case 6: return F<KIND, 6>::run(args...);
+    case 7: return F<KIND, 7>::run(args...);
+    default: return F<KIND, 8>::run(args...);
+  }
+}
+
+template <int KIND, int G>
+struct LaunchF {
+  static hipError_t run(const AttnArgs& a, hipStream_t s) { return launch_g<KIND, G>(a, s); }
+};
+template <int KIND, int G>
+struct OccF {
+  static int run(int src) { return occupancy_g<KIND, G>(src); }
+};
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 }  // namespace
 
-size_t attn_workspace_bytes(int64_t items, int G) {
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  return up((size_t)items * G * kHeadDim * 4) + up((size_t)items * G * 2 * 4);
+int balanced_blocks(int dtype, int G, int src, int64_t est_tiles) {
+  if (G < 1 || G > kMaxGroup) return 1;
+  const int occ = dtype == KIND_F16 ? dispatch_g<KIND_F16, OccF>(G, src)
+                                    : dispatch_g<KIND_BF16, OccF>(G, src);
+  const int64_t cap = (int64_t)device_cu_count() * occ;
+  // at least kMinTilesPerWave tiles per wave when the work is small
+  const int64_t need = (est_tiles + (int64_t)kWaves * kMinTilesPerWave - 1) / ((int64_t)kWaves * kMinTilesPerWave);
+  return (int)std::max<int64_t>(1, std::min(cap, need));
 }
 
-bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t items, int G, AttnArgs* a) {
+size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_pref) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  if (ws_bytes < attn_workspace_bytes(items, G) || ws == nullptr) return false;
+  return up((size_t)slots * G * kHeadDim * 4) + up((size_t)slots * G * 2 * 4) + up((size_t)n_pref * 4);
+}
+
+bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_pref,
+                          AttnArgs* a) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  if (ws_bytes < attn_workspace_bytes(slots, G, n_pref) || ws == nullptr) return false;
   char* p = static_cast<char*>(ws);
   a->ws_o = reinterpret_cast<float*>(p);
-  a->ws_ml = reinterpret_cast<float*>(p + up((size_t)items * G * kHeadDim * 4));
+  p += up((size_t)slots * G * kHeadDim * 4);
+  a->ws_ml = reinterpret_cast<float*>(p);
+  p += up((size_t)slots * G * 2 * 4);
+  a->ws_pref = n_pref > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;
   return true;
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream) {
-  return a.dtype == KIND_F16 ? launch_kind<KIND_F16>(a, stream) : launch_kind<KIND_BF16>(a, stream);
+  return a.dtype == KIND_F16 ? dispatch_g<KIND_F16, LaunchF>(a.G, a, stream)
+                             : dispatch_g<KIND_BF16, LaunchF>(a.G, a, stream);
 }
 
 }  // namespace kvdec

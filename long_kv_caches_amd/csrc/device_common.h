@@ -26,6 +26,7 @@ __device__ __forceinline__ u32x4 load_b128(const void* p) {
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
+__device__ __forceinline__ int uniform_i32(int x) { return __builtin_amdgcn_readfirstlane(x); }
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
@@ -109,35 +110,38 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Row exchanges between two registers a and b holding the same per-lane
-// value: afterwards (a, b) hold (row r, row r^1) for permlane16 and (half h,
-// half h^1) for permlane32 in every lane, so a op b combines the partners.
-// Issued as inline assembly with both operands in/out: the compiler builtins
-// for these swaps hand back the first result for both outputs.  The s_nop
-// pads cover the VALU-write / permlane-read hazard on either side.
-__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+// Row exchanges: from a value x, a pair (a, b) holding (row r, row r^1) for
+// permlane16 and (half h, half h^1) for permlane32 in every lane, so a op b
+// combines the partners.  The copy into b happens inside the same asm
+// statement, so the pair lives only for this exchange.  Inline assembly,
+// because the compiler builtins for these swaps hand back the first result
+// for both outputs.  The s_nop pads cover the VALU-write / permlane-read
+// hazard on either side.
+__device__ __forceinline__ void permlane16_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  a = x;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1"
+               : "+v"(a), "=&v"(b));
 }
-__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+__device__ __forceinline__ void permlane32_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  a = x;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
+               : "+v"(a), "=&v"(b));
 }
 
 // Combine the four 16-lane rows of the wave (every lane gets the result):
 // rows 0<->1 and 2<->3 by permlane16 swap, then halves by permlane32 swap.
 __device__ __forceinline__ float rowgroup_max(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  permlane16_swap(a, b);
+  uint32_t a, b;
+  permlane16_pair(__builtin_bit_cast(uint32_t, x), a, b);
   x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = b = __builtin_bit_cast(uint32_t, x);
-  permlane32_swap(a, b);
+  permlane32_pair(__builtin_bit_cast(uint32_t, x), a, b);
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 __device__ __forceinline__ float rowgroup_sum(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  permlane16_swap(a, b);
+  uint32_t a, b;
+  permlane16_pair(__builtin_bit_cast(uint32_t, x), a, b);
   x = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-  a = b = __builtin_bit_cast(uint32_t, x);
-  permlane32_swap(a, b);
+  permlane32_pair(__builtin_bit_cast(uint32_t, x), a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 

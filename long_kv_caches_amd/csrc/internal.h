@@ -16,7 +16,12 @@ constexpr int kHeadDim = 128;     // the one supported head_dim
 constexpr int kTile = 16;         // tokens per wave tile (one MFMA row block)
 constexpr int kWaves = 4;         // waves per attention workgroup
 constexpr int kMaxGroup = 8;      // query heads per KV head handled by one workgroup
-constexpr int kMaxChunks = 512;   // work items per (sequence, KV head) at most
+constexpr int kMaxChunks = 512;   // partials merged per LDS batch
+constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
+constexpr int kMinTilesPerWave = 8;
+
+// Tile schedules of the attention kernels.
+enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };
 
 // Where the K/V rows of one (sequence, KV head) pair live.
 enum Source : int { SRC_DENSE = 0, SRC_RAGGED = 1, SRC_PAGED = 2, SRC_HYBRID = 3 };
@@ -35,25 +40,34 @@ struct AttnArgs {
   const int32_t* head_map;
   uint16_t* out;
   float* lse;
-  float* ws_o;                  // [items, G, 128] unnormalised partial outputs
-  float* ws_ml;                 // [items, G, 2] partial (max, sum) in log2 units
+  float* ws_o;                  // [slots, G, 128] unnormalised partial outputs
+  float* ws_ml;                 // [slots, G, 2] partial (max, sum) in log2 units
+  int32_t* ws_pref;             // balanced: [n_units + 1] first tile of each unit
   int B, Hq, Hkv, G;
   int S;                        // dense: rows per sequence; ragged: token rows T;
                                 // paged: pages P in the pool
   int page, max_pages;          // paged
   int P_slots, pers_cap, buf_cap;  // hybrid
-  int chunk;                    // tokens per work item, a multiple of kTile * kWaves
-  int n_chunks;                 // work items per (sequence, KV head) in the grid
+  int mode;                     // Mode
+  int max_len;                  // lengths are clamped to this (the grid's coverage)
+  int chunk;                    // chunks: tokens per work item, a multiple of kTile * kWaves
+  int n_chunks;                 // chunks: work items per (sequence, KV head) in the grid
+  int n_blocks;                 // balanced: persistent workgroups
+  int n_units;                  // balanced: units of the tile line
   float scale_log2;             // softmax_scale * log2(e)
   int src;
   int dtype;
 };
 
-// Bytes of workspace for `items` partials of group size G.
-size_t attn_workspace_bytes(int64_t items, int G);
-// Carves ws into the partial-output and partial-(max, sum) regions; returns
-// false if ws_bytes is too small.
-bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t items, int G, AttnArgs* a);
+// Bytes of workspace for `slots` partials of group size G plus n_pref ints.
+size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_pref);
+// Carves ws into the partial-output, partial-(max, sum) and prefix regions;
+// returns false if ws_bytes is too small.
+bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_pref,
+                          AttnArgs* a);
+// Persistent workgroups for the balanced schedule on the current device:
+// CUs x resident workgroups per CU, fewer when est_tiles is small.
+int balanced_blocks(int dtype, int G, int src, int64_t est_tiles);
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream);
 
