@@ -203,6 +203,20 @@ kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_hea
                                 const void* w_k, const void* w_v, void* k_cache, void* v_cache,
                                 int64_t cache_batch_stride, hipStream_t stream);
 
+/* Kernel timing, a profiling aid.  While enabled on the calling thread, every
+ * call above records a pair of HIP events on its stream right before and
+ * right after its main kernel launch: the split kernel of an attention call
+ * (not the merge kernel), the lookup kernel of kvdec_headcache_lookup (not
+ * the compaction kernel), the GEMM of kvdec_kv_recompute.
+ * kvdec_kernel_timing(1) starts a new measurement (the library keeps and
+ * reuses its events); kvdec_kernel_timing(0) stops recording.
+ * kvdec_kernel_timing_read waits for the recorded events and returns the
+ * summed kernel time in milliseconds and the number of launches timed since
+ * the last kvdec_kernel_timing(1).  An event that could not be created or
+ * recorded stops further recording and is reported here as KVDEC_ERR_HIP. */
+kvdec_status kvdec_kernel_timing(int enable);
+kvdec_status kvdec_kernel_timing_read(double* total_ms, int64_t* launches);
+
 const char* kvdec_status_string(kvdec_status status);
 const char* kvdec_last_error(void);
 int kvdec_abi_version(void);

@@ -7,6 +7,6 @@ from ._lib import (  # noqa: F401
     KVDEC_BF16, KVDEC_DENSE, KVDEC_F16, KVDEC_PAGED, KVDEC_RAGGED, AttnDesc, HybridDesc,
     KvdecError, alloc_workspace, attn_desc, hybrid_desc, kvdec_decode_attn,
     kvdec_decode_attn_workspace, kvdec_headcache_lookup, kvdec_headcache_thresholds,
-    kvdec_kv_recompute, kvdec_sparse_hybrid_attn, kvdec_sparse_hybrid_attn_workspace,
-    last_error, status_string,
+    kvdec_kernel_timing, kvdec_kernel_timing_read, kvdec_kv_recompute, kvdec_sparse_hybrid_attn,
+    kvdec_sparse_hybrid_attn_workspace, last_error, status_string,
 )

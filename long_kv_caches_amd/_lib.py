@@ -59,6 +59,8 @@ def _load():
         "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
         "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, P, P, i64, P], st),
+        "kvdec_kernel_timing": ([ctypes.c_int], st),
+        "kvdec_kernel_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
         "kvdec_status_string": ([st], ctypes.c_char_p),
         "kvdec_last_error": ([], ctypes.c_char_p),
         "kvdec_abi_version": ([], ctypes.c_int),
@@ -73,7 +75,7 @@ def _load():
 lib = _load()
 EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
             "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_thresholds",
-            "kvdec_kv_recompute", "kvdec_status_string",
+            "kvdec_kv_recompute", "kvdec_kernel_timing", "kvdec_kernel_timing_read", "kvdec_status_string",
             "kvdec_last_error", "kvdec_abi_version")
 
 
@@ -130,6 +132,17 @@ def kvdec_sparse_hybrid_attn_workspace(desc: HybridDesc) -> int:
     n = ctypes.c_size_t()
     _check(lib.kvdec_sparse_hybrid_attn_workspace(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
+
+
+def kvdec_kernel_timing(enable: bool) -> None:
+    _check(lib.kvdec_kernel_timing(1 if enable else 0))
+
+
+def kvdec_kernel_timing_read():
+    """(summed main-kernel milliseconds, launches) since kvdec_kernel_timing(True)."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib.kvdec_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

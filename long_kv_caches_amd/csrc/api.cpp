@@ -7,6 +7,9 @@
 
 #include <algorithm>
 
+#include <utility>
+#include <vector>
+
 #include "internal.h"
 
 namespace kvdec {
@@ -182,6 +185,37 @@ static kvdec_status run_attn(const kvdec_attn_desc* d, const Plan& p, AttnArgs& 
   return hip_status(launch_decode_attn(a, stream), "decode attention launch");
 }
 
+// Kernel timing: per thread, a pool of event pairs reused from one
+// kvdec_kernel_timing(1) to the next.
+struct TimingState {
+  bool on = false;
+  size_t used = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  hipError_t err = hipSuccess;
+};
+static thread_local TimingState g_timing;
+
+void timing_begin(hipStream_t stream) {
+  TimingState& t = g_timing;
+  if (!t.on || t.err != hipSuccess) return;
+  if (t.used == t.pool.size()) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if ((t.err = hipEventCreate(&e0)) != hipSuccess) return;
+    if ((t.err = hipEventCreate(&e1)) != hipSuccess) {
+      (void)hipEventDestroy(e0);
+      return;
+    }
+    t.pool.emplace_back(e0, e1);
+  }
+  t.err = hipEventRecord(t.pool[t.used].first, stream);
+}
+
+void timing_end(hipStream_t stream) {
+  TimingState& t = g_timing;
+  if (!t.on || t.err != hipSuccess || t.used == t.pool.size()) return;
+  if ((t.err = hipEventRecord(t.pool[t.used].second, stream)) == hipSuccess) ++t.used;
+}
+
 }  // namespace kvdec
 
 using namespace kvdec;
@@ -189,6 +223,33 @@ using namespace kvdec;
 extern "C" {
 
 int kvdec_abi_version(void) { return KVDEC_ABI_VERSION; }
+
+kvdec_status kvdec_kernel_timing(int enable) {
+  TimingState& t = g_timing;
+  t.on = enable != 0;
+  if (t.on) {
+    t.used = 0;
+    t.err = hipSuccess;
+  }
+  return ok();
+}
+
+kvdec_status kvdec_kernel_timing_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(KVDEC_ERR_INVALID, "total_ms and launches must be non-NULL");
+  TimingState& t = g_timing;
+  if (t.err != hipSuccess) return hip_status(t.err, "kernel timing event");
+  double sum = 0.0;
+  for (size_t i = 0; i < t.used; ++i) {
+    hipError_t e = hipEventSynchronize(t.pool[i].second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.pool[i].first, t.pool[i].second);
+    if (e != hipSuccess) return hip_status(e, "kernel timing event");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)t.used;
+  return ok();
+}
 
 const char* kvdec_last_error(void) { return g_err; }
 

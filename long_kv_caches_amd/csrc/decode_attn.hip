@@ -27,16 +27,13 @@
 //
 // Two schedules distribute the tiles:
 //   balanced (default) -- a persistent grid of CUs x occupancy workgroups.
-//     The tile line (all pairs in (b, g) order) is cut into items of a fixed
-//     number of tiles; waves take items from an atomic counter in the
-//     workspace until none is left.  Measured on MI355X, equal static shares
-//     end far apart (waves of the second resident workgroup on a CU, and of
-//     some XCDs, run slower), and the hardware hands workgroups to XCDs in
-//     order, so a fast XCD can starve; taking items dynamically keeps every
-//     wave busy to the end.  An item may cover the end of one pair and the
-//     start of the next: it writes one partial per pair it touches (or the
-//     final output when it covers a whole pair).  Partials are indexed by
-//     item, so which wave ran an item does not change the result.
+//     The tile line (one KV head of every sequence) is cut into equal
+//     columns; wave k * Hkv + h runs column k for head h, so waves that run
+//     together read all heads of the same token rows.  A wave streams its
+//     column as one sequence of tiles (the next tile's loads are issued
+//     across pair boundaries) and writes one partial per pair it touches, or
+//     the final output when it covers a whole pair.  Its priority steps down
+//     as its share gets done, which keeps the waves of a CU in step.
 //   fixed chunks (split_tokens > 0) -- one workgroup per (b, g, chunk of
 //     split_tokens tokens); its four waves interleave the chunk's tiles and
 //     merge through LDS.  The partition then depends only on each sequence's
@@ -767,14 +764,18 @@ hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
   const dim3 block(256);
   if (a.mode == MODE_BALANCED) {
     const size_t lds = (size_t)(3 * a.n_units + 1) * sizeof(int);
+    timing_begin(stream);
     decode_balanced_kernel<KIND, G, SRC><<<dim3((unsigned)a.n_blocks), block, lds, stream>>>(a);
+    timing_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv));
+  timing_begin(stream);
   decode_chunk_kernel<KIND, G, SRC><<<grid, block, 0, stream>>>(a);
+  timing_end(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
   decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);

@@ -155,10 +155,14 @@ template <int KIND>
 hipError_t launch_lookup_kind(const LookupArgs& a, hipStream_t stream) {
   const int N = a.B * a.Hkv;
   if (N <= kOneBlockGroups) {
+    timing_begin(stream);
     lookup_one_block_kernel<KIND><<<1, kScanThreads, 0, stream>>>(a);
+    timing_end(stream);
     return hipGetLastError();
   }
+  timing_begin(stream);
   lookup_grid_kernel<KIND><<<(N + 3) / 4, 256, 0, stream>>>(a);
+  timing_end(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.miss_list) return e;
   compact_kernel<<<1, kScanThreads, 0, stream>>>(a.hit, N, a.miss_list, a.miss_count);

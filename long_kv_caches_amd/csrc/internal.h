@@ -71,6 +71,11 @@ int balanced_blocks(int dtype, int G, int src, int64_t est_tiles);
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream);
 
+// Profiling events around the main kernel launch of a call (no-ops unless
+// kvdec_kernel_timing is enabled on the calling thread).
+void timing_begin(hipStream_t stream);
+void timing_end(hipStream_t stream);
+
 struct LookupArgs {
   const uint16_t* q;
   uint16_t* labels;

@@ -145,7 +145,9 @@ __global__ __launch_bounds__(256) void kv_recompute_kernel(RecomputeArgs a) {
 hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
   const int M = a.b * a.l, N = 2 * a.h;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
+  timing_begin(stream);
   kv_recompute_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
+  timing_end(stream);
   return hipGetLastError();
 }
 

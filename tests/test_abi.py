@@ -148,3 +148,10 @@ def test_thresholds_host_helper_matches_oracle_bitwise():
         K.kvdec_headcache_thresholds([1.5])
     with pytest.raises(K.KvdecError):
         K.kvdec_headcache_thresholds([0.5], eta=1.5)
+
+
+def test_kernel_timing_without_launches():
+    """Timing can be switched on and read with nothing launched (no GPU needed)."""
+    K.kvdec_kernel_timing(True)
+    assert K.kvdec_kernel_timing_read() == (0.0, 0)
+    K.kvdec_kernel_timing(False)
