@@ -4,7 +4,7 @@ Workload: one Llama3-8B-shaped decode layer (32 query heads on 8 KV heads,
 head_dim 128), batch 16, context lengths uniform in [16384, 32768], ragged fp16
 KV with per-channel LogNormal(0, 0.5) K outlier scales (seeded synthetic
 data).  One step = one kvdec_decode_attn call over the whole batch: work
-split, Q load, K stream + MFMA scores, online softmax, V stream + P.V, the
+split, Q load, K stream + dot2 scores, online softmax, V stream + P.V, the
 in-workgroup merge and the split-K merge into the fp16 output and lse.
 
 Prints ONE JSON line.  `value` is achieved HBM throughput (algorithmic bytes /
@@ -12,8 +12,14 @@ time per step, TB/s) with inputs resident in HBM; `roofline` prices the same
 bytes against the 8 TB/s HBM3E peak; `cpu_baseline` times the fp64 CPU oracle
 on the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--split-tokens N]
-                       [--calibrate-copy] [--no-cpu-baseline]
+Other workloads (one JSON line each, same fields): --workload llama2-7b-paged
+(batch-1024 paged MHA), clo-llama3-8b-128k / clo-qwen2.5-14b-128k (CLO hybrid
+attention, plus the fused head-cache lookup's latency), kvpr-opt13b (partial
+K/V recompute TFLOP/s against the bf16 MFMA peak, plus attention over the
+merged cache).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload W]
+                       [--split-tokens N] [--calibrate-copy] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -54,12 +60,295 @@ def measured_traffic(per_launch_algorithmic):
     return t.get("hbm_bytes_per_launch")
 
 
+WORKLOADS = ("llama3-8b-32k", "llama2-7b-paged", "clo-llama3-8b-128k", "clo-qwen2.5-14b-128k",
+             "kvpr-opt13b")
+
+
+def time_steps(step, steps, warmup, stream, K, torch):
+    """(ms per step by events around the timed steps, mean main-kernel us, launches timed)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    K.kvdec_kernel_timing(True)  # HIP events around each main-kernel launch, on `stream`
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms_total, launches = K.kvdec_kernel_timing_read()
+    K.kvdec_kernel_timing(False)
+    return t0.elapsed_time(t1) / steps, kern_ms_total * 1e3 / max(launches, 1), launches
+
+
+def oracle_seconds(fn, reps=3):
+    times = []
+    for _ in range(reps):
+        c0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - c0)
+    return sorted(times)[reps // 2]
+
+
+def hbm_roofline(kernel, nbytes, kern_us, traffic=None):
+    gbs = nbytes / (kern_us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel_us": round(kern_us, 2)}
+
+
+def common(args, workload, metric, unit, value, ms, dtype, data, config, higher=True):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": higher,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": data,
+            "config": dict({"workload": workload}, **config)}
+
+
+def bench_llama3(args, K, np, torch, dev, stream):
+    import kvgen
+    d = kvgen.ragged_llama(seed=args.seed)
+    B, Hq, Hkv, D = d["B"], d["Hq"], d["Hkv"], d["D"]
+    lens = np.diff(d["cu_seqlens"]).astype(np.int64)
+    T = int(lens.sum())
+    q = torch.from_numpy(d["q"]).to(dev)
+    k = torch.from_numpy(d["k"]).to(dev)
+    v = torch.from_numpy(d["v"]).to(dev)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+    desc = K.attn_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
+                       layout=K.KVDEC_RAGGED, max_seqlen=int(lens.max()), softmax_scale=d["scale"],
+                       split_tokens=args.split_tokens, kv_rows=T)
+    ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc), device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    # algorithmic bytes of one step: attended K and V rows, q, out, lse, cu_seqlens
+    step_bytes = T * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2 + B * Hq * 4 + (B + 1) * 4
+
+    def step():
+        K.kvdec_decode_attn(desc, q, k, v, None, cu, None, out, lse, ws, stream=stream)
+
+    ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch)
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    r = common(args, "llama3-8b-32k-ragged-decode-attention",
+               "decode-attn achieved HBM TB/s (% of peak) + KV tokens·heads/s, Llama3-8B 32K",
+               "TB/s", round(gbs / 1e3, 4), ms, "f16",
+               "synthetic (seeded; shapes and distributions of the Llama3-8B 32K decode workload)",
+               {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                "context_lengths": "uniform [16384, 32768]", "total_tokens": T, "layout": "ragged",
+                "split_tokens": args.split_tokens or "auto"})
+    r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
+    r["kv_token_heads_per_s"] = round(T * Hkv / (ms * 1e-3), 1)
+    r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
+                                 step_bytes, kern_us, measured_traffic(step_bytes))
+    r["roofline"]["launches_timed"] = launches
+    if not args.no_cpu_baseline:
+        import oracle
+        cs = oracle_seconds(lambda: oracle.decode_attn(d["q"], d["k"], d["v"], num_kv_heads=Hkv,
+                                                       layout=oracle.RAGGED, scale=d["scale"],
+                                                       cu_seqlens=d["cu_seqlens"]))
+        r["cpu_baseline"] = {"value": round(step_bytes / cs / 1e12, 6), "unit": "TB/s",
+                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "sample": f"the full workload (all {B} sequences, {T} tokens), median of 3 runs, "
+                                       f"{cs:.2f} s each"}
+    return r
+
+
+def bench_paged(args, K, np, torch, dev, stream):
+    import kvgen
+    d = kvgen.paged_mha(seed=args.seed)
+    B, H, D, page = d["B"], d["Hq"], d["D"], d["page"]
+    lens = d["seqlens"].astype(np.int64)
+    T = int(lens.sum())
+    q = torch.from_numpy(d["q"]).to(dev)
+    k = torch.from_numpy(d["k"]).to(dev)
+    v = torch.from_numpy(d["v"]).to(dev)
+    bt = torch.from_numpy(d["block_table"]).to(dev)
+    sl = torch.from_numpy(d["seqlens"]).to(dev)
+    P = d["k"].shape[0]
+    desc = K.attn_desc(batch=B, num_q_heads=H, num_kv_heads=H, dtype=torch.float16,
+                       layout=K.KVDEC_PAGED, max_seqlen=int(lens.max()), softmax_scale=d["scale"],
+                       page_size=page, max_pages_per_seq=d["max_pages"],
+                       split_tokens=args.split_tokens, kv_rows=P)
+    ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc), device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    used_pages = int(((lens + page - 1) // page).sum())
+    step_bytes = T * H * D * 4 + B * H * D * 4 + B * H * 4 + B * 4 + used_pages * 4
+
+    def step():
+        K.kvdec_decode_attn(desc, q, k, v, sl, None, bt, out, lse, ws, stream=stream)
+
+    ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    r = common(args, "llama2-7b-paged-decode-attention",
+               "paged decode-attn achieved HBM TB/s (% of peak), Llama-2-7B MHA batch 1024", "TB/s",
+               round(gbs / 1e3, 4), ms, "f16",
+               "synthetic (seeded; LogNormal(ln 1024, 1.0) lengths clipped to [128, 4096], shuffled page pool)",
+               {"batch": B, "num_q_heads": H, "num_kv_heads": H, "head_dim": D, "page_size": page,
+                "total_tokens": T, "pool_pages": P, "layout": "paged",
+                "split_tokens": args.split_tokens or "auto"})
+    r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
+    r["kv_token_heads_per_s"] = round(T * H / (ms * 1e-3), 1)
+    r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
+                                 step_bytes, kern_us)
+    r["roofline"]["launches_timed"] = launches
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 64  # a bounded sample: the first 64 sequences
+        sub_bytes = int(lens[:n].sum()) * H * D * 4 + n * H * D * 4
+        cs = oracle_seconds(lambda: oracle.decode_attn(d["q"][:n], d["k"], d["v"], num_kv_heads=H,
+                                                       layout=oracle.PAGED, scale=d["scale"],
+                                                       seqlens=d["seqlens"][:n],
+                                                       block_table=d["block_table"][:n], page_size=page))
+        r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
+                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "sample": f"the first {n} of {B} sequences ({int(lens[:n].sum())} tokens), "
+                                       f"median of 3 runs, {cs:.2f} s each"}
+    return r
+
+
+def bench_clo(args, K, np, torch, dev, stream, model):
+    import kvgen
+    d = kvgen.clo_hybrid(seed=args.seed, model=model)
+    B, Hq, Hkv, D = d["B"], d["Hq"], d["Hkv"], d["D"]
+    G = Hq // Hkv
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, pk, pv, bk, bv = (to(d[n]) for n in ("q", "pers_k", "pers_v", "buf_k", "buf_v"))
+    pl, blen, hm = to(d["pers_len"]), to(d["buf_len"]), to(d["head_map"])
+    desc = K.hybrid_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
+                         softmax_scale=d["scale"], split_tokens=args.split_tokens,
+                         num_pers_slots=d["pers_k"].shape[1], pers_cap=d["pers_k"].shape[2],
+                         buf_cap=d["buf_k"].shape[2])
+    ws = K.alloc_workspace(K.kvdec_sparse_hybrid_attn_workspace(desc), device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    hmn = d["head_map"]
+    rows = sum(int(d["pers_len"][b]) if hmn[g] >= 0 else int(d["buf_len"][b * Hkv + g])
+               for b in range(B) for g in range(Hkv))
+    step_bytes = rows * D * 4 + B * Hq * D * 4 + B * Hq * 4 + (B + B * Hkv + Hkv) * 4
+
+    def step():
+        K.kvdec_sparse_hybrid_attn(desc, q, pk, pv, pl, bk, bv, blen, hm, out, lse, ws, stream=stream)
+
+    ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    name = {"llama3-8b": "Llama3-8B", "qwen2.5-14b": "Qwen2.5-14B"}[model]
+    r = common(args, f"clo-{model}-128k-hybrid-attention",
+               f"CLO hybrid (buffer + persistent) attn achieved HBM TB/s, {name} 128K batch 4", "TB/s",
+               round(gbs / 1e3, 4), ms, "f16",
+               "synthetic (seeded; 2 persistent KV heads with all 131072 rows, 10% of rows per buffer head)",
+               {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "context": d["S"],
+                "persistent_heads": int((hmn >= 0).sum()), "buffer_rows": d["ksel"],
+                "split_tokens": args.split_tokens or "auto"})
+    r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
+    r["kv_token_heads_per_s"] = round(rows / (ms * 1e-3), 1)
+    r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
+                                 step_bytes, kern_us)
+    r["roofline"]["launches_timed"] = launches
+
+    # the fused head-cache lookup on the same queries (launch-bound at this size)
+    tau = K.kvdec_headcache_thresholds(kvgen.group_importance(d["s"], Hkv).astype(np.float32),
+                                       d["eta"], d["n_exp"]).to(dev)
+    labels = to(d["labels"])
+    w = to(d["weights"])
+    hit = torch.empty(B * Hkv, dtype=torch.uint8, device=dev)
+    ml = torch.empty(B * Hkv, dtype=torch.int32, device=dev)
+    mc = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def lookup():
+        K.kvdec_headcache_lookup(q, labels, w, tau, hit, None, None, ml, mc, stream=stream)
+
+    lookup()  # decides against the generated labels; later calls see the updated labels
+    torch.cuda.synchronize()
+    misses_first = int(mc.item())
+    lms, lkern_us, _ = time_steps(lookup, args.steps, args.warmup, stream, K, torch)
+    lbytes = B * Hq * D * 2 * 2 + Hq * 4 + Hkv * 4 + B * Hkv * 1 + 4
+    r["lookup"] = {"us_per_call": round(lms * 1e3, 2), "kernel_us": round(lkern_us, 2),
+                   "bytes": lbytes, "misses_on_first_call": misses_first, "groups": B * Hkv,
+                   "achieved_gbs": round(lbytes / (lkern_us * 1e-6) / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        import oracle
+        sub_rows = sum(int(d["pers_len"][0]) if hmn[g] >= 0 else int(d["buf_len"][g]) for g in range(Hkv))
+        sub_bytes = sub_rows * D * 4 + Hq * D * 4
+        cs = oracle_seconds(lambda: oracle.hybrid_attn(d["q"][:1], d["pers_k"][:1], d["pers_v"][:1],
+                                                       d["pers_len"][:1], d["buf_k"][:1], d["buf_v"][:1],
+                                                       d["buf_len"][:Hkv], hmn, scale=d["scale"]))
+        r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
+                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "sample": f"batch element 0 of {B} ({sub_rows} KV rows), median of 3 runs, "
+                                       f"{cs:.2f} s each"}
+    return r
+
+
+def bench_kvpr(args, K, np, torch, dev, stream):
+    import kvgen
+    d = kvgen.kvpr_layer(seed=args.seed)
+    b, h, H, D, s, l = d["b"], d["h"], d["H"], d["D"], d["s"], d["l"]
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = to(d["x"]).view(torch.bfloat16)
+    wk = to(d["w_k"]).view(torch.bfloat16)
+    wv = to(d["w_v"]).view(torch.bfloat16)
+    kc, vc, q = to(d["k_cache"]), to(d["v_cache"]), to(d["q"])
+    flops = 4.0 * b * l * h * h
+
+    def step():
+        K.kvdec_kv_recompute(x, wk, wv, kc, vc, l, stream=stream)
+
+    ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch)
+    tflops = flops / (ms * 1e-3) / 1e12
+    kern_tflops = flops / (kern_us * 1e-6) / 1e12
+    r = common(args, "kvpr-opt13b-partial-recompute",
+               "KVPR partial K/V recompute TFLOP/s (% of bf16 MFMA peak), OPT-13B b=32 l=256", "TFLOP/s",
+               round(tflops, 2), ms, "bf16",
+               "synthetic (seeded; X ~ N(0,1), W ~ N(0, 1/h), bf16)",
+               {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "split_point": l,
+                "context": s, "flops_per_step": flops})
+    r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel", "achieved": round(kern_tflops, 2),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
+                     "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
+    # attention over the merged cache [0, s') (dense MHA)
+    desc = K.attn_desc(batch=b, num_q_heads=H, num_kv_heads=H, dtype=torch.float16,
+                       layout=K.KVDEC_DENSE, max_seqlen=s, softmax_scale=d["scale"])
+    ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc), device=dev)
+    out = torch.empty((b, H, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((b, H), dtype=torch.float32, device=dev)
+
+    def attn():
+        K.kvdec_decode_attn(desc, q, kc, vc, None, None, None, out, lse, ws, stream=stream)
+
+    ams, akern_us, _ = time_steps(attn, args.steps, args.warmup, stream, K, torch)
+    abytes = b * s * H * D * 4 + b * H * D * 4 + b * H * 4
+    r["attention"] = {"us_per_call": round(ams * 1e3, 2), "kernel_us": round(akern_us, 2),
+                      "bytes": abytes, "tbs": round(abytes / (ams * 1e-3) / 1e12, 4),
+                      "kernel_frac_of_hbm_peak": round(abytes / (akern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.arange(0, b * l, (b * l) // 16, dtype=np.int32)  # 16 of the b*l rows
+        cs = oracle_seconds(lambda: oracle.kv_recompute(d["x"], d["w_k"], d["w_v"], l=l, rows=rows))
+        r["cpu_baseline"] = {"value": round(4.0 * rows.size * h * h / cs / 1e12, 6), "unit": "TFLOP/s",
+                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "sample": f"{rows.size} of the {b * l} recomputed rows (both K and V), "
+                                       f"median of 3 runs, {cs:.2f} s each"}
+    return r
+
+
+def calibrate_copy(torch, dev):
+    src = torch.ones(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", choices=WORKLOADS, default=WORKLOADS[0])
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
@@ -74,116 +363,19 @@ def main():
     import numpy as np
     import torch
 
-    import kvgen
     import long_kv_caches_amd as K
 
-    d = kvgen.ragged_llama(seed=args.seed)
-    B, Hq, Hkv, D = d["B"], d["Hq"], d["Hkv"], d["D"]
-    lens = np.diff(d["cu_seqlens"]).astype(np.int64)
-    T = int(lens.sum())
     dev = torch.device("cuda:0")
-    q = torch.from_numpy(d["q"]).to(dev)
-    k = torch.from_numpy(d["k"]).to(dev)
-    v = torch.from_numpy(d["v"]).to(dev)
-    cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
-    max_seqlen = int(lens.max())
-    desc = K.attn_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
-                       layout=K.KVDEC_RAGGED, max_seqlen=max_seqlen, softmax_scale=d["scale"],
-                       split_tokens=args.split_tokens, kv_rows=T)
-    ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc), device=dev)
-    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    # algorithmic bytes of one step: attended K and V rows, q, out, lse, cu_seqlens
-    kv_bytes = T * Hkv * D * 2 * 2
-    step_bytes = kv_bytes + B * Hq * D * 2 * 2 + B * Hq * 4 + (B + 1) * 4
-    token_heads = T * Hkv
-
-    def step():
-        K.kvdec_decode_attn(desc, q, k, v, None, cu, None, out, lse, ws, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    K.kvdec_kernel_timing(True)  # HIP events around each split-kernel launch, on `stream`
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    kern_ms_total, kern_launches = K.kvdec_kernel_timing_read()
-    K.kvdec_kernel_timing(False)
-    ms = t0.elapsed_time(t1) / args.steps
-    sec = ms / 1e3
-    kern_sec = kern_ms_total / max(kern_launches, 1) / 1e3
-
-    if args.calibrate_copy:
-        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    achieved_gbs = step_bytes / sec / 1e9
-    # roofline of the dominant kernel (the split kernel: it streams all of K
-    # and V); its algorithmic bytes per launch are the step's bytes
-    kern_gbs = step_bytes / kern_sec / 1e9
-    traffic = measured_traffic(step_bytes)
-    result = {
-        "metric": "decode-attn achieved HBM TB/s (% of peak) + KV tokens·heads/s, Llama3-8B 32K",
-        "value": round(achieved_gbs / 1e3, 4),
-        "unit": "TB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded; shapes and distributions of the Llama3-8B 32K decode workload)",
-        "config": {
-            "workload": "llama3-8b-32k-ragged-decode-attention",
-            "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-            "context_lengths": "uniform [16384, 32768]", "total_tokens": T,
-            "layout": "ragged", "split_tokens": args.split_tokens or "auto",
-        },
-        "pct_of_hbm_peak": round(100.0 * achieved_gbs / HBM_PEAK_GBS, 2),
-        "kv_token_heads_per_s": round(token_heads / sec, 1),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-            "achieved": round(kern_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_us": round(kern_sec * 1e6, 2),
-            "launches_timed": kern_launches,
-        },
-    }
-
-    if not args.no_cpu_baseline:
-        import oracle
-        reps, times = 3, []
-        for _ in range(reps):
-            c0 = time.perf_counter()
-            oracle.decode_attn(d["q"], d["k"], d["v"], num_kv_heads=Hkv, layout=oracle.RAGGED,
-                               scale=d["scale"], cu_seqlens=d["cu_seqlens"])
-            times.append(time.perf_counter() - c0)
-        cs = sorted(times)[reps // 2]
-        result["cpu_baseline"] = {
-            "value": round(step_bytes / cs / 1e12, 6),
-            "unit": "TB/s",
-            "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"the full workload (all {B} sequences, {T} tokens), median of {reps} runs, "
-                      f"{cs:.2f} s each",
-        }
-    print(json.dumps(result), flush=True)
+    if args.workload == "llama3-8b-32k":
+        r = bench_llama3(args, K, np, torch, dev, stream)
+    elif args.workload == "llama2-7b-paged":
+        r = bench_paged(args, K, np, torch, dev, stream)
+    elif args.workload.startswith("clo-"):
+        r = bench_clo(args, K, np, torch, dev, stream, args.workload[4:-5])
+    else:
+        r = bench_kvpr(args, K, np, torch, dev, stream)
+    print(json.dumps(r), flush=True)
 
 
 if __name__ == "__main__":
