@@ -46,6 +46,7 @@ struct Plan {
   int max_len;
   int chunk, n_chunks;    // chunks
   int n_blocks, n_units;  // balanced
+  int n_cu;               // balanced
   int64_t max_items;      // balanced: columns of the line
   int line_heads;         // balanced: heads run per line item
 };
@@ -65,6 +66,7 @@ static Plan plan_attn(int dtype, int G, int src, int64_t pairs, int64_t n_units,
     p.mode = MODE_BALANCED;
     p.n_units = (int)n_units;
     p.n_blocks = balanced_blocks(dtype, G, src, est_tiles);
+    p.n_cu = device_cu_count();
     // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
     const int64_t LH = pairs / std::max<int64_t>(n_units, 1);
     p.max_items = (int64_t)p.n_blocks * kWaves / std::max<int64_t>(LH, 1);
@@ -167,6 +169,7 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->n_chunks = p.n_chunks;
   a->n_blocks = p.n_blocks;
   a->n_units = p.n_units;
+  a->n_cu = p.n_cu;
   a->scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
   a->dtype = d->dtype;
 }

@@ -19,6 +19,7 @@ constexpr int kMaxGroup = 8;      // query heads per KV head handled by one work
 constexpr int kMaxChunks = 512;   // partials merged per LDS batch
 constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
 constexpr int kMinTilesPerWave = 8;
+constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-round column
 
 // Tile schedules of the attention kernels.
 enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };
@@ -53,6 +54,7 @@ struct AttnArgs {
   int chunk;                    // chunks: tokens per work item, a multiple of kTile * kWaves
   int n_chunks;                 // chunks: work items per (sequence, KV head) in the grid
   int n_blocks;                 // balanced: persistent workgroups
+  int n_cu;                     // balanced: CUs of the device (workgroups of the first round)
   int n_units;                  // balanced: units of the tile line
   float scale_log2;             // softmax_scale * log2(e)
   int src;
@@ -68,6 +70,8 @@ bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
 int balanced_blocks(int dtype, int G, int src, int64_t est_tiles);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream);
 
