@@ -121,3 +121,22 @@ def test_headline_full_size():
     """Llama3-8B 32K ragged batch at full size, default plan (as the bench runs it)."""
     d = kvgen.ragged_llama(seed=0)
     _parity(d, "Llama3-8B ragged B=16 16K-32K (full)")
+
+
+def test_paged_llama2_full_size_sampled():
+    """Llama-2-7B paged MHA at full size (B = 1024, ~1.4M tokens, 24 GB of K/V),
+    default plan as the bench runs it; 24 sequences checked against the oracle:
+    the shortest, the longest and 22 drawn at random (seeded)."""
+    d = kvgen.paged_mha(seed=0)
+    lens = d["seqlens"]
+    rng = np.random.default_rng(1234)
+    pick = np.unique(np.concatenate([[int(np.argmin(lens)), int(np.argmax(lens))],
+                                     rng.choice(d["B"], 22, replace=False)]))
+    say(f"[decode] paged Llama-2-7B full size, B={d['B']}, tokens={int(lens.sum())}, "
+        f"checking {pick.size} sequences")
+    out, lse = decode_on_gpu(d)
+    ref_o, ref_l = oracle.decode_attn(d["q"][pick], d["k"], d["v"], num_kv_heads=d["Hkv"],
+                                      layout=oracle.PAGED, scale=d["scale"],
+                                      seqlens=lens[pick], block_table=d["block_table"][pick])
+    check_close(host_f64(out)[pick], ref_o, "paged full size (sampled sequences)")
+    check_lse(lse[pick], ref_l, "paged full size lse (sampled)")
