@@ -9,19 +9,22 @@
 // fp16 and writes row (batch i, token t) straight into k_cache / v_cache
 // [b, s_cap, H, 128] at rows t < l (every other byte untouched).
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of C; its four
-// waves each own a 64 x 64 quarter as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
-// K advances 32 at a time through double-buffered LDS.  X rows are already
-// K-contiguous; W is N-contiguous, so each thread transposes a 4 x 4 block of
-// W in registers (byte permutes) before storing it K-contiguous in LDS, where
-// every MFMA operand is one 16-byte LDS read.
+// Tiling: a 256-thread workgroup computes a 256 x 128 tile of C; its four
+// waves each own a 128 x 64 quarter as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks
+// (accumulators in AGPRs), so each 32-wide K step issues 16 MFMAs per wave
+// against 6 LDS operand reads per 16 k.  Global loads run two K steps ahead
+// in registers (a K step of MFMA work alone does not cover the load latency
+// under full load), LDS is double-buffered with one barrier per step.  X rows
+// are already K-contiguous; W is N-contiguous, so each thread transposes a
+// 4 x 4 block of W in registers (byte permutes) before storing it
+// K-contiguous in LDS, where every MFMA operand is one 16-byte LDS read.
 #include "device_common.h"
 #include "internal.h"
 
 namespace kvdec {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BM = 256, BN = 128, BK = 32;
 constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (80 bytes: spreads banks)
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -34,10 +37,16 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-__global__ __launch_bounds__(256) void kv_recompute_kernel(RecomputeArgs a) {
+// One K step's global data of this thread: four 16-byte pieces of X rows and
+// a 4 x 4 block of W.
+struct Stage {
+  u32x4 a[4];
+  u32x2 b[4];
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_recompute_kernel(RecomputeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = a.b * a.l, N = 2 * a.h, K = a.h;
   const int n_tiles_n = N / BN;
@@ -49,85 +58,100 @@ __global__ __launch_bounds__(256) void kv_recompute_kernel(RecomputeArgs a) {
   const uint16_t* W = is_v ? a.wv : a.wk;
   const int wn0 = is_v ? n0 - a.h : n0;
 
-  // A loads: thread -> (row am, 16-byte piece ak) for two rows am, am + 64.
+  // A loads: thread -> 16-byte piece ak of rows am + 64 i (i < 4); rows past
+  // M read row M - 1 (their results are not stored).
   const int am = tid >> 2, ak = (tid & 3) * 8;
-  const uint16_t* xrow[2];
+  const uint16_t* xrow[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int r = min(m0 + am + 64 * i, M - 1);
     const int bi = r / a.l, t = r - bi * a.l;
     xrow[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
   }
-  // B loads: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns (bn .. bn+3).
+  // B loads: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns (bn .. bn+3);
+  // 32 lanes read one 256-byte W row piece.  (Measured: a k-fastest mapping,
+  // which avoids the LDS bank conflicts of the transposed stores, was slower
+  // overall because of the scattered global reads.)
   const int bn = (tid & 31) * 4, bk = (tid >> 5) * 4;
   const uint16_t* wcol = W + (int64_t)bk * a.h + wn0 + bn;
 
-  u32x4 ra[2];
-  u32x2 rb[4];
-  auto gload = [&](int k0) {
+  auto gload = [&](int k0, Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = load_b128(xrow[i] + k0);
+    for (int i = 0; i < 4; ++i) st.a[i] = load_b128(xrow[i] + k0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rb[i] = *reinterpret_cast<const u32x2*>(wcol + (int64_t)(k0 + i) * a.h);
+      st.b[i] = *reinterpret_cast<const u32x2*>(wcol + (int64_t)(k0 + i) * a.h);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      store_b128(&As[buf][(am + 64 * i) * LDS_STRIDE + ak], ra[i]);
-    // rb[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
+    for (int i = 0; i < 4; ++i) store_b128(&As[buf][(am + 64 * i) * LDS_STRIDE + ak], st.a[i]);
+    // st.b[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
     u32x2 col[4];
-    col[0] = u32x2{pack_lo(rb[0].x, rb[1].x), pack_lo(rb[2].x, rb[3].x)};
-    col[1] = u32x2{pack_hi(rb[0].x, rb[1].x), pack_hi(rb[2].x, rb[3].x)};
-    col[2] = u32x2{pack_lo(rb[0].y, rb[1].y), pack_lo(rb[2].y, rb[3].y)};
-    col[3] = u32x2{pack_hi(rb[0].y, rb[1].y), pack_hi(rb[2].y, rb[3].y)};
+    col[0] = u32x2{pack_lo(st.b[0].x, st.b[1].x), pack_lo(st.b[2].x, st.b[3].x)};
+    col[1] = u32x2{pack_hi(st.b[0].x, st.b[1].x), pack_hi(st.b[2].x, st.b[3].x)};
+    col[2] = u32x2{pack_lo(st.b[0].y, st.b[1].y), pack_lo(st.b[2].y, st.b[3].y)};
+    col[3] = u32x2{pack_hi(st.b[0].y, st.b[1].y), pack_hi(st.b[2].y, st.b[3].y)};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
   };
 
-  // Wave quarter: rows wm .. wm+63, cols wn .. wn+63.
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];
+  // Wave quarter: rows wm .. wm+127, cols wn .. wn+63.
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 fa[2], fb[2];
+      u32x4 fa[4], fb[2];
       const int kk = 16 * ks + 8 * (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
         fa[i] = *reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * i + (lane & 31)) * LDS_STRIDE + kk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         fb[j] = *reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  // K step kt computes from LDS[kt & 1]; the registers of stage kt & 1 are
+  // refilled with step kt + 2 as soon as step kt has been stored, and step
+  // kt + 1 (loaded during step kt - 1) is stored after the compute.
+  const int nk = K / BK;  // a multiple of 8 (h % 256 == 0)
+  Stage s0, s1;
+  gload(0, s0);
+  gload(BK, s1);
+  lstore(0, s0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even step: LDS[0] holds kt, s1 holds kt + 1
+    if (kt + 2 < nk) gload((kt + 2) * BK, s0);
+    compute(0);
+    lstore(1, s1);
+    __syncthreads();
+    // odd step: LDS[1] holds kt + 1, s0 holds kt + 2
+    if (kt + 3 < nk) gload((kt + 3) * BK, s1);
+    compute(1);
+    if (kt + 2 < nk) lstore(0, s0);
     __syncthreads();
   }
 
   // Epilogue: acc[i][j][e] = C[row wm + 32i + 8*(e/4) + 4*(lane/32) + e%4][col wn + 32j + lane%32]
   uint16_t* C = is_v ? a.vc : a.kc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
