@@ -10,8 +10,8 @@
 // One wave owns one (sequence, KV head) group: each lane holds two of the 128
 // elements of every query head of the group, so the query and label rows are
 // read once (coalesced 256-byte rows) and, on a miss, the query still in
-// registers is written over the labels.  Reductions are fp32 wave butterflies
-// in a fixed order, so results are deterministic.
+// registers is written over the labels.  Reductions are fp32 DPP row sums
+// and permlane swaps in a fixed order, so results are deterministic.
 //
 // The ascending miss list needs a scan over all groups.  Small problems
 // (<= kOneBlockGroups groups) run in one workgroup: decisions go to LDS and the
@@ -26,53 +26,61 @@ namespace {
 constexpr int kOneBlockGroups = 512;
 constexpr int kScanThreads = 1024;
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
+// Sum over the 64 lanes (every lane gets it): DPP steps within each 16-lane
+// row, then permlane swaps across the rows; all on the VALU, fixed order.
+__device__ __forceinline__ float lanes_sum(float x) { return rowgroup_sum(row_sum16(x)); }
 
 // Processes group `grp` = b * Hkv + g with the 64 lanes of the calling wave.
-// Returns the hit decision (uniform across the wave).
+// Returns the hit decision (uniform across the wave).  Every global load is
+// issued before the first store, so none waits behind a possibly aliasing
+// store, and the 3 G reductions are independent of each other.
 template <int KIND>
 __device__ bool lookup_group(const LookupArgs& a, int grp, int lane) {
   const int b = grp / a.Hkv, g = grp - b * a.Hkv;
   const int G = a.G;
   constexpr int kMaxG = 16;
-  uint32_t qv[kMaxG];
-  float num = 0.f, wsum = 0.f, csum = 0.f;
-  bool degenerate = false;
   const int64_t row0 = ((int64_t)b * a.Hq + (int64_t)g * G) * kHeadDim;
-  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(a.q + row0);
-  uint32_t* l32 = reinterpret_cast<uint32_t*>(a.labels + row0);
-  uint32_t lv[kMaxG];
+  const uint32_t* __restrict__ q32 = reinterpret_cast<const uint32_t*>(a.q + row0);
+  uint32_t* __restrict__ l32 = reinterpret_cast<uint32_t*>(a.labels + row0);
+  const float* __restrict__ wg = a.w + g * G;
+  uint32_t qv[kMaxG], lv[kMaxG];
+  float w[kMaxG];
 #pragma unroll
   for (int j = 0; j < kMaxG; ++j) {
     if (j < G) {
       qv[j] = q32[j * (kHeadDim / 2) + lane];
       lv[j] = l32[j * (kHeadDim / 2) + lane];
+      w[j] = wg[j];
     }
   }
+  const float tau = a.tau[g];
+  float dot[kMaxG], qq[kMaxG], ll[kMaxG];
 #pragma unroll
   for (int j = 0; j < kMaxG; ++j) {
     if (j < G) {
       const float q0 = lo_f32<KIND>(qv[j]), q1 = hi_f32<KIND>(qv[j]);
       const float l0 = lo_f32<KIND>(lv[j]), l1 = hi_f32<KIND>(lv[j]);
-      const float dot = wave_sum(__builtin_fmaf(q0, l0, q1 * l1));
-      const float qq = wave_sum(__builtin_fmaf(q0, q0, q1 * q1));
-      const float ll = wave_sum(__builtin_fmaf(l0, l0, l1 * l1));
+      dot[j] = lanes_sum(__builtin_fmaf(q0, l0, q1 * l1));
+      qq[j] = lanes_sum(__builtin_fmaf(q0, q0, q1 * q1));
+      ll[j] = lanes_sum(__builtin_fmaf(l0, l0, l1 * l1));
+    }
+  }
+  float num = 0.f, wsum = 0.f, csum = 0.f;
+  bool degenerate = false;
+#pragma unroll
+  for (int j = 0; j < kMaxG; ++j) {
+    if (j < G) {
       float c = 0.f;
-      if (qq == 0.f || ll == 0.f) degenerate = true;
-      else c = dot / (__builtin_sqrtf(qq) * __builtin_sqrtf(ll));
-      if (a.cos && lane == 0) a.cos[(int64_t)b * a.Hq + g * G + j] = c;
-      const float w = a.w[g * G + j];
-      num = __builtin_fmaf(w, c, num);
-      wsum += w;
+      if (qq[j] == 0.f || ll[j] == 0.f) degenerate = true;
+      else c = dot[j] / (__builtin_sqrtf(qq[j]) * __builtin_sqrtf(ll[j]));
+      if (a.cos && lane == j) a.cos[(int64_t)b * a.Hq + g * G + j] = c;
+      num = __builtin_fmaf(w[j], c, num);
+      wsum += w[j];
       csum += c;
     }
   }
   const float agg = wsum != 0.f ? num / wsum : csum / (float)G;
-  const bool hit = !degenerate && agg >= a.tau[g];
+  const bool hit = !degenerate && agg >= tau;
   if (lane == 0) {
     a.hit[grp] = hit ? 1 : 0;
     if (a.agg) a.agg[grp] = agg;
