@@ -106,7 +106,9 @@ kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* desc, size_t* by
 
 /*
  * Decode attention.
- *   q   [B, Hq, 128]; out [B, Hq, 128] (dtype); lse [B, Hq] fp32 (may be NULL)
+ *   q   [B, Hq, 128]; out [B, Hq, 128] (dtype); lse [B, Hq] fp32 (may be NULL);
+ *   k and v may be NULL when there are no rows to read (RAGGED with
+ *   kv_rows = 0, DENSE with max_seqlen = 0): every sequence is then empty
  *   DENSE : k, v [B, max_seqlen, Hkv, 128]; seqlens [B] int32 (NULL => all max_seqlen)
  *   RAGGED: k, v [T, Hkv, 128] packed by sequence; cu_seqlens [B+1] int32,
  *           cu_seqlens[0] = 0, nondecreasing; seqlens ignored

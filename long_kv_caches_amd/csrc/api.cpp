@@ -65,10 +65,13 @@ static Plan plan_attn(int dtype, int G, int src, int64_t pairs, int64_t n_units,
   if (split_tokens == 0 && n_units <= kMaxUnits && est_tiles < (int64_t(1) << 30)) {
     p.mode = MODE_BALANCED;
     p.n_units = (int)n_units;
-    p.n_blocks = balanced_blocks(dtype, G, src, est_tiles);
+    // at least one wave per line head: with fewer, no column exists and
+    // some heads would never be run
+    const int64_t LH = pairs / std::max<int64_t>(n_units, 1);
+    p.n_blocks = (int)std::max<int64_t>(balanced_blocks(dtype, G, src, est_tiles),
+                                        (LH + kWaves - 1) / kWaves);
     p.n_cu = device_cu_count();
     // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
-    const int64_t LH = pairs / std::max<int64_t>(n_units, 1);
     p.max_items = (int64_t)p.n_blocks * kWaves / std::max<int64_t>(LH, 1);
     p.line_heads = (int)LH;
     return p;
@@ -282,7 +285,12 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* d, const void* q, const vo
   kvdec_status st = check_common(d, true);
   if (st != KVDEC_OK) return st;
   if (d->batch == 0) return ok();
-  if (!q || !k || !v || !out) return fail(KVDEC_ERR_INVALID, "q, k, v and out must be non-NULL");
+  if (!q || !out) return fail(KVDEC_ERR_INVALID, "q and out must be non-NULL");
+  // k and v may be NULL only when no row can be read
+  const bool no_rows = (d->layout == KVDEC_RAGGED && d->kv_rows == 0) ||
+                       (d->layout == KVDEC_DENSE && d->max_seqlen == 0);
+  if ((!k || !v) && !no_rows)
+    return fail(KVDEC_ERR_INVALID, "k and v must be non-NULL (unless there are no K/V rows)");
   if (d->layout == KVDEC_RAGGED && !cu_seqlens)
     return fail(KVDEC_ERR_INVALID, "RAGGED needs cu_seqlens");
   if (d->layout == KVDEC_PAGED && (!seqlens || !block_table))

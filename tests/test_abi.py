@@ -155,3 +155,10 @@ def test_kernel_timing_without_launches():
     K.kvdec_kernel_timing(True)
     assert K.kvdec_kernel_timing_read() == (0.0, 0)
     K.kvdec_kernel_timing(False)
+
+
+def test_null_kv_only_without_rows():
+    """k / v may be NULL only when no K/V row can be read."""
+    assert _decode(_desc(kv_rows=100), k=None, v=None) == K._lib.KVDEC_ERR_INVALID
+    assert "k and v" in K.last_error()
+    assert _decode(_desc(layout=K.KVDEC_DENSE, max_seqlen=16), k=None) == K._lib.KVDEC_ERR_INVALID

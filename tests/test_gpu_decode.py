@@ -62,36 +62,51 @@ def test_ragged_tiles_and_tails(split):
     _parity(d, f"ragged lens={lens}", split_tokens=split)
 
 
-def test_deterministic_repeats():
+@pytest.mark.parametrize("split", [0, 256])
+def test_deterministic_repeats(split):
     d = kvgen.ragged_llama(seed=3, lens=[5000, 333, 4097], Hq=32, Hkv=8)
-    say("[decode] determinism x3")
-    outs, _ = decode_on_gpu(d, split_tokens=256, repeat=3)
+    say(f"[decode] determinism x3 split={split}")
+    outs, _ = decode_on_gpu(d, split_tokens=split, repeat=3)
     b0 = bits(outs[0])
     for o in outs[1:]:
         assert np.array_equal(bits(o), b0)
 
 
-def test_empty_sequences():
+@pytest.mark.parametrize("split", [0, 64])
+def test_empty_sequences(split):
     d = kvgen.ragged_llama(seed=4, lens=[0, 5, 0, 300, 0], Hq=8, Hkv=2)
-    out = _parity(d, "ragged with empty sequences", split_tokens=64)
+    out = _parity(d, "ragged with empty sequences", split_tokens=split)
     got = host_f64(out)
     assert np.all(got[[0, 2, 4]] == 0.0)
 
 
+@pytest.mark.parametrize("split", [0, 256])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (12, 4), (40, 8), (48, 8), (56, 8), (64, 8)])
-def test_group_sizes(hq, hkv):
+def test_group_sizes(hq, hkv, split):
     d = kvgen.ragged_llama(seed=5, lens=[1, 77, 1500, 2049], Hq=hq, Hkv=hkv)
-    _parity(d, f"G={hq // hkv}", split_tokens=256)
+    _parity(d, f"G={hq // hkv}", split_tokens=split)
 
 
-def test_dense_with_seqlens():
+@pytest.mark.parametrize("split", [0, 128])
+def test_dense_with_seqlens(split):
     d = kvgen.dense_small(seed=6, B=4, Hq=16, Hkv=4, S=2000, seqlens=[2000, 1, 999, 0])
-    _parity(d, "dense with seqlens", split_tokens=128)
+    _parity(d, "dense with seqlens", split_tokens=split)
 
 
-def test_bf16():
+@pytest.mark.parametrize("split", [0, 256])
+def test_bf16(split):
     d = kvgen.ragged_llama(seed=7, lens=[100, 2000, 4321], Hq=32, Hkv=8)
-    _parity(d, "ragged bf16", split_tokens=256, bf16=True)
+    _parity(d, "ragged bf16", split_tokens=split, bf16=True)
+
+
+@pytest.mark.parametrize("lens", [[1], [17, 0, 3], [0, 0], [16] * 40])
+def test_tiny_lines_default_plan(lens):
+    """Fewer line tiles than persistent waves (columns capped at the line length,
+    equal weights below two tiles per column) and all-empty batches."""
+    d = kvgen.ragged_llama(seed=13, lens=lens, Hq=32, Hkv=8)
+    out = _parity(d, f"tiny ragged lens={lens[:4]}{'...' if len(lens) > 4 else ''}", split_tokens=0)
+    empty = [i for i, n in enumerate(lens) if n == 0]
+    assert np.all(host_f64(out)[empty] == 0.0)
 
 
 def test_paged_bitwise_equals_ragged():
