@@ -93,3 +93,25 @@ def test_hybrid_full_size_128k():
         check_close(host_f64(out), ro, f"hybrid {model} 128K")
         check_lse(lse, rl)
         del d
+
+
+@pytest.mark.parametrize("split", [0, 128])
+def test_uneven_and_empty_lengths(split):
+    """Persistent and buffer lengths that differ per sequence and per head,
+    including empty ones and single rows (the oracle takes the same lengths)."""
+    d = kvgen.clo_hybrid(seed=5, B=3, S=3000, frac=0.3)
+    Hkv = d["Hkv"]
+    d["pers_len"] = np.array([3000, 1, 0], np.int32)
+    bl = d["buf_len"].reshape(3, Hkv).copy()
+    buf_heads = np.nonzero(d["head_map"] < 0)[0]
+    cap = d["buf_k"].shape[2]
+    pattern = [0, 1, 17, cap, cap - 5, 255]
+    for b in range(3):
+        for i, g in enumerate(buf_heads):
+            bl[b, g] = min(cap, pattern[(i + 2 * b) % len(pattern)])
+    d["buf_len"] = bl.reshape(-1)
+    say(f"[hybrid] uneven lengths split={split}")
+    out, lse = hybrid_on_gpu(d, split)
+    ro, rl = hybrid_oracle(d)
+    check_close(host_f64(out), ro, f"hybrid uneven lengths split={split}")
+    check_lse(lse, rl)
