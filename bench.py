@@ -305,13 +305,20 @@ def bench_kvpr(args, K, np, torch, dev, stream):
     b, h, H, D, s, l = d["b"], d["h"], d["H"], d["D"], d["s"], d["l"]
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x = to(d["x"]).view(torch.bfloat16)
-    wk = to(d["w_k"]).view(torch.bfloat16)
-    wv = to(d["w_v"]).view(torch.bfloat16)
+    # W as a model stores its projection weights (nn.Linear: [out, in]); the
+    # [in, out] layout is timed too and reported beside it
+    wk_io = to(d["w_k"]).view(torch.bfloat16)
+    wv_io = to(d["w_v"]).view(torch.bfloat16)
+    wk = wk_io.t().contiguous()
+    wv = wv_io.t().contiguous()
     kc, vc, q = to(d["k_cache"]), to(d["v_cache"]), to(d["q"])
     flops = 4.0 * b * l * h * h
 
     def step():
-        K.kvdec_kv_recompute(x, wk, wv, kc, vc, l, stream=stream)
+        K.kvdec_kv_recompute(x, wk, wv, kc, vc, l, K.KVDEC_W_OUT_IN, stream=stream)
+
+    def step_io():
+        K.kvdec_kv_recompute(x, wk_io, wv_io, kc, vc, l, K.KVDEC_W_IN_OUT, stream=stream)
 
     ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch, args.prewarm_ms)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -321,10 +328,14 @@ def bench_kvpr(args, K, np, torch, dev, stream):
                round(tflops, 2), ms, "bf16",
                "synthetic (seeded; X ~ N(0,1), W ~ N(0, 1/h), bf16)",
                {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "split_point": l,
-                "context": s, "flops_per_step": flops})
+                "context": s, "flops_per_step": flops, "w_layout": "out_in (nn.Linear)"})
     r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel", "achieved": round(kern_tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
                      "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
+    io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)
+    r["w_in_out"] = {"ms_per_step": round(io_ms, 4), "tflops": round(flops / (io_ms * 1e-3) / 1e12, 2),
+                     "kernel_us": round(io_kern_us, 2),
+                     "kernel_frac_of_mfma_peak": round(flops / (io_kern_us * 1e-6) / 1e12 / 2500.0, 4)}
     # attention over the merged cache [0, s') (dense MHA)
     desc = K.attn_desc(batch=b, num_q_heads=H, num_kv_heads=H, dtype=torch.float16,
                        layout=K.KVDEC_DENSE, max_seqlen=s, softmax_scale=d["scale"])

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 1
+#define KVDEC_ABI_VERSION 2
 
 typedef enum {
   KVDEC_OK = 0,
@@ -192,7 +192,11 @@ kvdec_status kvdec_headcache_thresholds(int32_t n, const float* s /*(host)*/, do
  * already resident before attention runs over [0, s')).
  *
  *   x        [b, *, h] bf16, row t of batch i at x + i*x_batch_stride + t*h (elements)
- *   w_k, w_v [h, h] bf16 row-major, input index first (the product is x . W)
+ *   w_k, w_v [h, h] bf16 row-major; w_layout KVDEC_W_IN_OUT: input index
+ *            first, W[i][n] (the product is x . W); KVDEC_W_OUT_IN: output
+ *            index first, W[n][i], as a torch.nn.Linear weight stores it (the
+ *            same product with W read transposed; the faster layout here, as
+ *            its rows are contiguous along the contraction)
  *   k_cache, v_cache [b, s_cap, H, head_dim] fp16 with h = H * head_dim; batch i
  *            starts cache_batch_stride elements after batch i-1.  Rows [0, l)
  *            are overwritten with fp16(x . W) (fp32 accumulation, one rounding);
@@ -200,10 +204,13 @@ kvdec_status kvdec_headcache_thresholds(int32_t n, const float* s /*(host)*/, do
  *   Requires l >= 0, b >= 0, head_dim == 128, h % 256 == 0 (covers the 40-head
  *   OPT-13B width 5120), x_batch_stride >= l*h, cache_batch_stride >= l*h.
  */
+typedef enum { KVDEC_W_IN_OUT = 0, KVDEC_W_OUT_IN = 1 } kvdec_w_layout;
+
 kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_heads,
                                 int32_t head_dim, const void* x, int64_t x_batch_stride,
-                                const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                                int64_t cache_batch_stride, hipStream_t stream);
+                                const void* w_k, const void* w_v, int32_t w_layout,
+                                void* k_cache, void* v_cache, int64_t cache_batch_stride,
+                                hipStream_t stream);
 
 /* Kernel timing, a profiling aid.  While enabled on the calling thread, every
  * call above records a pair of HIP events on its stream right before and

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libkvdec.so")
 KVDEC_OK, KVDEC_ERR_INVALID, KVDEC_ERR_UNSUPPORTED, KVDEC_ERR_WORKSPACE, KVDEC_ERR_HIP = range(5)
 KVDEC_F16, KVDEC_BF16 = 0, 1
 KVDEC_DENSE, KVDEC_RAGGED, KVDEC_PAGED = 0, 1, 2
+KVDEC_W_IN_OUT, KVDEC_W_OUT_IN = 0, 1
 
 _DTYPES = {torch.float16: KVDEC_F16, torch.bfloat16: KVDEC_BF16}
 
@@ -58,7 +59,7 @@ def _load():
                                       sz, P], st),
         "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
-        "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, P, P, i64, P], st),
+        "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, i32, P, P, i64, P], st),
         "kvdec_kernel_timing": ([ctypes.c_int], st),
         "kvdec_kernel_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
         "kvdec_status_string": ([st], ctypes.c_char_p),
@@ -190,10 +191,12 @@ def kvdec_headcache_thresholds(s, eta=0.8, n_exp=3.0):
     return tau
 
 
-def kvdec_kv_recompute(x, w_k, w_v, k_cache, v_cache, l, stream=None):
-    """x [b, s_x, h] bf16; k_cache, v_cache [b, s_cap, H, 128] fp16 (rows [0, l) written)."""
+def kvdec_kv_recompute(x, w_k, w_v, k_cache, v_cache, l, w_layout=0, stream=None):
+    """x [b, s_x, h] bf16; w_k, w_v [h, h] bf16 ([in, out] for KVDEC_W_IN_OUT,
+    [out, in] as nn.Linear stores them for KVDEC_W_OUT_IN); k_cache, v_cache
+    [b, s_cap, H, 128] fp16 (rows [0, l) written)."""
     b, s_x, h = x.shape
     H, hd = k_cache.shape[2], k_cache.shape[3]
-    _check(lib.kvdec_kv_recompute(b, l, h, H, hd, _ptr(x), s_x * h, _ptr(w_k), _ptr(w_v),
+    _check(lib.kvdec_kv_recompute(b, l, h, H, hd, _ptr(x), s_x * h, _ptr(w_k), _ptr(w_v), int(w_layout),
                                   _ptr(k_cache), _ptr(v_cache), k_cache.shape[1] * H * hd,
                                   _stream(stream)))

@@ -425,9 +425,12 @@ kvdec_status kvdec_headcache_thresholds(int32_t n, const float* s, double eta, d
 
 kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_heads,
                                 int32_t head_dim, const void* x, int64_t x_batch_stride,
-                                const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                                int64_t cache_batch_stride, hipStream_t stream) {
+                                const void* w_k, const void* w_v, int32_t w_layout,
+                                void* k_cache, void* v_cache, int64_t cache_batch_stride,
+                                hipStream_t stream) {
   if (b < 0 || l < 0 || h < 1 || num_heads < 1) return fail(KVDEC_ERR_INVALID, "bad sizes");
+  if (w_layout != KVDEC_W_IN_OUT && w_layout != KVDEC_W_OUT_IN)
+    return fail(KVDEC_ERR_INVALID, "w_layout must be KVDEC_W_IN_OUT or KVDEC_W_OUT_IN");
   if (head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
   if ((int64_t)num_heads * head_dim != h) return fail(KVDEC_ERR_INVALID, "h != num_heads * head_dim");
   if (h % 256 != 0) return fail(KVDEC_ERR_UNSUPPORTED, "h must be a multiple of 256");
@@ -447,6 +450,7 @@ kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_hea
   a.b = b;
   a.l = l;
   a.h = h;
+  a.w_layout = w_layout;
   return hip_status(launch_kv_recompute(a, stream), "kv recompute launch");
 }
 

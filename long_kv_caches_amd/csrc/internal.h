@@ -104,6 +104,7 @@ struct RecomputeArgs {
   int64_t x_bstride;
   int64_t c_bstride;
   int b, l, h;
+  int w_layout;  // kvdec_w_layout
 };
 hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream);
 

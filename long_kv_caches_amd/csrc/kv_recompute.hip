@@ -15,9 +15,14 @@
 // against 6 LDS operand reads per 16 k.  Global loads run two K steps ahead
 // in registers (a K step of MFMA work alone does not cover the load latency
 // under full load), LDS is double-buffered with one barrier per step.  X rows
-// are already K-contiguous; W is N-contiguous, so each thread transposes a
-// 4 x 4 block of W in registers (byte permutes) before storing it
-// K-contiguous in LDS, where every MFMA operand is one 16-byte LDS read.
+// are already K-contiguous.  W stored [out, in] (as a torch.nn.Linear weight)
+// is K-contiguous too and is staged exactly like X.  W stored [in, out] is
+// N-contiguous: each thread transposes a 4 x 4 block of it in registers (byte
+// permutes) before storing it K-contiguous in LDS, where every MFMA operand
+// is one 16-byte LDS read.  The transposed 8-byte stores of that layout put
+// rows 4 apart on the same LDS banks (measured on MI355X: the kernel then
+// runs at about 40% of the MFMA rate with no global loads at all, 85% with
+// no LDS operand traffic), which is why the [out, in] layout is the fast one.
 #include "device_common.h"
 #include "internal.h"
 
@@ -38,12 +43,20 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 }
 
 // One K step's global data of this thread: four 16-byte pieces of X rows and
-// a 4 x 4 block of W.
+// either a 4 x 4 block of W ([in, out]) or two 16-byte pieces of W rows
+// ([out, in]).
+template <int WL>
 struct Stage {
   u32x4 a[4];
   u32x2 b[4];
 };
+template <>
+struct Stage<KVDEC_W_OUT_IN> {
+  u32x4 a[4];
+  u32x4 b[2];
+};
 
+template <int WL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_recompute_kernel(RecomputeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
@@ -68,32 +81,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int bi = r / a.l, t = r - bi * a.l;
     xrow[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
   }
-  // B loads: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns (bn .. bn+3);
-  // 32 lanes read one 256-byte W row piece.  (Measured: a k-fastest mapping,
-  // which avoids the LDS bank conflicts of the transposed stores, was slower
-  // overall because of the scattered global reads.)
+  // B loads.  [in, out]: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns
+  // (bn .. bn+3); 32 lanes read one 256-byte W row piece.  (Measured: a
+  // k-fastest mapping, which avoids the LDS bank conflicts of the transposed
+  // stores, was slower overall because of its scattered global reads.)
+  // [out, in]: thread -> 16-byte piece ak of W rows n = am + 64 i (i < 2).
   const int bn = (tid & 31) * 4, bk = (tid >> 5) * 4;
-  const uint16_t* wcol = W + (int64_t)bk * a.h + wn0 + bn;
+  const uint16_t* wsrc = WL == KVDEC_W_OUT_IN ? W + (int64_t)(wn0 + am) * a.h + ak
+                                              : W + (int64_t)bk * a.h + wn0 + bn;
 
-  auto gload = [&](int k0, Stage& st) {
+  auto gload = [&](int k0, Stage<WL>& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.a[i] = load_b128(xrow[i] + k0);
+    if constexpr (WL == KVDEC_W_OUT_IN) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st.b[i] = *reinterpret_cast<const u32x2*>(wcol + (int64_t)(k0 + i) * a.h);
+      for (int i = 0; i < 2; ++i) st.b[i] = load_b128(wsrc + (int64_t)64 * i * a.h + k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.b[i] = *reinterpret_cast<const u32x2*>(wsrc + (int64_t)(k0 + i) * a.h);
+    }
   };
-  auto lstore = [&](int buf, const Stage& st) {
+  auto lstore = [&](int buf, const Stage<WL>& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_b128(&As[buf][(am + 64 * i) * LDS_STRIDE + ak], st.a[i]);
-    // st.b[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
-    u32x2 col[4];
-    col[0] = u32x2{pack_lo(st.b[0].x, st.b[1].x), pack_lo(st.b[2].x, st.b[3].x)};
-    col[1] = u32x2{pack_hi(st.b[0].x, st.b[1].x), pack_hi(st.b[2].x, st.b[3].x)};
-    col[2] = u32x2{pack_lo(st.b[0].y, st.b[1].y), pack_lo(st.b[2].y, st.b[3].y)};
-    col[3] = u32x2{pack_hi(st.b[0].y, st.b[1].y), pack_hi(st.b[2].y, st.b[3].y)};
+    if constexpr (WL == KVDEC_W_OUT_IN) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
+      for (int i = 0; i < 2; ++i) store_b128(&Bs[buf][(am + 64 * i) * LDS_STRIDE + ak], st.b[i]);
+    } else {
+      // st.b[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
+      u32x2 col[4];
+      col[0] = u32x2{pack_lo(st.b[0].x, st.b[1].x), pack_lo(st.b[2].x, st.b[3].x)};
+      col[1] = u32x2{pack_hi(st.b[0].x, st.b[1].x), pack_hi(st.b[2].x, st.b[3].x)};
+      col[2] = u32x2{pack_lo(st.b[0].y, st.b[1].y), pack_lo(st.b[2].y, st.b[3].y)};
+      col[3] = u32x2{pack_hi(st.b[0].y, st.b[1].y), pack_hi(st.b[2].y, st.b[3].y)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
+    }
   };
 
   // Wave quarter: rows wm .. wm+127, cols wn .. wn+63.
@@ -130,7 +155,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // refilled with step kt + 2 as soon as step kt has been stored, and step
   // kt + 1 (loaded during step kt - 1) is stored after the compute.
   const int nk = K / BK;  // a multiple of 8 (h % 256 == 0)
-  Stage s0, s1;
+  Stage<WL> s0, s1;
   gload(0, s0);
   gload(BK, s1);
   lstore(0, s0);
@@ -170,7 +195,10 @@ hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
   const int M = a.b * a.l, N = 2 * a.h;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
   timing_begin(stream);
-  kv_recompute_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
+  if (a.w_layout == KVDEC_W_OUT_IN)
+    kv_recompute_kernel<KVDEC_W_OUT_IN><<<(unsigned)blocks, 256, 0, stream>>>(a);
+  else
+    kv_recompute_kernel<KVDEC_W_IN_OUT><<<(unsigned)blocks, 256, 0, stream>>>(a);
   timing_end(stream);
   return hipGetLastError();
 }

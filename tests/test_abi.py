@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 1
+    assert _lib.lib.kvdec_abi_version() == 2
 
 
 def test_status_strings():
@@ -131,11 +131,13 @@ def test_lookup_validation():
 
 def test_recompute_validation():
     R = _lib.lib.kvdec_kv_recompute
-    assert R(2, 4, 5000, 40, 128, FAKE, 4 * 5000, FAKE, FAKE, FAKE, FAKE, 8 * 5000, None) == 1
-    assert R(2, 4, 5120, 40, 64, FAKE, 4 * 5120, FAKE, FAKE, FAKE, FAKE, 8 * 5120, None) == 2
-    assert R(2, 4, 384, 3, 128, FAKE, 4 * 384, FAKE, FAKE, FAKE, FAKE, 8 * 384, None) == 2
-    assert R(2, 4, 5120, 40, 128, FAKE, 3 * 5120, FAKE, FAKE, FAKE, FAKE, 8 * 5120, None) == 1
-    assert R(2, 0, 5120, 40, 128, None, 0, None, None, None, None, 0, None) == 0
+    assert R(2, 4, 5000, 40, 128, FAKE, 4 * 5000, FAKE, FAKE, 0, FAKE, FAKE, 8 * 5000, None) == 1
+    assert R(2, 4, 5120, 40, 64, FAKE, 4 * 5120, FAKE, FAKE, 0, FAKE, FAKE, 8 * 5120, None) == 2
+    assert R(2, 4, 384, 3, 128, FAKE, 4 * 384, FAKE, FAKE, 0, FAKE, FAKE, 8 * 384, None) == 2
+    assert R(2, 4, 5120, 40, 128, FAKE, 3 * 5120, FAKE, FAKE, 0, FAKE, FAKE, 8 * 5120, None) == 1
+    assert R(2, 4, 5120, 40, 128, FAKE, 4 * 5120, FAKE, FAKE, 2, FAKE, FAKE, 8 * 5120, None) == 1
+    assert "w_layout" in K.last_error()
+    assert R(2, 0, 5120, 40, 128, None, 0, None, None, 1, None, None, 0, None) == 0
 
 
 def test_thresholds_host_helper_matches_oracle_bitwise():

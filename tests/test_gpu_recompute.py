@@ -12,13 +12,19 @@ from gpu_util import bits, check_close, decode_on_gpu, dev, host_f64, say
 pytestmark = pytest.mark.gpu
 
 
-def recompute_on_gpu(d):
+LAYOUTS = [K.KVDEC_W_IN_OUT, K.KVDEC_W_OUT_IN]
+
+
+def recompute_on_gpu(d, w_layout=K.KVDEC_W_IN_OUT):
+    """The generated W is [in, out]; the [out, in] layout gets its transpose
+    (the same matrix stored the other way, as nn.Linear stores it)."""
+    conv = (lambda w: np.ascontiguousarray(w.T)) if w_layout == K.KVDEC_W_OUT_IN else (lambda w: w)
     x = dev(d["x"], bf16=True)
-    wk = dev(d["w_k"], bf16=True)
-    wv = dev(d["w_v"], bf16=True)
+    wk = dev(conv(d["w_k"]), bf16=True)
+    wv = dev(conv(d["w_v"]), bf16=True)
     kc = dev(d["k_cache"])
     vc = dev(d["v_cache"])
-    K.kvdec_kv_recompute(x, wk, wv, kc, vc, d["l"])
+    K.kvdec_kv_recompute(x, wk, wv, kc, vc, d["l"], w_layout)
     torch.cuda.synchronize()
     return kc, vc
 
@@ -38,16 +44,18 @@ def _check_rows(d, kc, vc, rows=None):
     assert np.array_equal(bits(vc)[:, l:], d["v_cache"][:, l:].view(np.uint16))
 
 
+@pytest.mark.parametrize("w_layout", LAYOUTS)
 @pytest.mark.parametrize("b,l,h,H", [(3, 17, 256, 2), (2, 150, 512, 4), (1, 1, 256, 2),
                                      (4, 128, 1024, 8)])
-def test_small_shapes(b, l, h, H):
+def test_small_shapes(b, l, h, H, w_layout):
     d = kvgen.kvpr_layer(seed=1, b=b, h=h, H=H, s=l + 40, l=l)
-    say(f"[recompute] b={b} l={l} h={h}")
-    kc, vc = recompute_on_gpu(d)
+    say(f"[recompute] b={b} l={l} h={h} w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
     _check_rows(d, kc, vc)
 
 
-def test_unit_vector_rows_bit_exact():
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+def test_unit_vector_rows_bit_exact(w_layout):
     rng = np.random.default_rng(2)
     d = kvgen.kvpr_layer(seed=2, b=2, h=512, H=4, s=40, l=33)
     idx = rng.integers(0, 512, size=(2, 33))
@@ -56,8 +64,8 @@ def test_unit_vector_rows_bit_exact():
         for t in range(33):
             x[i, t, idx[i, t]] = 1.0
     d["x"] = kvgen.f32_to_bf16_bits(x)
-    say("[recompute] unit-vector rows")
-    kc, vc = recompute_on_gpu(d)
+    say(f"[recompute] unit-vector rows w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
     kg = bits(kc).reshape(2, 40, 512)
     vg = bits(vc).reshape(2, 40, 512)
     wk16 = kvgen.bf16_bits_to_f32(d["w_k"]).astype(np.float16).view(np.uint16)
@@ -68,10 +76,11 @@ def test_unit_vector_rows_bit_exact():
             assert np.array_equal(vg[i, t], wv16[idx[i, t]])
 
 
-def test_opt13b_full_size_sampled_rows_then_attention():
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+def test_opt13b_full_size_sampled_rows_then_attention(w_layout):
     d = kvgen.kvpr_layer(seed=0)
-    say("[recompute] OPT-13B b=32 l=256 h=5120 (sampled rows)")
-    kc, vc = recompute_on_gpu(d)
+    say(f"[recompute] OPT-13B b=32 l=256 h=5120 (sampled rows) w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
     rows = np.sort(np.random.default_rng(3).choice(d["b"] * d["l"], 40, replace=False)).astype(np.int32)
     _check_rows(d, kc, vc, rows=rows)
     # attention over [0, s'): first with the GPU's own recomputed rows (isolates attention)
