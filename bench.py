@@ -329,7 +329,7 @@ def bench_kvpr(args, K, np, torch, dev, stream):
                "synthetic (seeded; X ~ N(0,1), W ~ N(0, 1/h), bf16)",
                {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "split_point": l,
                 "context": s, "flops_per_step": flops, "w_layout": "out_in (nn.Linear)"})
-    r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel", "achieved": round(kern_tflops, 2),
+    r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel_k64", "achieved": round(kern_tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
                      "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
     io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)

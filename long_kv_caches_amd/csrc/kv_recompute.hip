@@ -11,18 +11,17 @@
 //
 // Tiling: a 256-thread workgroup computes a 256 x 128 tile of C; its four
 // waves each own a 128 x 64 quarter as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks
-// (accumulators in AGPRs), so each 32-wide K step issues 16 MFMAs per wave
-// against 6 LDS operand reads per 16 k.  Global loads run two K steps ahead
-// in registers (a K step of MFMA work alone does not cover the load latency
-// under full load), LDS is double-buffered with one barrier per step.  X rows
-// are already K-contiguous.  W stored [out, in] (as a torch.nn.Linear weight)
-// is K-contiguous too and is staged exactly like X.  W stored [in, out] is
+// (accumulators in VGPRs, two waves per SIMD), so each 16-wide k slice issues
+// 8 MFMAs per wave against 6 LDS operand reads.  X rows are K-contiguous.  W
+// stored [out, in] (as a torch.nn.Linear weight) is K-contiguous too and is
+// staged exactly like X, in 64-wide K steps.  W stored [in, out] is
 // N-contiguous: each thread transposes a 4 x 4 block of it in registers (byte
-// permutes) before storing it K-contiguous in LDS, where every MFMA operand
-// is one 16-byte LDS read.  The transposed 8-byte stores of that layout put
-// rows 4 apart on the same LDS banks (measured on MI355X: the kernel then
-// runs at about 40% of the MFMA rate with no global loads at all, 85% with
-// no LDS operand traffic), which is why the [out, in] layout is the fast one.
+// permutes) before storing it K-contiguous in LDS, in 32-wide K steps with
+// loads two steps ahead and double-buffered LDS.  The transposed 8-byte
+// stores put rows 4 apart on the same LDS banks (measured on MI355X: that
+// kernel runs at about 40% of the MFMA rate with no global loads at all, 85%
+// with no LDS operand traffic), which is why the [out, in] layout is the
+// fast one.
 #include "device_common.h"
 #include "internal.h"
 
@@ -43,20 +42,13 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 }
 
 // One K step's global data of this thread: four 16-byte pieces of X rows and
-// either a 4 x 4 block of W ([in, out]) or two 16-byte pieces of W rows
-// ([out, in]).
-template <int WL>
+// a 4 x 4 block of W.
 struct Stage {
   u32x4 a[4];
   u32x2 b[4];
 };
-template <>
-struct Stage<KVDEC_W_OUT_IN> {
-  u32x4 a[4];
-  u32x4 b[2];
-};
 
-template <int WL>
+// [in, out] weights.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_recompute_kernel(RecomputeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
@@ -81,44 +73,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int bi = r / a.l, t = r - bi * a.l;
     xrow[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
   }
-  // B loads.  [in, out]: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns
-  // (bn .. bn+3); 32 lanes read one 256-byte W row piece.  (Measured: a
-  // k-fastest mapping, which avoids the LDS bank conflicts of the transposed
-  // stores, was slower overall because of its scattered global reads.)
-  // [out, in]: thread -> 16-byte piece ak of W rows n = am + 64 i (i < 2).
+  // B loads: thread -> 4 k-rows (bk .. bk+3) x 4 n-columns (bn .. bn+3); 32
+  // lanes read one 256-byte W row piece.  (Measured: a k-fastest mapping,
+  // which avoids the LDS bank conflicts of the transposed stores, was slower
+  // overall because of its scattered global reads.)
   const int bn = (tid & 31) * 4, bk = (tid >> 5) * 4;
-  const uint16_t* wsrc = WL == KVDEC_W_OUT_IN ? W + (int64_t)(wn0 + am) * a.h + ak
-                                              : W + (int64_t)bk * a.h + wn0 + bn;
+  const uint16_t* wsrc = W + (int64_t)bk * a.h + wn0 + bn;
 
-  auto gload = [&](int k0, Stage<WL>& st) {
+  auto gload = [&](int k0, Stage& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.a[i] = load_b128(xrow[i] + k0);
-    if constexpr (WL == KVDEC_W_OUT_IN) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) st.b[i] = load_b128(wsrc + (int64_t)64 * i * a.h + k0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.b[i] = *reinterpret_cast<const u32x2*>(wsrc + (int64_t)(k0 + i) * a.h);
-    }
+    for (int i = 0; i < 4; ++i) st.b[i] = *reinterpret_cast<const u32x2*>(wsrc + (int64_t)(k0 + i) * a.h);
   };
-  auto lstore = [&](int buf, const Stage<WL>& st) {
+  auto lstore = [&](int buf, const Stage& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_b128(&As[buf][(am + 64 * i) * LDS_STRIDE + ak], st.a[i]);
-    if constexpr (WL == KVDEC_W_OUT_IN) {
+    // st.b[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
+    u32x2 col[4];
+    col[0] = u32x2{pack_lo(st.b[0].x, st.b[1].x), pack_lo(st.b[2].x, st.b[3].x)};
+    col[1] = u32x2{pack_hi(st.b[0].x, st.b[1].x), pack_hi(st.b[2].x, st.b[3].x)};
+    col[2] = u32x2{pack_lo(st.b[0].y, st.b[1].y), pack_lo(st.b[2].y, st.b[3].y)};
+    col[3] = u32x2{pack_hi(st.b[0].y, st.b[1].y), pack_hi(st.b[2].y, st.b[3].y)};
 #pragma unroll
-      for (int i = 0; i < 2; ++i) store_b128(&Bs[buf][(am + 64 * i) * LDS_STRIDE + ak], st.b[i]);
-    } else {
-      // st.b[i] = W[bk+i][bn .. bn+3] as two dwords; transpose to columns.
-      u32x2 col[4];
-      col[0] = u32x2{pack_lo(st.b[0].x, st.b[1].x), pack_lo(st.b[2].x, st.b[3].x)};
-      col[1] = u32x2{pack_hi(st.b[0].x, st.b[1].x), pack_hi(st.b[2].x, st.b[3].x)};
-      col[2] = u32x2{pack_lo(st.b[0].y, st.b[1].y), pack_lo(st.b[2].y, st.b[3].y)};
-      col[3] = u32x2{pack_hi(st.b[0].y, st.b[1].y), pack_hi(st.b[2].y, st.b[3].y)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
-    }
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(&Bs[buf][(bn + j) * LDS_STRIDE + bk]) = col[j];
   };
 
   // Wave quarter: rows wm .. wm+127, cols wn .. wn+63.
@@ -155,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // refilled with step kt + 2 as soon as step kt has been stored, and step
   // kt + 1 (loaded during step kt - 1) is stored after the compute.
   const int nk = K / BK;  // a multiple of 8 (h % 256 == 0)
-  Stage<WL> s0, s1;
+  Stage s0, s1;
   gload(0, s0);
   gload(BK, s1);
   lstore(0, s0);
@@ -189,6 +167,99 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// [out, in] weights: W rows are K-contiguous like X rows and are staged the
+// same way.  64-wide K steps, so each wave issues 32 MFMAs between barriers;
+// the next step's loads are in flight in registers during the compute, and
+// one LDS buffer with two barriers per step keeps two workgroups on a CU
+// (measured on MI355X: 0.99-1.03 PFLOP/s on the OPT-13B shape, against
+// 0.92 with 32-wide steps and double-buffered LDS).  144-byte LDS rows:
+// fragment reads of 32 consecutive rows hit distinct banks.
+constexpr int BK2 = 64, LDS2 = BK2 + 8;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kv_recompute_kernel_k64(RecomputeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS2];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = a.b * a.l, N = 2 * a.h, K = a.h;
+  const int n_tiles_n = N / BN;
+  const int tile_m = blockIdx.x / n_tiles_n, tile_n = blockIdx.x % n_tiles_n;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const bool is_v = n0 >= a.h;
+  const uint16_t* W = is_v ? a.wv : a.wk;
+  const int wn0 = is_v ? n0 - a.h : n0;
+  const int am = tid >> 3, ak = (tid & 7) * 8;
+  const uint16_t* xrow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = min(m0 + am + 32 * i, M - 1);
+    const int bi = r / a.l, t = r - bi * a.l;
+    xrow[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
+  }
+  const uint16_t* wsrc = W + (int64_t)(wn0 + am) * a.h + ak;
+  u32x4 sa[8], sb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sa[i] = load_b128(xrow[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sb[i] = load_b128(wsrc + (int64_t)32 * i * a.h + k0);
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store_b128(&As[(am + 32 * i) * LDS2 + ak], sa[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_b128(&Bs[(am + 32 * i) * LDS2 + ak], sb[i]);
+  };
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int nk = K / BK2;
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((kt + 1) * BK2);
+#pragma unroll
+    for (int ks = 0; ks < BK2 / 16; ++ks) {
+      u32x4 fa[4], fb[2];
+      const int kk = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(&As[(wm + 32 * i + (lane & 31)) * LDS2 + kk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const u32x4*>(&Bs[(wn + 32 * j + (lane & 31)) * LDS2 + kk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      lstore();
+      __syncthreads();
+    }
+  }
+  uint16_t* C = is_v ? a.vc : a.kc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (r >= M) continue;
+      const int bi = r / a.l, t = r - bi * a.l;
+      uint16_t* crow = C + (int64_t)bi * a.c_bstride + (int64_t)t * a.h + wn0 + wn + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) crow[32 * j] = to_bits<KIND_F16>(acc[i][j][e]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
@@ -196,9 +267,9 @@ hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
   timing_begin(stream);
   if (a.w_layout == KVDEC_W_OUT_IN)
-    kv_recompute_kernel<KVDEC_W_OUT_IN><<<(unsigned)blocks, 256, 0, stream>>>(a);
+    kv_recompute_kernel_k64<<<(unsigned)blocks, 256, 0, stream>>>(a);
   else
-    kv_recompute_kernel<KVDEC_W_IN_OUT><<<(unsigned)blocks, 256, 0, stream>>>(a);
+    kv_recompute_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
   timing_end(stream);
   return hipGetLastError();
 }
