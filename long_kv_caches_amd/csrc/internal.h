@@ -16,7 +16,6 @@ constexpr int kHeadDim = 128;     // the one supported head_dim
 constexpr int kTile = 16;         // tokens per wave tile (one MFMA row block)
 constexpr int kWaves = 4;         // waves per attention workgroup
 constexpr int kMaxGroup = 8;      // query heads per KV head handled by one workgroup
-constexpr int kMaxChunks = 512;   // partials merged per LDS batch
 constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
 constexpr int kMinTilesPerWave = 8;
 constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-round column
