@@ -155,3 +155,12 @@ def test_paged_llama2_full_size_sampled():
                                       seqlens=lens[pick], block_table=d["block_table"][pick])
     check_close(host_f64(out)[pick], ref_o, "paged full size (sampled sequences)")
     check_lse(lse[pick], ref_l, "paged full size lse (sampled)")
+
+
+def test_many_sequences_fall_back_to_chunks():
+    """More sequences than the balanced schedule keeps in LDS (4096): the
+    default plan falls back to fixed chunks."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, 80, size=5000).tolist()
+    d = kvgen.ragged_llama(seed=21, lens=lens, Hq=8, Hkv=2)
+    _parity(d, "ragged B=5000 short sequences (default plan)", split_tokens=0)
