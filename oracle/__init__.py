@@ -65,6 +65,10 @@ def _load():
     lib.orc_kv_recompute.restype = i32
     lib.orc_kvpr_cost.argtypes = [f64, f64, f64, f64, f64, P, P, P]
     lib.orc_kvpr_cost.restype = None
+    lib.orc_kvpr_time.argtypes = [f64] * 7
+    lib.orc_kvpr_time.restype = f64
+    lib.orc_kvpr_best_split.argtypes = [f64, ctypes.c_int, ctypes.c_int, f64, f64, f64, f64, P]
+    lib.orc_kvpr_best_split.restype = ctypes.c_int
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i32
     _lib = lib
@@ -220,3 +224,17 @@ def kvpr_cost(b, l, s_prime, h, p):
     _load().orc_kvpr_cost(float(b), float(l), float(s_prime), float(h), float(p),
                           ctypes.byref(mx), ctypes.byref(mkv), ctypes.byref(nf))
     return mx.value, mkv.value, nf.value
+
+
+def kvpr_time(b, l, s_prime, h, p, v_com, v_gpu):
+    """KVPR section A2 layer time t(l) = M_X/v_com + max(N/v_gpu, M_KV/v_com)."""
+    return _load().orc_kvpr_time(float(b), float(l), float(s_prime), float(h), float(p),
+                                 float(v_com), float(v_gpu))
+
+
+def kvpr_best_split(b, s_prime, l_max, h, p, v_com, v_gpu):
+    """(l, t) of least t(l) over every integer l in [0, l_max], tried one by one."""
+    t = ctypes.c_double()
+    l = _load().orc_kvpr_best_split(float(b), int(s_prime), int(l_max), float(h), float(p),
+                                    float(v_com), float(v_gpu), ctypes.byref(t))
+    return l, t.value

@@ -351,3 +351,30 @@ void orc_kvpr_cost(double b, double l, double s_prime, double h, double p,
   *m_kv = 2.0 * b * (s_prime - l) * h * p;
   *n_flops = 4.0 * b * l * h * h;
 }
+
+/* KVPR page, section A2, total time of one layer with split point l:
+ * t(l) = M_X / v_com + max(N / v_gpu, M_KV / v_com). */
+double orc_kvpr_time(double b, double l, double s_prime, double h, double p, double v_com,
+                     double v_gpu) {
+  double m_x, m_kv, n;
+  orc_kvpr_cost(b, l, s_prime, h, p, &m_x, &m_kv, &n);
+  const double t_rec = n / v_gpu, t_kv = m_kv / v_com;
+  return m_x / v_com + (t_rec > t_kv ? t_rec : t_kv);
+}
+
+/* The split point of least t(l) over every integer l in [0, l_max], by
+ * trying each one; the first (smallest) l wins ties. */
+int orc_kvpr_best_split(double b, int s_prime, int l_max, double h, double p, double v_com,
+                        double v_gpu, double* t_best) {
+  int best = 0;
+  double tb = orc_kvpr_time(b, 0.0, s_prime, h, p, v_com, v_gpu);
+  for (int l = 1; l <= l_max; ++l) {
+    const double t = orc_kvpr_time(b, (double)l, s_prime, h, p, v_com, v_gpu);
+    if (t < tb) {
+      tb = t;
+      best = l;
+    }
+  }
+  if (t_best) *t_best = tb;
+  return best;
+}

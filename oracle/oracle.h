@@ -112,6 +112,15 @@ int orc_kv_recompute(int b, int l, int h, int kind, const uint16_t* x, int64_t x
 void orc_kvpr_cost(double b, double l, double s_prime, double h, double p,
                    double* m_x, double* m_kv, double* n_flops);
 
+/* KVPR page, section A2: t(l) = M_X / v_com + max(N / v_gpu, M_KV / v_com). */
+double orc_kvpr_time(double b, double l, double s_prime, double h, double p, double v_com,
+                     double v_gpu);
+
+/* Split point of least t(l) by trying every l in [0, l_max] (smallest l on
+ * ties); *t_best (may be NULL) gets its time. */
+int orc_kvpr_best_split(double b, int s_prime, int l_max, double h, double p, double v_com,
+                        double v_gpu, double* t_best);
+
 /* Threads the OpenMP runtime would use for nthreads <= 0. */
 int orc_max_threads(void);
 

@@ -3,6 +3,7 @@ vectors, zero input, numpy's fp64 matmul and the printed Table 1 sizes."""
 import os
 
 import numpy as np
+import pytest
 
 import kvgen
 import oracle
@@ -76,3 +77,37 @@ def test_kvpr_cost_closed_forms():
     assert m_x == 32 * 256 * 5120 * 2
     assert m_kv == 2 * 32 * (1024 - 256) * 5120 * 2
     assert n == 4 * 32 * 256 * 5120 ** 2  # = 2 (b l) h (2 h): two h x h products
+
+
+def test_kvpr_time_is_the_section_a2_formula_at_its_ends():
+    """At l = 0 nothing is recomputed: t = M_KV(0) / v_com, the whole cache over
+    PCIe.  At l = s' nothing but X crosses: t = M_X(s') / v_com + N(s') / v_gpu."""
+    b, s, h, p, vc, vg = 32, 1024, 5120, 2, 50e9, 1e15
+    assert oracle.kvpr_time(b, 0, s, h, p, vc, vg) == 2 * b * s * h * p / vc
+    assert np.isclose(oracle.kvpr_time(b, s, s, h, p, vc, vg),
+                      b * s * h * p / vc + 4 * b * s * h * h / vg, rtol=1e-15)
+
+
+@pytest.mark.parametrize("vc,vg", [(50e9, 1e15), (25e9, 3e14), (1e12, 1e14), (8e9, 2.5e15)])
+def test_kvpr_best_split_at_the_crossing(vc, vg):
+    """t(l) = a l + max(c l, d (s' - l)) with a = d / 2: it falls while the
+    transfer of the rows left dominates and rises after, so the scan's l must
+    be one of the two integers around l_c = d s' / (c + d) (clamped)."""
+    b, s, h, p = 32, 1024, 5120, 2
+    c = 4 * b * h * h / vg
+    d = 2 * b * h * p / vc
+    lc = d * s / (c + d)
+    for l_max in (s, 300, 0):
+        l, t = oracle.kvpr_best_split(b, s, l_max, h, p, vc, vg)
+        cands = sorted({min(max(int(np.floor(lc)), 0), l_max), min(max(int(np.ceil(lc)), 0), l_max)})
+        best = min(cands, key=lambda x: (oracle.kvpr_time(b, x, s, h, p, vc, vg), x))
+        assert l == best, (l, cands)
+        assert t == oracle.kvpr_time(b, l, s, h, p, vc, vg)
+
+
+def test_kvpr_best_split_limits():
+    """Free compute recomputes every row it may; free transfer recomputes none."""
+    b, s, h, p = 4, 500, 1024, 2
+    assert oracle.kvpr_best_split(b, s, s, h, p, 1e9, 1e30)[0] == s
+    assert oracle.kvpr_best_split(b, s, 123, h, p, 1e9, 1e30)[0] == 123
+    assert oracle.kvpr_best_split(b, s, s, h, p, 1e30, 1e9)[0] == 0
