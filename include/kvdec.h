@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 2
+#define KVDEC_ABI_VERSION 3
 
 typedef enum {
   KVDEC_OK = 0,
@@ -212,11 +212,60 @@ kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_hea
                                 void* k_cache, void* v_cache, int64_t cache_batch_stride,
                                 hipStream_t stream);
 
+/*
+ * KVPR split point (KVPR page, section A2, the scheduler's choice of l): the
+ * integer l in [0, l_max] that minimises the layer time
+ *   t(l) = M_X(l) / v_com + max(N(l) / v_gpu, M_KV(l) / v_com),
+ *   M_X = b l h p,  M_KV = 2 b (s' - l) h p,  N = 4 b l h^2,
+ * with p = elem_bytes, v_com the host-to-device rate in bytes/s and v_gpu the
+ * recompute rate in FLOP/s.  t falls while the transfer of the rows left
+ * dominates and rises after, so the minimum is at one of the two integers
+ * around the crossing (clamped to [0, l_max]); ties go to the smaller l.
+ * Host only; *t_out (may be NULL) gets t(l) in seconds.
+ * Requires b >= 0, 0 <= l_max <= s_prime, h >= 1, elem_bytes >= 1 and
+ * finite v_com, v_gpu > 0.
+ */
+kvdec_status kvdec_kvpr_split(int64_t b, int64_t s_prime, int64_t l_max, int64_t h,
+                              int32_t elem_bytes, double v_com, double v_gpu, int32_t* l_out,
+                              double* t_out);
+
+/*
+ * One KVPR layer load (KVPR page, section A2, runtime module: the activations
+ * of the first l tokens cross PCIe first and the GPU recomputes their K/V
+ * while the K/V rows [l, s') are still in transfer).  Enqueues
+ *   on copy_stream:    host-to-device copies of X[0:l] into x_dev, then of
+ *                      the K and V rows [l, s') into k_cache, v_cache;
+ *   on compute_stream: once X has arrived, the recompute of rows [0, l)
+ *                      (as kvdec_kv_recompute), then a wait for the K/V
+ *                      copies, so work queued on compute_stream after this
+ *                      call sees cache rows [0, s') complete.
+ *   x_host   [b, *, h] bf16, pinned host memory, batch stride x_host_bstride
+ *            elements (>= l*h)
+ *   x_dev    [b, l, h] bf16 device staging buffer (written)
+ *   k_host, v_host  [b, *, H, head_dim] fp16 pinned host memory, batch stride
+ *            kv_host_bstride elements (>= s_prime*h); rows [l, s_prime) are read
+ *   w_k, w_v, w_layout, k_cache, v_cache, cache_bstride (>= s_prime*h): as in
+ *            kvdec_kv_recompute
+ * compute_stream and copy_stream must differ.  The call orders only its own
+ * work: x_dev and the cache rows it writes must not be in use by work already
+ * queued on either stream.  Without page-locked host memory the copies are
+ * not asynchronous.  Requires 0 <= l <= s_prime and the kvdec_kv_recompute
+ * shape rules; l == 0 copies everything, l == s_prime recomputes everything.
+ */
+kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_t h,
+                                   int32_t num_heads, int32_t head_dim, const void* x_host,
+                                   int64_t x_host_bstride, void* x_dev, const void* k_host,
+                                   const void* v_host, int64_t kv_host_bstride, const void* w_k,
+                                   const void* w_v, int32_t w_layout, void* k_cache, void* v_cache,
+                                   int64_t cache_bstride, hipStream_t compute_stream,
+                                   hipStream_t copy_stream);
+
 /* Kernel timing, a profiling aid.  While enabled on the calling thread, every
  * call above records a pair of HIP events on its stream right before and
  * right after its main kernel launch: the split kernel of an attention call
  * (not the merge kernel), the lookup kernel of kvdec_headcache_lookup (not
- * the compaction kernel), the GEMM of kvdec_kv_recompute.
+ * the compaction kernel), the GEMM of kvdec_kv_recompute and of
+ * kvdec_kvpr_load_layer.
  * kvdec_kernel_timing(1) starts a new measurement (the library keeps and
  * reuses its events); kvdec_kernel_timing(0) stops recording.
  * kvdec_kernel_timing_read waits for the recorded events and returns the

@@ -60,6 +60,10 @@ def _load():
         "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
         "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, i32, P, P, i64, P], st),
+        "kvdec_kvpr_split": ([i64, i64, i64, i64, i32, ctypes.c_double, ctypes.c_double,
+                              ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)], st),
+        "kvdec_kvpr_load_layer": ([i32, i32, i32, i32, i32, i32, P, i64, P, P, P, i64, P, P, i32, P,
+                                   P, i64, P, P], st),
         "kvdec_kernel_timing": ([ctypes.c_int], st),
         "kvdec_kernel_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
         "kvdec_status_string": ([st], ctypes.c_char_p),
@@ -76,7 +80,8 @@ def _load():
 lib = _load()
 EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
             "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_thresholds",
-            "kvdec_kv_recompute", "kvdec_kernel_timing", "kvdec_kernel_timing_read", "kvdec_status_string",
+            "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
+            "kvdec_kernel_timing_read", "kvdec_status_string",
             "kvdec_last_error", "kvdec_abi_version")
 
 
@@ -133,6 +138,38 @@ def kvdec_sparse_hybrid_attn_workspace(desc: HybridDesc) -> int:
     n = ctypes.c_size_t()
     _check(lib.kvdec_sparse_hybrid_attn_workspace(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
+
+
+def kvdec_kvpr_split(b, s_prime, l_max, h, elem_bytes, v_com, v_gpu):
+    """KVPR split point: (l, t(l) in seconds) minimising the section A2 layer time."""
+    l, t = ctypes.c_int32(), ctypes.c_double()
+    _check(lib.kvdec_kvpr_split(int(b), int(s_prime), int(l_max), int(h), int(elem_bytes),
+                                float(v_com), float(v_gpu), ctypes.byref(l), ctypes.byref(t)))
+    return l.value, t.value
+
+
+def _host_ptr(t):
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise TypeError("expected a host (CPU) torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvdec_kvpr_load_layer(x_host, x_dev, k_host, v_host, w_k, w_v, k_cache, v_cache, l, s_prime,
+                          w_layout=0, compute_stream=None, copy_stream=None):
+    """x_host [b, s_x, h] bf16 and k_host, v_host [b, s_cap_h, H, 128] fp16 in pinned host
+    memory; x_dev [b, l, h] bf16 staging; caches [b, s_cap, H, 128] fp16 (rows [0, s') made
+    complete on compute_stream)."""
+    b, s_x, h = x_host.shape
+    H, hd = k_cache.shape[2], k_cache.shape[3]
+    if copy_stream is None:
+        raise ValueError("copy_stream is required (a stream other than compute_stream)")
+    _check(lib.kvdec_kvpr_load_layer(b, int(l), int(s_prime), h, H, hd, _host_ptr(x_host), s_x * h,
+                                     _ptr(x_dev), _host_ptr(k_host), _host_ptr(v_host),
+                                     k_host.shape[1] * H * hd, _ptr(w_k), _ptr(w_v), int(w_layout),
+                                     _ptr(k_cache), _ptr(v_cache), k_cache.shape[1] * H * hd,
+                                     _stream(compute_stream), _stream(copy_stream)))
 
 
 def kvdec_kernel_timing(enable: bool) -> None:

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include <utility>
 #include <vector>
@@ -222,6 +223,37 @@ void timing_end(hipStream_t stream) {
   if ((t.err = hipEventRecord(t.pool[t.used].second, stream)) == hipSuccess) ++t.used;
 }
 
+// Checks the kvdec_kv_recompute arguments and fills a.
+static kvdec_status recompute_args(int32_t b, int32_t l, int32_t h, int32_t num_heads,
+                                   int32_t head_dim, const void* x, int64_t x_batch_stride,
+                                   const void* w_k, const void* w_v, int32_t w_layout,
+                                   void* k_cache, void* v_cache, int64_t cache_batch_stride,
+                                   RecomputeArgs* a) {
+  if (b < 0 || l < 0 || h < 1 || num_heads < 1) return fail(KVDEC_ERR_INVALID, "bad sizes");
+  if (w_layout != KVDEC_W_IN_OUT && w_layout != KVDEC_W_OUT_IN)
+    return fail(KVDEC_ERR_INVALID, "w_layout must be KVDEC_W_IN_OUT or KVDEC_W_OUT_IN");
+  if (head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
+  if ((int64_t)num_heads * head_dim != h) return fail(KVDEC_ERR_INVALID, "h != num_heads * head_dim");
+  if (h % 256 != 0) return fail(KVDEC_ERR_UNSUPPORTED, "h must be a multiple of 256");
+  if (x_batch_stride < (int64_t)l * h || cache_batch_stride < (int64_t)l * h)
+    return fail(KVDEC_ERR_INVALID, "batch strides smaller than l * h");
+  if (b == 0 || l == 0) return ok();
+  if (!x || !w_k || !w_v || !k_cache || !v_cache)
+    return fail(KVDEC_ERR_INVALID, "x, w_k, w_v, k_cache and v_cache must be non-NULL");
+  a->x = static_cast<const uint16_t*>(x);
+  a->wk = static_cast<const uint16_t*>(w_k);
+  a->wv = static_cast<const uint16_t*>(w_v);
+  a->kc = static_cast<uint16_t*>(k_cache);
+  a->vc = static_cast<uint16_t*>(v_cache);
+  a->x_bstride = x_batch_stride;
+  a->c_bstride = cache_batch_stride;
+  a->b = b;
+  a->l = l;
+  a->h = h;
+  a->w_layout = w_layout;
+  return ok();
+}
+
 }  // namespace kvdec
 
 using namespace kvdec;
@@ -428,30 +460,115 @@ kvdec_status kvdec_kv_recompute(int32_t b, int32_t l, int32_t h, int32_t num_hea
                                 const void* w_k, const void* w_v, int32_t w_layout,
                                 void* k_cache, void* v_cache, int64_t cache_batch_stride,
                                 hipStream_t stream) {
-  if (b < 0 || l < 0 || h < 1 || num_heads < 1) return fail(KVDEC_ERR_INVALID, "bad sizes");
-  if (w_layout != KVDEC_W_IN_OUT && w_layout != KVDEC_W_OUT_IN)
-    return fail(KVDEC_ERR_INVALID, "w_layout must be KVDEC_W_IN_OUT or KVDEC_W_OUT_IN");
-  if (head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
-  if ((int64_t)num_heads * head_dim != h) return fail(KVDEC_ERR_INVALID, "h != num_heads * head_dim");
-  if (h % 256 != 0) return fail(KVDEC_ERR_UNSUPPORTED, "h must be a multiple of 256");
-  if (x_batch_stride < (int64_t)l * h || cache_batch_stride < (int64_t)l * h)
-    return fail(KVDEC_ERR_INVALID, "batch strides smaller than l * h");
-  if (b == 0 || l == 0) return ok();
-  if (!x || !w_k || !w_v || !k_cache || !v_cache)
-    return fail(KVDEC_ERR_INVALID, "x, w_k, w_v, k_cache and v_cache must be non-NULL");
   RecomputeArgs a = {};
-  a.x = static_cast<const uint16_t*>(x);
-  a.wk = static_cast<const uint16_t*>(w_k);
-  a.wv = static_cast<const uint16_t*>(w_v);
-  a.kc = static_cast<uint16_t*>(k_cache);
-  a.vc = static_cast<uint16_t*>(v_cache);
-  a.x_bstride = x_batch_stride;
-  a.c_bstride = cache_batch_stride;
-  a.b = b;
-  a.l = l;
-  a.h = h;
-  a.w_layout = w_layout;
+  kvdec_status st = recompute_args(b, l, h, num_heads, head_dim, x, x_batch_stride, w_k, w_v,
+                                   w_layout, k_cache, v_cache, cache_batch_stride, &a);
+  if (st != KVDEC_OK || b == 0 || l == 0) return st;
   return hip_status(launch_kv_recompute(a, stream), "kv recompute launch");
+}
+
+kvdec_status kvdec_kvpr_split(int64_t b, int64_t s_prime, int64_t l_max, int64_t h,
+                              int32_t elem_bytes, double v_com, double v_gpu, int32_t* l_out,
+                              double* t_out) {
+  if (!l_out) return fail(KVDEC_ERR_INVALID, "l_out is NULL");
+  if (b < 0 || s_prime < 0 || l_max < 0 || l_max > s_prime || s_prime > INT32_MAX || h < 1 ||
+      elem_bytes < 1)
+    return fail(KVDEC_ERR_INVALID, "need b >= 0, 0 <= l_max <= s_prime < 2^31, h >= 1, elem_bytes >= 1");
+  if (!(std::isfinite(v_com) && v_com > 0.0 && std::isfinite(v_gpu) && v_gpu > 0.0))
+    return fail(KVDEC_ERR_INVALID, "v_com and v_gpu must be finite and > 0");
+  const double B = (double)b, S = (double)s_prime, H = (double)h, p = (double)elem_bytes;
+  auto t_of = [&](double l) {
+    const double t_x = B * l * H * p / v_com;
+    const double t_rec = 4.0 * B * l * H * H / v_gpu;
+    const double t_kv = 2.0 * B * (S - l) * H * p / v_com;
+    return t_x + std::max(t_rec, t_kv);
+  };
+  // crossing of the recompute time c l and the remaining transfer d (s' - l)
+  const double c = 4.0 * H * H / v_gpu, d = 2.0 * H * p / v_com;
+  const double lc = d * S / (c + d);
+  int64_t best = 0;
+  double tb = t_of(0.0);
+  const double cands[2] = {std::floor(lc), std::ceil(lc)};
+  for (double x : cands) {
+    const int64_t l = std::min<int64_t>(std::max<int64_t>((int64_t)x, 0), l_max);
+    const double t = t_of((double)l);
+    if (t < tb || (t == tb && l < best)) {
+      tb = t;
+      best = l;
+    }
+  }
+  const double t_max = t_of((double)l_max);
+  if (t_max < tb) {
+    tb = t_max;
+    best = l_max;
+  }
+  *l_out = (int32_t)best;
+  if (t_out) *t_out = tb;
+  return ok();
+}
+
+// Per-thread events that order the copies of a layer load against its
+// recompute (reused from call to call: a wait always refers to the record
+// just before it).
+struct LoadEvents {
+  hipEvent_t x_done = nullptr, kv_done = nullptr;
+};
+static thread_local LoadEvents g_load_events;
+
+kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_t h,
+                                   int32_t num_heads, int32_t head_dim, const void* x_host,
+                                   int64_t x_host_bstride, void* x_dev, const void* k_host,
+                                   const void* v_host, int64_t kv_host_bstride, const void* w_k,
+                                   const void* w_v, int32_t w_layout, void* k_cache, void* v_cache,
+                                   int64_t cache_bstride, hipStream_t compute_stream,
+                                   hipStream_t copy_stream) {
+  if (l < 0 || s_prime < l) return fail(KVDEC_ERR_INVALID, "need 0 <= l <= s_prime");
+  if (compute_stream == copy_stream)
+    return fail(KVDEC_ERR_INVALID, "compute_stream and copy_stream must differ");
+  RecomputeArgs a = {};
+  kvdec_status st = recompute_args(b, l, h, num_heads, head_dim, x_dev, (int64_t)l * h, w_k, w_v,
+                                   w_layout, k_cache, v_cache, cache_bstride, &a);
+  if (st != KVDEC_OK) return st;
+  if (x_host_bstride < (int64_t)l * h) return fail(KVDEC_ERR_INVALID, "x_host_bstride < l * h");
+  if (kv_host_bstride < (int64_t)s_prime * h || cache_bstride < (int64_t)s_prime * h)
+    return fail(KVDEC_ERR_INVALID, "kv_host_bstride and cache_bstride must be >= s_prime * h");
+  if (b == 0 || s_prime == 0) return ok();
+  if ((s_prime > l && (!k_host || !v_host)) || (l > 0 && !x_host))
+    return fail(KVDEC_ERR_INVALID, "x_host, k_host and v_host must be non-NULL where rows are read");
+  LoadEvents& ev = g_load_events;
+  if (!ev.x_done) {
+    hipError_t e = hipEventCreateWithFlags(&ev.x_done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev.kv_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (ev.x_done) (void)hipEventDestroy(ev.x_done);
+      ev.x_done = nullptr;
+      return hip_status(e, "event create");
+    }
+  }
+  const size_t e2 = sizeof(uint16_t);
+  hipError_t e = hipSuccess;
+  if (l > 0) {
+    e = hipMemcpy2DAsync(x_dev, (size_t)l * h * e2, x_host, (size_t)x_host_bstride * e2,
+                         (size_t)l * h * e2, (size_t)b, hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(ev.x_done, copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(compute_stream, ev.x_done, 0);
+    if (e != hipSuccess) return hip_status(e, "activation copy");
+    e = launch_kv_recompute(a, compute_stream);
+    if (e != hipSuccess) return hip_status(e, "kv recompute launch");
+  }
+  if (s_prime > l) {
+    const size_t off = (size_t)l * h * e2, width = (size_t)(s_prime - l) * h * e2;
+    const void* srcs[2] = {k_host, v_host};
+    void* dsts[2] = {k_cache, v_cache};
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+      e = hipMemcpy2DAsync(static_cast<char*>(dsts[i]) + off, (size_t)cache_bstride * e2,
+                           static_cast<const char*>(srcs[i]) + off, (size_t)kv_host_bstride * e2,
+                           width, (size_t)b, hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(ev.kv_done, copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(compute_stream, ev.kv_done, 0);
+    if (e != hipSuccess) return hip_status(e, "K/V copy");
+  }
+  return ok();
 }
 
 

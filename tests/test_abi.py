@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 2
+    assert _lib.lib.kvdec_abi_version() == 3
 
 
 def test_status_strings():
@@ -164,3 +164,35 @@ def test_null_kv_only_without_rows():
     assert _decode(_desc(kv_rows=100), k=None, v=None) == K._lib.KVDEC_ERR_INVALID
     assert "k and v" in K.last_error()
     assert _decode(_desc(layout=K.KVDEC_DENSE, max_seqlen=16), k=None) == K._lib.KVDEC_ERR_INVALID
+
+
+def test_kvpr_split_matches_the_oracle_scan():
+    """The closed-form split point equals the oracle's try-every-l scan."""
+    rng = np.random.default_rng(5)
+    cases = [(32, 1024, 1024, 5120, 2, 50e9, 1e15), (32, 1024, 256, 5120, 2, 50e9, 1e15),
+             (1, 1, 1, 256, 2, 1e9, 1e9), (4, 0, 0, 512, 2, 1e9, 1e12)]
+    for _ in range(300):
+        s = int(rng.integers(0, 3000))
+        cases.append((int(rng.integers(1, 64)), s, int(rng.integers(0, s + 1)), int(rng.integers(1, 9000)),
+                      int(rng.choice([1, 2, 4])), float(10 ** rng.uniform(8, 12)), float(10 ** rng.uniform(11, 16))))
+    for b, s, lmax, h, p, vc, vg in cases:
+        l, t = K.kvdec_kvpr_split(b, s, lmax, h, p, vc, vg)
+        lo, to = oracle.kvpr_best_split(b, s, lmax, h, p, vc, vg)
+        assert abs(t - to) <= 1e-12 * max(to, 1e-30), (b, s, lmax, h, p, vc, vg)
+        # equal times: the oracle keeps the smallest l, so l may only differ on an exact tie
+        assert l == lo or oracle.kvpr_time(b, l, s, h, p, vc, vg) == to
+
+
+def test_kvpr_split_and_load_validation():
+    with pytest.raises(K.KvdecError):
+        K.kvdec_kvpr_split(1, 10, 11, 256, 2, 1e9, 1e12)  # l_max > s'
+    with pytest.raises(K.KvdecError):
+        K.kvdec_kvpr_split(1, 10, 5, 256, 2, 0.0, 1e12)
+    L = _lib.lib.kvdec_kvpr_load_layer
+    S1, S2 = ctypes.c_void_p(0x10), ctypes.c_void_p(0x20)
+    args = (FAKE, 4 * 512, FAKE, FAKE, FAKE, 8 * 512, FAKE, FAKE, 0, FAKE, FAKE, 8 * 512)
+    assert L(2, 4, 8, 512, 4, 128, *args, S1, S1) == K._lib.KVDEC_ERR_INVALID  # same stream
+    assert "differ" in K.last_error()
+    assert L(2, 9, 8, 512, 4, 128, *args, S1, S2) == K._lib.KVDEC_ERR_INVALID  # l > s'
+    assert L(2, 4, 8, 512, 4, 128, *args[:5], 7 * 512, *args[6:], S1, S2) == K._lib.KVDEC_ERR_INVALID
+    assert "s_prime" in K.last_error()

@@ -109,3 +109,39 @@ def test_end_to_end_against_fp64_recompute():
     ro, _ = oracle.decode_attn(d["q"], kref, vref, num_kv_heads=8, layout=oracle.DENSE,
                                scale=d["scale"])
     check_close(host_f64(out), ro, "end to end")
+
+
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+@pytest.mark.parametrize("l", [0, 40, 96])
+def test_kvpr_load_layer(l, w_layout):
+    """Overlapped layer load: rows [0, l) recomputed from X copied in from
+    pinned host memory, rows [l, s') copied bit for bit from the pinned host
+    cache, rows from s' on left untouched; the staging buffer holds X[0:l]."""
+    b, h, H, s_cap, s_prime = 2, 512, 4, 120, 96
+    d = kvgen.kvpr_layer(seed=6, b=b, h=h, H=H, s=s_cap, l=s_prime)   # X: s' rows of activations
+    kv = kvgen.kvpr_layer(seed=7, b=b, h=h, H=H, s=s_cap, l=0)        # host cache: every row drawn
+    conv = (lambda w: np.ascontiguousarray(w.T)) if w_layout == K.KVDEC_W_OUT_IN else (lambda w: w)
+    x_host = torch.from_numpy(d["x"].view(np.int16)).pin_memory()
+    k_host = torch.from_numpy(kv["k_cache"]).pin_memory()
+    v_host = torch.from_numpy(kv["v_cache"]).pin_memory()
+    wk = dev(conv(d["w_k"]), bf16=True)
+    wv = dev(conv(d["w_v"]), bf16=True)
+    kc = torch.full((b, s_cap, H, 128), 1000.0, dtype=torch.float16, device="cuda")
+    vc = torch.full((b, s_cap, H, 128), 1000.0, dtype=torch.float16, device="cuda")
+    x_dev = torch.zeros((b, max(l, 1), h), dtype=torch.bfloat16, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    say(f"[kvpr load] l={l} s'={s_prime} w_layout={w_layout}")
+    K.kvdec_kvpr_load_layer(x_host, x_dev, k_host, v_host, wk, wv, kc, vc, l, s_prime, w_layout,
+                            copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    kb = bits(kc).reshape(b, s_cap, h)
+    vb = bits(vc).reshape(b, s_cap, h)
+    poison = np.float16(1000.0).view(np.uint16)
+    assert np.all(kb[:, s_prime:] == poison) and np.all(vb[:, s_prime:] == poison)
+    assert np.array_equal(kb[:, l:s_prime], kv["k_cache"].view(np.uint16).reshape(b, s_cap, h)[:, l:s_prime])
+    assert np.array_equal(vb[:, l:s_prime], kv["v_cache"].view(np.uint16).reshape(b, s_cap, h)[:, l:s_prime])
+    if l > 0:
+        assert np.array_equal(bits(x_dev), d["x"][:, :l])
+        ko, vo = oracle.kv_recompute(d["x"], d["w_k"], d["w_v"], l=l)
+        check_close(host_f64(kc).reshape(b, s_cap, h)[:, :l].reshape(b * l, h), ko, "K rows [0, l)")
+        check_close(host_f64(vc).reshape(b, s_cap, h)[:, :l].reshape(b * l, h), vo, "V rows [0, l)")
