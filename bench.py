@@ -61,7 +61,7 @@ def measured_traffic(per_launch_algorithmic):
 
 
 WORKLOADS = ("llama3-8b-32k", "llama2-7b-paged", "clo-llama3-8b-128k", "clo-qwen2.5-14b-128k",
-             "kvpr-opt13b")
+             "kvpr-opt13b", "kvpr-overlap")
 
 
 def prewarm(torch, dev, ms):
@@ -362,6 +362,96 @@ def bench_kvpr(args, K, np, torch, dev, stream):
     return r
 
 
+def bench_kvpr_overlap(args, K, np, torch, dev, stream):
+    """One OPT-13B layer load with partial recompute: X[0:l] and K/V[l:s') cross
+    PCIe from pinned host memory on a copy stream while the GPU recomputes
+    K/V[0:l].  v_com (pinned host-to-device rate) and v_gpu (recompute rate)
+    are measured here, l comes from kvdec_kvpr_split, and the load is timed at
+    that l, at l = 0 (transfer only), at the 256 of the recompute config and at
+    l = s' (recompute only)."""
+    import kvgen
+    b, h, H, D, s = 32, 5120, 40, 128, 1024
+    d = kvgen.kvpr_layer(seed=args.seed, b=b, h=h, H=H, s=s, l=s)     # activations of all s' rows
+    kv = kvgen.kvpr_layer(seed=args.seed + 1, b=b, h=h, H=H, s=s, l=0)  # a full host cache
+    x_host = torch.from_numpy(d["x"].view(np.int16)).pin_memory()
+    k_host = torch.from_numpy(kv["k_cache"]).pin_memory()
+    v_host = torch.from_numpy(kv["v_cache"]).pin_memory()
+    wk = torch.from_numpy(np.ascontiguousarray(d["w_k"].T).view(np.int16)).to(dev).view(torch.bfloat16)
+    wv = torch.from_numpy(np.ascontiguousarray(d["w_v"].T).view(np.int16)).to(dev).view(torch.bfloat16)
+    kc = torch.empty((b, s, H, D), dtype=torch.float16, device=dev)
+    vc = torch.empty_like(kc)
+    x_dev = torch.empty((b, s, h), dtype=torch.bfloat16, device=dev)
+    copy_stream = torch.cuda.Stream(dev)
+    prewarm(torch, dev, args.prewarm_ms)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        copy_stream.wait_event(e0)  # both streams start at e0
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3  # seconds
+
+    # v_com: the K and V rows of the whole cache from pinned memory, on the copy stream
+    kv_bytes = 2 * b * s * h * 2
+
+    def h2d():
+        with torch.cuda.stream(copy_stream):
+            kc.copy_(k_host.view_as(kc), non_blocking=True)
+            vc.copy_(v_host.view_as(vc), non_blocking=True)
+        stream.wait_stream(copy_stream)
+    v_com = kv_bytes / timed(h2d, 5)
+    # v_gpu: the recompute at the recompute config's split point
+    x_dev_l = torch.empty((b, 256, h), dtype=torch.bfloat16, device=dev)
+    x_dev_l.copy_(torch.from_numpy(d["x"][:, :256].copy().view(np.int16)).view(torch.bfloat16).to(dev))
+    v_gpu = 4.0 * b * 256 * h * h / timed(
+        lambda: K.kvdec_kv_recompute(x_dev_l, wk, wv, kc, vc, 256, K.KVDEC_W_OUT_IN, stream=stream), 10)
+    l_best, t_model = K.kvdec_kvpr_split(b, s, s, h, 2, v_com, v_gpu)
+
+    def load(l):
+        def one():
+            # layers one after another (the row-wise, latency schedule): this
+            # layer's copies wait for the work already queued on the compute
+            # stream, which also frees x_dev and the cache for them
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            copy_stream.wait_event(ev)
+            K.kvdec_kvpr_load_layer(x_host, x_dev, k_host, v_host, wk, wv, kc, vc, l, s,
+                                    K.KVDEC_W_OUT_IN, compute_stream=stream, copy_stream=copy_stream)
+        return one
+    reps = max(3, min(args.steps, 20))
+    rows = {}
+    def model(l):  # the section A2 layer time with the measured rates
+        return b * l * h * 2 / v_com + max(4.0 * b * l * h * h / v_gpu, 2.0 * b * (s - l) * h * 2 / v_com)
+    for l in sorted({0, 256, l_best, s}):
+        rows[str(l)] = {"ms": round(timed(load(l), reps) * 1e3, 4), "model_ms": round(model(l) * 1e3, 4)}
+    t_best = rows[str(l_best)]["ms"]
+    r = common(args, "kvpr-opt13b-overlapped-layer-load",
+               "KVPR layer load with partial recompute: ms per layer (X[0:l] + K/V[l:s') over PCIe, "
+               "K/V[0:l] recomputed), OPT-13B b=32 s'=1024", "ms", t_best, t_best, "bf16",
+               "synthetic (seeded; pinned host activations and K/V, W as nn.Linear stores it)",
+               {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "context": s,
+                "split_point": l_best, "w_layout": "out_in (nn.Linear)"}, higher=False)
+    r["steps"] = reps
+    r["v_com_gbs"] = round(v_com / 1e9, 2)
+    r["v_gpu_tflops"] = round(v_gpu / 1e12, 1)
+    r["model_ms_at_split"] = round(t_model * 1e3, 4)
+    r["by_split_point"] = rows
+    r["speedup_vs_transfer_only"] = round(rows["0"]["ms"] / t_best, 3)
+    r["roofline"] = {"bound": "pcie", "kernel": "kvdec_kvpr_load_layer (copies + kv_recompute_kernel_k64)",
+                     "achieved": round((b * l_best * h * 2 + 2 * b * (s - l_best) * h * 2) / (t_best * 1e-3) / 1e9, 2),
+                     "peak": round(v_com / 1e9, 2), "unit": "GB/s", "frac": None, "traffic": None,
+                     "note": "bytes that crossed PCIe per ms of layer load, against the measured "
+                             "pinned host-to-device rate; the model time at the split is model_ms_at_split"}
+    r["roofline"]["frac"] = round(r["roofline"]["achieved"] / r["roofline"]["peak"], 4)
+    return r
+
+
 def calibrate_copy(torch, dev):
     src = torch.ones(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
     dst = torch.empty_like(src)
@@ -403,6 +493,8 @@ def main():
         r = bench_paged(args, K, np, torch, dev, stream)
     elif args.workload.startswith("clo-"):
         r = bench_clo(args, K, np, torch, dev, stream, args.workload[4:-5])
+    elif args.workload == "kvpr-overlap":
+        r = bench_kvpr_overlap(args, K, np, torch, dev, stream)
     else:
         r = bench_kvpr(args, K, np, torch, dev, stream)
     print(json.dumps(r), flush=True)
