@@ -18,6 +18,9 @@ Workload shapes:
   * ``clo_hybrid``   -- CLO head-wise cache at 128K (Llama3-8B 32/8 or
     Qwen2.5-14B 40/8), batch 4: labels, queries near their labels, Beta(0.5, 2)
     importances, 2 persistent heads, a 10% token selection per buffer head.
+  * ``clo_ahead``    -- CLO one-layer-ahead lookup: hidden states x [B, h] of
+    the previous layer, the next layer's W_Q [Hq*D, h] (nn.Linear layout), and
+    hidden states of the step the labels came from (x plus a per-sequence drift).
   * ``kvpr_layer``   -- KVPR OPT-13B layer: h 5120, 40 heads, batch 32,
     s' 1024, split l 256, bf16 X and W, fp16 resident cache rows.
 """
@@ -326,6 +329,37 @@ def clo_hybrid(seed=0, model="llama3-8b", B=4, S=131072, frac=0.1, n_pers=2, D=D
     return dict(base, S=S, k_full=kf, v_full=vf, head_map=hm, pers_k=pers_k, pers_v=pers_v,
                 pers_len=np.full(B, S, np.int32), buf_k=buf_k, buf_v=buf_v, buf_len=buf_len,
                 selection=sel, ksel=ksel, scale=1.0 / math.sqrt(D))
+
+
+CLO_HIDDEN = {"llama3-8b": 4096, "qwen2.5-14b": 5120}
+
+
+def clo_ahead(seed=0, model="llama3-8b", B=4, h=None, Hq=None, Hkv=None, D=D_HEAD,
+              drift=(0.1, 1.0), out_dtype=np.float16):
+    """Inputs of the one-layer-ahead head-cache lookup.
+
+    Draw order: the ``clo_queries`` importances (``Draws(seed).ctl``, first
+    draw only); then from ``Draws(seed + 2000003)``: per-sequence drift scale
+    ~ U[drift] (``ctl``), x_prev [B, h] ~ N(0,1), drift noise [B, h] ~ N(0,1),
+    W_Q [Hq*D, h] ~ N(0, 1/h).  x_label = x_prev + scale_b * noise (fp32, cast
+    once): the hidden state of the step whose query became the label, so the
+    label/query cosines fall as the drift grows.  h, Hq, Hkv default to the
+    model's; out_dtype float16, or uint16 for bfloat16 bits.
+    """
+    mq, mkv = CLO_MODELS[model]
+    Hq = mq if Hq is None else Hq
+    Hkv = mkv if Hkv is None else Hkv
+    h = CLO_HIDDEN[model] if h is None else h
+    s = Draws(seed).ctl.beta(0.5, 2.0, size=Hq)
+    dr = Draws(seed + 2_000_003)
+    scale = dr.ctl.uniform(drift[0], drift[1], size=B).astype(np.float32)
+    x32 = dr.normal((B, h), out_dtype=np.float16).astype(np.float32)
+    noise = dr.normal((B, h), out_dtype=np.float16).astype(np.float32)
+    w = dr.normal((Hq * D, h), out_dtype=out_dtype, std=1.0 / math.sqrt(h))
+    cast = (lambda a: a.astype(np.float16)) if out_dtype == np.float16 else f32_to_bf16_bits
+    return dict(model=model, B=B, Hq=Hq, Hkv=Hkv, D=D, h=h, s=s, weights=s.astype(np.float32),
+                x_prev=cast(x32), x_label=cast(x32 + scale[:, None] * noise), w_q=w,
+                drift=scale, eta=0.8, n_exp=3.0)
 
 
 # ---------------------------------------------------------------------------

@@ -199,6 +199,21 @@ def headcache_lookup(q, labels, weights, tau, *, num_kv_heads, kind=F16):
                 labels=lab, miss_list=ml[:n].copy(), miss_count=n)
 
 
+def approx_query(x_prev, w_q, *, kind=F16):
+    """CLO one-layer-ahead query (CLO page, section 3, decoding flow, Figure 9):
+    q_approx = x_{l-1} W_Q^l in fp64, with W_Q stored output index first
+    ([N, h], as nn.Linear keeps it), so q[b][n] = sum_i x[b][i] W[n][i].
+
+    x_prev [B, h] and w_q [N, h] are 16-bit bits; returns [B, N] fp64.  The
+    products and sums are exact-to-fp64 (numpy matmul as the one step).
+    """
+    x = widen(x_prev, kind)
+    w = widen(w_q, kind)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("approx_query: x_prev [B, h] and w_q [N, h] expected")
+    return x @ w.T
+
+
 def kv_recompute(x, w_k, w_v, *, l, rows=None, kind=BF16, nthreads=0):
     """KVPR partial recompute in fp64: rows of X[:, 0:l] . W_K and . W_V.
 

@@ -177,3 +177,61 @@ def test_generated_cosine_band():
     # finite D = 128 spreads each draw by about +-0.02 around that.
     assert 0.77 < np.percentile(c, 5) and np.percentile(c, 95) < 0.955
     assert 0.85 < np.median(c) < 0.91
+
+
+# ---------------------------------------------------------------------------
+# One-layer-ahead approximate query q_approx = x_{l-1} W_Q^l (CLO page,
+# section 3, decoding flow, Figure 9), W_Q stored output index first.
+# ---------------------------------------------------------------------------
+
+def test_approx_query_basis_rows_pick_weight_columns():
+    # x = e_i gives q[n] = W[n][i] exactly; a transposed operand would give W[i][n]
+    rng = np.random.default_rng(11)
+    h, N = 24, 40
+    w = rng.standard_normal((N, h)).astype(np.float16)
+    x = np.eye(h, dtype=np.float16)[[0, 5, 23]]
+    q = oracle.approx_query(x, w)
+    assert np.array_equal(q, w[:, [0, 5, 23]].T.astype(np.float64))
+
+
+def test_approx_query_brute_force_tiny():
+    rng = np.random.default_rng(12)
+    B, h, N = 3, 8, 6
+    x = rng.integers(-8, 9, (B, h)).astype(np.float16)
+    w = rng.integers(-8, 9, (N, h)).astype(np.float16)
+    q = oracle.approx_query(x, w)
+    for b in range(B):
+        for n in range(N):
+            acc = 0
+            for i in range(h):
+                acc += int(x[b, i]) * int(w[n, i])
+            assert q[b, n] == acc
+
+
+def test_approx_query_matches_the_c_recompute_loop():
+    # the independently written X . W loop, fed W_Q's transpose (input index first)
+    d = kvgen.clo_ahead(seed=13, model="llama3-8b", B=3, h=256, Hq=2, Hkv=1)
+    q = oracle.approx_query(d["x_prev"], d["w_q"])
+    wt = np.ascontiguousarray(d["w_q"].T)
+    k, _ = oracle.kv_recompute(d["x_prev"][:, None, :], wt, wt, l=1, kind=oracle.F16)
+    np.testing.assert_allclose(q, k, rtol=0, atol=1e-12)
+
+
+def test_approx_query_bf16_widening():
+    # bf16 bit patterns of small integers multiply exactly
+    x = kvgen.f32_to_bf16_bits(np.array([[1, 2, -3, 4, 0, 0, 0, 1]], np.float32))
+    w = kvgen.f32_to_bf16_bits(np.array([[1, 1, 1, 1, 1, 1, 1, 1],
+                                         [0, 0, 2, 0, 0, 0, 0, 64]], np.float32))
+    assert oracle.approx_query(x, w, kind=oracle.BF16).tolist() == [[5.0, 58.0]]
+
+
+def test_clo_ahead_drift_sets_cosines():
+    # x_label = x + s n with x, n independent N(0, I): the cosine of the two
+    # projections is close to 1 / sqrt(1 + s^2) (checked on the oracle's fp64
+    # projections; spread about 1 / sqrt(h))
+    d = kvgen.clo_ahead(seed=14, model="llama3-8b", B=8, h=2048, Hq=8, Hkv=2)
+    qa = oracle.approx_query(d["x_prev"], d["w_q"])
+    ql = oracle.approx_query(d["x_label"], d["w_q"])
+    cos = (qa * ql).sum(1) / np.linalg.norm(qa, axis=1) / np.linalg.norm(ql, axis=1)
+    expect = 1.0 / np.sqrt(1.0 + d["drift"].astype(np.float64) ** 2)
+    assert np.all(np.abs(cos - expect) < 0.06), (cos, expect)
