@@ -285,6 +285,30 @@ def bench_clo(args, K, np, torch, dev, stream, model):
     r["lookup"] = {"us_per_call": round(lms * 1e3, 2), "kernel_us": round(lkern_us, 2),
                    "bytes": lbytes, "misses_on_first_call": misses_first, "groups": B * Hkv,
                    "achieved_gbs": round(lbytes / (lkern_us * 1e-6) / 1e9, 1)}
+    # the same lookup one layer ahead: q_approx = x_{l-1} W_Q^l (GEMV over the
+    # next layer's W_Q), then the lookup on it
+    a = kvgen.clo_ahead(seed=args.seed, model=model, B=B)
+    x_prev = to(a["x_prev"])
+    # one W_Q per layer, 12 layers in turn (more bytes than the 256 MB last-level
+    # cache holds), so each call reads its W_Q from HBM as a layer would
+    w_layers = [to(a["w_q"]) for _ in range(12)]
+    q_approx = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    labels2 = to(d["labels"])
+    layer = [0]
+
+    def ahead():
+        wq = w_layers[layer[0] % len(w_layers)]
+        layer[0] += 1
+        K.kvdec_headcache_lookup_ahead(x_prev, wq, q_approx, labels2, w, tau, hit, None, None, ml, mc,
+                                       stream=stream)
+
+    ams, akern_us, alaunches = time_steps(ahead, args.steps, args.warmup, stream, K, torch)
+    proj_us = akern_us * alaunches / args.steps - lkern_us  # per call, both kernels less the lookup's
+    pbytes = a["w_q"].nbytes + a["x_prev"].nbytes + B * Hq * D * 2
+    r["lookup_ahead"] = {"us_per_call": round(ams * 1e3, 2), "hidden": a["h"], "w_q_layers_cycled": len(w_layers),
+                         "w_q_bytes": a["w_q"].nbytes, "projection_kernel_us": round(proj_us, 2),
+                         "projection_achieved_gbs": round(pbytes / (proj_us * 1e-6) / 1e9, 1),
+                         "projection_frac_of_hbm_peak": round(pbytes / (proj_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         import oracle
         sub_rows = sum(int(d["pers_len"][0]) if hmn[g] >= 0 else int(d["buf_len"][g]) for g in range(Hkv))

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 3
+#define KVDEC_ABI_VERSION 4
 
 typedef enum {
   KVDEC_OK = 0,
@@ -175,6 +175,30 @@ kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
                                     const void* q, void* labels, const float* weights,
                                     const float* tau, uint8_t* hit, float* agg, float* cos,
                                     int32_t* miss_list, int32_t* miss_count, hipStream_t stream);
+
+/*
+ * Head-cache lookup one layer ahead (CLO page, section 3, decoding flow,
+ * Figure 9: at the start of layer l-1 the query of layer l is approximated by
+ * q_approx = x_{l-1} W_Q^l and the lookup runs on it, so the heads it misses
+ * can be fetched while layer l-1 still computes).  Computes
+ *   q_approx[b][n] = sum_i x_prev[b][i] * w_q[n][i]   (fp32 sums, one rounding)
+ * and then runs kvdec_headcache_lookup on q_approx (labels of missed groups
+ * get q_approx).  The miss list is the prefetch queue.
+ *   x_prev   [B, h] (dtype), the previous layer's hidden states
+ *   w_q      [Hq * D, h] (dtype), output index first as torch.nn.Linear stores
+ *            it (the query projection of the next layer)
+ *   q_approx [B, Hq, D] (dtype), written
+ *   the other arguments as kvdec_headcache_lookup.
+ * Requires h a multiple of 8 in [8, 8192] and x_prev, w_q 16-byte aligned,
+ * plus the kvdec_headcache_lookup rules.  W_Q is read once per group of four
+ * batch rows; the two launches (projection, then lookup) go on `stream`.
+ */
+kvdec_status kvdec_headcache_lookup_ahead(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t h, int32_t dtype, const void* x_prev,
+                                          const void* w_q, void* q_approx, void* labels,
+                                          const float* weights, const float* tau, uint8_t* hit,
+                                          float* agg, float* cos, int32_t* miss_list,
+                                          int32_t* miss_count, hipStream_t stream);
 
 /*
  * CLO threshold chain, Eqs. 7-9 (host only, fp64, rounded to fp32 once):

@@ -58,6 +58,7 @@ def _load():
         "kvdec_sparse_hybrid_attn": ([ctypes.POINTER(HybridDesc), P, P, P, P, P, P, P, P, P, P, P,
                                       sz, P], st),
         "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
+        "kvdec_headcache_lookup_ahead": ([i32] * 6 + [P] * 11 + [P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
         "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, i32, P, P, i64, P], st),
         "kvdec_kvpr_split": ([i64, i64, i64, i64, i32, ctypes.c_double, ctypes.c_double,
@@ -79,7 +80,8 @@ def _load():
 
 lib = _load()
 EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
-            "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_thresholds",
+            "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_lookup_ahead",
+            "kvdec_headcache_thresholds",
             "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
             "kvdec_kernel_timing_read", "kvdec_status_string",
             "kvdec_last_error", "kvdec_abi_version")
@@ -216,6 +218,20 @@ def kvdec_headcache_lookup(q, labels, weights, tau, hit, agg=None, cos=None, mis
     _check(lib.kvdec_headcache_lookup(B, Hq, Hkv, D, _DTYPES[q.dtype], _ptr(q), _ptr(labels),
                                       _ptr(weights), _ptr(tau), _ptr(hit), _ptr(agg), _ptr(cos),
                                       _ptr(miss_list), _ptr(miss_count), _stream(stream)))
+    return hit
+
+
+def kvdec_headcache_lookup_ahead(x_prev, w_q, q_approx, labels, weights, tau, hit, agg=None,
+                                 cos=None, miss_list=None, miss_count=None, stream=None):
+    """x_prev [B, h]; w_q [Hq*D, h] as nn.Linear stores it; q_approx [B, Hq, D]
+    (written); the rest as kvdec_headcache_lookup, run on q_approx."""
+    B, Hq, D = q_approx.shape
+    h = x_prev.shape[1]
+    Hkv = tau.numel()
+    _check(lib.kvdec_headcache_lookup_ahead(B, Hq, Hkv, D, h, _DTYPES[q_approx.dtype], _ptr(x_prev),
+                                            _ptr(w_q), _ptr(q_approx), _ptr(labels), _ptr(weights),
+                                            _ptr(tau), _ptr(hit), _ptr(agg), _ptr(cos),
+                                            _ptr(miss_list), _ptr(miss_count), _stream(stream)))
     return hit
 
 

@@ -223,6 +223,40 @@ void timing_end(hipStream_t stream) {
   if ((t.err = hipEventRecord(t.pool[t.used].second, stream)) == hipSuccess) ++t.used;
 }
 
+// Checks the kvdec_headcache_lookup arguments and fills a.
+static kvdec_status lookup_args(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                const void* q, void* labels, const float* weights,
+                                const float* tau, uint8_t* hit, float* agg, float* cos,
+                                int32_t* miss_list, int32_t* miss_count, LookupArgs* a) {
+  if (B < 0 || Hq < 1 || Hkv < 1) return fail(KVDEC_ERR_INVALID, "bad B / Hq / Hkv");
+  if (Hq % Hkv != 0) return fail(KVDEC_ERR_INVALID, "Hq %% Hkv != 0");
+  if (Hq / Hkv > 16) return fail(KVDEC_ERR_UNSUPPORTED, "query heads per KV head > 16");
+  if (D != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "D must be 128");
+  if (dtype != KVDEC_F16 && dtype != KVDEC_BF16) return fail(KVDEC_ERR_UNSUPPORTED, "bad dtype");
+  if ((int64_t)B * Hkv > INT32_MAX / 4 || (int64_t)B * Hq * D > INT32_MAX)
+    return fail(KVDEC_ERR_UNSUPPORTED, "B * Hkv too large");
+  if (B == 0) return ok();
+  if (!q || !labels || !weights || !tau || !hit)
+    return fail(KVDEC_ERR_INVALID, "q, labels, weights, tau and hit must be non-NULL");
+  if ((miss_list == nullptr) != (miss_count == nullptr))
+    return fail(KVDEC_ERR_INVALID, "miss_list and miss_count go together");
+  a->q = static_cast<const uint16_t*>(q);
+  a->labels = static_cast<uint16_t*>(labels);
+  a->w = weights;
+  a->tau = tau;
+  a->hit = hit;
+  a->agg = agg;
+  a->cos = cos;
+  a->miss_list = miss_list;
+  a->miss_count = miss_count;
+  a->B = B;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->G = Hq / Hkv;
+  a->dtype = dtype;
+  return ok();
+}
+
 // Checks the kvdec_kv_recompute arguments and fills a.
 static kvdec_status recompute_args(int32_t b, int32_t l, int32_t h, int32_t num_heads,
                                    int32_t head_dim, const void* x, int64_t x_batch_stride,
@@ -409,32 +443,39 @@ kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
                                     const void* q, void* labels, const float* weights,
                                     const float* tau, uint8_t* hit, float* agg, float* cos,
                                     int32_t* miss_list, int32_t* miss_count, hipStream_t stream) {
-  if (B < 0 || Hq < 1 || Hkv < 1) return fail(KVDEC_ERR_INVALID, "bad B / Hq / Hkv");
-  if (Hq % Hkv != 0) return fail(KVDEC_ERR_INVALID, "Hq %% Hkv != 0");
-  if (Hq / Hkv > 16) return fail(KVDEC_ERR_UNSUPPORTED, "query heads per KV head > 16");
-  if (D != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "D must be 128");
-  if (dtype != KVDEC_F16 && dtype != KVDEC_BF16) return fail(KVDEC_ERR_UNSUPPORTED, "bad dtype");
-  if ((int64_t)B * Hkv > INT32_MAX / 4) return fail(KVDEC_ERR_UNSUPPORTED, "B * Hkv too large");
-  if (B == 0) return ok();
-  if (!q || !labels || !weights || !tau || !hit)
-    return fail(KVDEC_ERR_INVALID, "q, labels, weights, tau and hit must be non-NULL");
-  if ((miss_list == nullptr) != (miss_count == nullptr))
-    return fail(KVDEC_ERR_INVALID, "miss_list and miss_count go together");
   LookupArgs a = {};
-  a.q = static_cast<const uint16_t*>(q);
-  a.labels = static_cast<uint16_t*>(labels);
-  a.w = weights;
-  a.tau = tau;
-  a.hit = hit;
-  a.agg = agg;
-  a.cos = cos;
-  a.miss_list = miss_list;
-  a.miss_count = miss_count;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = Hq / Hkv;
-  a.dtype = dtype;
+  kvdec_status st = lookup_args(B, Hq, Hkv, D, dtype, q, labels, weights, tau, hit, agg, cos,
+                                miss_list, miss_count, &a);
+  if (st != KVDEC_OK || B == 0) return st;
+  return hip_status(launch_headcache_lookup(a, stream), "head-cache lookup launch");
+}
+
+kvdec_status kvdec_headcache_lookup_ahead(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t h, int32_t dtype, const void* x_prev,
+                                          const void* w_q, void* q_approx, void* labels,
+                                          const float* weights, const float* tau, uint8_t* hit,
+                                          float* agg, float* cos, int32_t* miss_list,
+                                          int32_t* miss_count, hipStream_t stream) {
+  LookupArgs a = {};
+  kvdec_status st = lookup_args(B, Hq, Hkv, D, dtype, q_approx, labels, weights, tau, hit, agg,
+                                cos, miss_list, miss_count, &a);
+  if (st != KVDEC_OK) return st;
+  if (h < 8 || h % 8 != 0 || h > 8192)  // x of four batch rows fits the staging
+    return fail(KVDEC_ERR_UNSUPPORTED, "h must be a multiple of 8 in [8, 8192]");
+  if (B == 0) return ok();
+  if (!x_prev || !w_q) return fail(KVDEC_ERR_INVALID, "x_prev and w_q must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(x_prev) | reinterpret_cast<uintptr_t>(w_q)) & 15)
+    return fail(KVDEC_ERR_INVALID, "x_prev and w_q must be 16-byte aligned");
+  QProjArgs qa = {};
+  qa.x = static_cast<const uint16_t*>(x_prev);
+  qa.w = static_cast<const uint16_t*>(w_q);
+  qa.q = static_cast<uint16_t*>(q_approx);
+  qa.B = B;
+  qa.h = h;
+  qa.N = Hq * D;
+  qa.dtype = dtype;
+  hipError_t e = launch_qproj(qa, stream);
+  if (e != hipSuccess) return hip_status(e, "query projection launch");
   return hip_status(launch_headcache_lookup(a, stream), "head-cache lookup launch");
 }
 

@@ -145,4 +145,62 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// In-place exchanges of two registers across row pairs / wave halves:
+// permlane16: the odd rows of a trade places with the even rows of b;
+// permlane32: the upper half of a trades places with the lower half of b.
+// Afterwards a + b pairs row r (half h) of a with row r^1 (half h^1) of a in
+// the rows (halves) where a's own lanes stayed, and likewise for b.
+__device__ __forceinline__ void permlane16_swap2(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap2(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// One halving step of a transposed reduction over lane bit `bit` (0..3) inside
+// 16-lane rows: the lane keeps `lo` if its bit is clear, `hi` if set, and adds
+// the partner's copy of the same one.  Partners: bit 3 by rotating a row by 8,
+// bit 2 by mirroring each half-row (the partner differs in bit 2 and agrees in
+// bits 3 and up), bits 1 and 0 by quad permutes.
+template <int BIT>
+__device__ __forceinline__ float transpose_step(float lo, float hi, int lane) {
+  const bool up = (lane >> BIT) & 1;
+  const float keep = up ? hi : lo, send = up ? lo : hi;
+  if constexpr (BIT == 3) return keep + dpp_f32<0x128>(send);       // row_ror:8
+  else if constexpr (BIT == 2) return keep + dpp_f32<0x141>(send);  // row_half_mirror
+  else if constexpr (BIT == 1) return keep + dpp_f32<0x4E>(send);   // quad_perm [2,3,0,1]
+  else return keep + dpp_f32<0xB1>(send);                           // quad_perm [1,0,3,2]
+}
+
+// Sums each of V = 16 or 32 values over the 64 lanes of the wave at once.
+// Each level halves the number of registers: the lanes of one side keep the
+// first half of the values, the other side the second half, and each adds its
+// partner's copy; levels run over lane bits 5, 4, 3, ... .  The last levels,
+// once one register is left, are plain pair sums.  On return lane l holds the
+// full sum of value l / (64 / V).  Fixed order, so deterministic.  v is
+// clobbered.
+template <int V>
+__device__ __forceinline__ float transpose_reduce(float (&v)[V], int lane) {
+  static_assert(V == 16 || V == 32, "V must be 16 or 32");
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {  // bit 5
+    permlane32_swap2(v[i], v[V / 2 + i]);
+    v[i] += v[V / 2 + i];
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {  // bit 4
+    permlane16_swap2(v[i], v[V / 4 + i]);
+    v[i] += v[V / 4 + i];
+  }
+#pragma unroll
+  for (int i = 0; i < V / 8; ++i) v[i] = transpose_step<3>(v[i], v[V / 8 + i], lane);
+#pragma unroll
+  for (int i = 0; i < V / 16; ++i) v[i] = transpose_step<2>(v[i], v[V / 16 + i], lane);
+  float x = v[0];
+  if constexpr (V == 32) x = transpose_step<1>(v[0], v[1], lane);
+  else x += dpp_f32<0x4E>(x);  // bit 1, plain
+  x += dpp_f32<0xB1>(x);       // bit 0, plain
+  return x;
+}
+
 }  // namespace kvdec

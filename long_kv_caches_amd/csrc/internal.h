@@ -94,6 +94,16 @@ struct LookupArgs {
 };
 hipError_t launch_headcache_lookup(const LookupArgs& a, hipStream_t stream);
 
+// q = x . W_q^T for a batch of rows (W_q stored [N, h], output index first).
+struct QProjArgs {
+  const uint16_t* x;  // [B, h]
+  const uint16_t* w;  // [N, h]
+  uint16_t* q;        // [B, N]
+  int B, h, N;
+  int dtype;
+};
+hipError_t launch_qproj(const QProjArgs& a, hipStream_t stream);
+
 struct RecomputeArgs {
   const uint16_t* x;
   const uint16_t* wk;

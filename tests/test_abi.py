@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 3
+    assert _lib.lib.kvdec_abi_version() == 4
 
 
 def test_status_strings():
@@ -127,6 +127,24 @@ def test_lookup_validation():
     assert L(2, 8, 2, 128, 0, *args, None, None, FAKE, None, None) == K._lib.KVDEC_ERR_INVALID
     assert "miss_list" in K.last_error()
     assert L(0, 8, 2, 128, 0, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_lookup_ahead_validation():
+    A = _lib.lib.kvdec_headcache_lookup_ahead
+    lk = [FAKE] * 5  # q_approx, labels, weights, tau, hit
+    # the lookup rules apply first
+    assert A(2, 8, 3, 128, 4096, 0, FAKE, FAKE, *lk, None, None, None, None, None) == 1
+    # h: a multiple of 8 in [8, 8192]
+    assert A(2, 8, 2, 128, 4100, 0, FAKE, FAKE, *lk, None, None, None, None, None) == 2
+    assert A(2, 8, 2, 128, 8200, 0, FAKE, FAKE, *lk, None, None, None, None, None) == 2
+    assert A(2, 8, 2, 128, 0, 0, FAKE, FAKE, *lk, None, None, None, None, None) == 2
+    assert A(2, 8, 2, 128, 4096, 0, None, FAKE, *lk, None, None, None, None, None) == 1
+    assert "x_prev" in K.last_error()
+    misaligned = ctypes.c_void_p(FAKE.value + 2)
+    assert A(2, 8, 2, 128, 4096, 0, FAKE, misaligned, *lk, None, None, None, None, None) == 1
+    assert "aligned" in K.last_error()
+    assert A(0, 8, 2, 128, 4096, 0, None, None, None, None, None, None, None, None, None, None,
+             None, None) == 0
 
 
 def test_recompute_validation():
