@@ -110,6 +110,47 @@ def bf16_bits_to_f32(bits):
 # Decode attention workloads
 # ---------------------------------------------------------------------------
 
+E4M3_MAX = 448.0
+
+
+def e4m3_scale(x):
+    """Per-tensor scale of an e4m3 KV cache: max |x| / 448 in fp32 (1 for an
+    all-zero tensor), so the largest element maps to the largest code."""
+    amax = 0.0
+    flat = np.asarray(x).reshape(-1)
+    for lo in range(0, flat.size, BLOCK):
+        blk = flat[lo:lo + BLOCK].astype(np.float32)
+        amax = max(amax, float(np.abs(blk).max()) if blk.size else 0.0)
+    return np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+
+
+def to_e4m3(x, scale):
+    """e4m3 ("fn") codes of x / scale: the quotient in fp32, clipped to +-448,
+    then one round-to-nearest-even cast (torch's float8_e4m3fn)."""
+    import torch
+    flat = np.asarray(x).reshape(-1)
+    out = np.empty(flat.size, np.uint8)
+    inv = np.float32(scale)
+    for lo in range(0, flat.size, BLOCK):
+        blk = flat[lo:lo + BLOCK].astype(np.float32) / inv
+        t = torch.from_numpy(np.clip(blk, -E4M3_MAX, E4M3_MAX)).to(torch.float8_e4m3fn)
+        out[lo:lo + blk.size] = t.view(torch.uint8).numpy()
+    return out.reshape(np.asarray(x).shape)
+
+
+def fp8_kv(d, keys=("k", "v")):
+    """A copy of workload d whose K/V arrays (``keys``, K first) are e4m3
+    codes with per-tensor scales ``k_scale`` / ``v_scale`` (the arrays keep
+    their layout; one byte per element)."""
+    out = dict(d)
+    kname, vname = keys
+    ks, vs = e4m3_scale(d[kname]), e4m3_scale(d[vname])
+    out[kname] = to_e4m3(d[kname], ks)
+    out[vname] = to_e4m3(d[vname], vs)
+    out["k_scale"], out["v_scale"] = float(ks), float(vs)
+    return out
+
+
 def dense_small(seed=0, B=1, Hq=8, Hkv=2, S=1024, D=D_HEAD, seqlens=None):
     """Dense KV [B, S, Hkv, D].  Draw order: q, K, V (all N(0,1) -> fp16)."""
     dr = Draws(seed)

@@ -49,6 +49,14 @@ def _load():
     lib.orc_widen.restype = f64
     lib.orc_widen_array.argtypes = [P, P, ctypes.c_size_t, i32]
     lib.orc_widen_array.restype = None
+    lib.orc_widen_e4m3_array.argtypes = [P, P, ctypes.c_size_t]
+    lib.orc_widen_e4m3_array.restype = None
+    lib.orc_decode_attn_e4m3.argtypes = [i32, i32, i32, i32, f64, i32, i32, i32, i32, i32,
+                                         P, P, P, f64, f64, P, P, P, P, P, i32]
+    lib.orc_decode_attn_e4m3.restype = i32
+    lib.orc_hybrid_attn_e4m3.argtypes = [i32, i32, i32, i32, f64, i32, i32, i32, i32,
+                                         P, P, P, P, P, P, P, P, f64, f64, P, P, i32]
+    lib.orc_hybrid_attn_e4m3.restype = i32
     lib.orc_decode_attn.argtypes = [i32, i32, i32, i32, f64, i32, i32, i32, i32, i32,
                                     P, P, P, P, P, P, P, P, i32]
     lib.orc_decode_attn.restype = i32
@@ -105,16 +113,34 @@ def widen(bits, kind=F16):
     return out
 
 
+def widen_e4m3(codes):
+    """Exact values of OCP e4m3 codes (uint8) as fp64."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_widen_e4m3_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
 def decode_attn(q, k, v, *, num_kv_heads, layout, scale, kind=F16, seqlens=None,
-                cu_seqlens=None, block_table=None, page_size=16, nthreads=0):
+                cu_seqlens=None, block_table=None, page_size=16, nthreads=0, k_scale=None,
+                v_scale=None):
     """Decode attention in fp64 (KVPR page, section A3 MHA equation, one query token).
 
     q [B, Hq, D]; k, v in the dense [B, S, Hkv, D], ragged [T, Hkv, D] or
     paged [P, Hkv, page, D] layout.  Returns (out [B, Hq, D], lse [B, Hq]).
     Pinned by: single key, identical keys, q = 0, two-key logistic closed form,
     shift/permutation invariance, torch fp64 SDPA, paged = ragged = dense.
+    k and v as uint8 arrays are e4m3 codes: element = code value * k_scale
+    (v_scale for V); q and the output keep `kind`.
     """
-    q = _u16(q); k = _u16(k); v = _u16(v)
+    fp8 = np.asarray(k).dtype == np.uint8
+    q = _u16(q)
+    if fp8:
+        k = np.ascontiguousarray(k, dtype=np.uint8); v = np.ascontiguousarray(v, dtype=np.uint8)
+        if k_scale is None or v_scale is None:
+            raise ValueError("e4m3 K/V need k_scale and v_scale")
+    else:
+        k = _u16(k); v = _u16(v)
     B, Hq, D = q.shape
     S = k.shape[1] if layout == DENSE else 0
     max_pages = 0
@@ -124,10 +150,17 @@ def decode_attn(q, k, v, *, num_kv_heads, layout, scale, kind=F16, seqlens=None,
         page_size = k.shape[2]
     out = np.zeros((B, Hq, D), np.float64)
     lse = np.zeros((B, Hq), np.float64)
-    rc = _load().orc_decode_attn(B, Hq, num_kv_heads, D, float(scale), kind, layout, S,
-                                 page_size, max_pages, _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(_i32(seqlens)), _ptr(_i32(cu_seqlens)),
-                                 _ptr(block_table), _ptr(out), _ptr(lse), nthreads)
+    if fp8:
+        rc = _load().orc_decode_attn_e4m3(B, Hq, num_kv_heads, D, float(scale), kind, layout, S,
+                                          page_size, max_pages, _ptr(q), _ptr(k), _ptr(v),
+                                          float(k_scale), float(v_scale), _ptr(_i32(seqlens)),
+                                          _ptr(_i32(cu_seqlens)), _ptr(block_table), _ptr(out),
+                                          _ptr(lse), nthreads)
+    else:
+        rc = _load().orc_decode_attn(B, Hq, num_kv_heads, D, float(scale), kind, layout, S,
+                                     page_size, max_pages, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(_i32(seqlens)), _ptr(_i32(cu_seqlens)),
+                                     _ptr(block_table), _ptr(out), _ptr(lse), nthreads)
     if rc != 0:
         raise ValueError("orc_decode_attn: bad arguments")
     return out, lse
@@ -146,20 +179,38 @@ def attend_rows(q_row, k, v, rows, scale, kind=F16):
 
 
 def hybrid_attn(q, pers_k, pers_v, pers_len, buf_k, buf_v, buf_len, head_map, *, scale,
-                kind=F16, nthreads=0):
-    """CLO cache buffer + persistent cache attention in fp64 (CLO page, section 7)."""
-    q = _u16(q); pers_k = _u16(pers_k); pers_v = _u16(pers_v)
-    buf_k = _u16(buf_k); buf_v = _u16(buf_v)
+                kind=F16, nthreads=0, k_scale=None, v_scale=None):
+    """CLO cache buffer + persistent cache attention in fp64 (CLO page, section 7).
+    uint8 K/V arrays are e4m3 codes, as in decode_attn."""
+    fp8 = np.asarray(pers_k).dtype == np.uint8
+    q = _u16(q)
+    if fp8:
+        conv = lambda a: np.ascontiguousarray(a, dtype=np.uint8)
+        if k_scale is None or v_scale is None:
+            raise ValueError("e4m3 K/V need k_scale and v_scale")
+    else:
+        conv = _u16
+    pers_k = conv(pers_k); pers_v = conv(pers_v)
+    buf_k = conv(buf_k); buf_v = conv(buf_v)
     B, Hq, D = q.shape
     Hkv = buf_k.shape[1]
     P_slots, pers_cap = pers_k.shape[1], pers_k.shape[2]
     buf_cap = buf_k.shape[2]
     out = np.zeros((B, Hq, D), np.float64)
     lse = np.zeros((B, Hq), np.float64)
-    rc = _load().orc_hybrid_attn(B, Hq, Hkv, D, float(scale), kind, P_slots, pers_cap, buf_cap,
-                                 _ptr(q), _ptr(pers_k), _ptr(pers_v), _ptr(_i32(pers_len)),
-                                 _ptr(buf_k), _ptr(buf_v), _ptr(_i32(buf_len)),
-                                 _ptr(_i32(head_map)), _ptr(out), _ptr(lse), nthreads)
+    if fp8:
+        rc = _load().orc_hybrid_attn_e4m3(B, Hq, Hkv, D, float(scale), kind, P_slots, pers_cap,
+                                          buf_cap, _ptr(q), _ptr(pers_k), _ptr(pers_v),
+                                          _ptr(_i32(pers_len)), _ptr(buf_k), _ptr(buf_v),
+                                          _ptr(_i32(buf_len)), _ptr(_i32(head_map)),
+                                          float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
+                                          nthreads)
+    else:
+        rc = _load().orc_hybrid_attn(B, Hq, Hkv, D, float(scale), kind, P_slots, pers_cap,
+                                     buf_cap, _ptr(q), _ptr(pers_k), _ptr(pers_v),
+                                     _ptr(_i32(pers_len)), _ptr(buf_k), _ptr(buf_v),
+                                     _ptr(_i32(buf_len)), _ptr(_i32(head_map)), _ptr(out),
+                                     _ptr(lse), nthreads)
     if rc != 0:
         raise ValueError("orc_hybrid_attn: bad arguments")
     return out, lse

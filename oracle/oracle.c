@@ -48,6 +48,27 @@ double orc_widen(uint16_t bits, int kind) {
   return kind == 0 ? widen_f16(bits) : widen_bf16(bits);
 }
 
+/* OCP 8-bit e4m3 (the "fn" variant: no infinities): 1 sign, 4 exponent
+ * (bias 7) and 3 fraction bits; exponent 0 is subnormal (f * 2^-9); the one
+ * pattern with every exponent and fraction bit set is NaN; the largest
+ * magnitude is 448.  A KV element stored this way means code * scale, one
+ * scale per tensor (the CLO page's open question on FP8 KV caches). */
+static double widen_e4m3(uint8_t c) {
+  int sign = c >> 7;
+  int e = (c >> 3) & 0xf;
+  int f = c & 0x7;
+  double mag;
+  if (e == 0xf && f == 0x7)
+    mag = NAN;
+  else if (e == 0)
+    mag = ldexp((double)f, -9);
+  else
+    mag = ldexp((double)(8 + f), e - 10); /* (1 + f/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+double orc_widen_e4m3(uint8_t code) { return widen_e4m3(code); }
+
 /* Lookup table of the two widenings: 2 x 65536 doubles, filled once. */
 static double g_lut[2][65536];
 static pthread_once_t g_lut_once = PTHREAD_ONCE_INIT;
@@ -65,6 +86,29 @@ static const double* lut(int kind) {
 void orc_widen_array(const uint16_t* src, double* dst, size_t n, int kind) {
   const double* L = lut(kind);
   for (size_t i = 0; i < n; ++i) dst[i] = L[src[i]];
+}
+
+void orc_widen_e4m3_array(const uint8_t* src, double* dst, size_t n) {
+  for (size_t i = 0; i < n; ++i) dst[i] = widen_e4m3(src[i]);
+}
+
+/* A K or V tensor as the attention reads it: 16-bit elements of the query's
+ * kind, or e4m3 codes times the tensor's scale. */
+typedef struct {
+  const void* base;
+  int fp8;
+  double scale;
+  const double* lut;
+} kv_view;
+
+static inline double kv_elem(const kv_view* t, int64_t i) {
+  return t->fp8 ? t->scale * widen_e4m3(((const uint8_t*)t->base)[i])
+                : t->lut[((const uint16_t*)t->base)[i]];
+}
+
+static kv_view kv16(const uint16_t* base, int kind) {
+  kv_view t = {base, 0, 1.0, lut(kind)};
+  return t;
 }
 
 int orc_max_threads(void) {
@@ -92,18 +136,17 @@ static void set_threads(int nthreads) {
 
 /* Scores s_t = scale * q . K_t for every listed row. */
 static void scores(const double* L, int D, double scale, const uint16_t* q,
-                   const uint16_t* k, const int64_t* rows, int n, double* s) {
+                   const kv_view* k, const int64_t* rows, int n, double* s) {
   for (int t = 0; t < n; ++t) {
-    const uint16_t* kr = k + rows[t];
     double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += L[q[d]] * L[kr[d]];
+    for (int d = 0; d < D; ++d) acc += L[q[d]] * kv_elem(k, rows[t] + d);
     s[t] = scale * acc;
   }
 }
 
-void orc_attend_rows(int D, double scale, int kind, const uint16_t* q,
-                     const uint16_t* k, const uint16_t* v, const int64_t* rows, int n,
-                     double* o_unnorm, double* m_out, double* l_out) {
+static void attend_rows_view(int D, double scale, int kind, const uint16_t* q,
+                             const kv_view* k, const kv_view* v, const int64_t* rows, int n,
+                             double* o_unnorm, double* m_out, double* l_out) {
   const double* L = lut(kind);
   for (int d = 0; d < D; ++d) o_unnorm[d] = 0.0;
   if (n <= 0) {
@@ -120,20 +163,26 @@ void orc_attend_rows(int D, double scale, int kind, const uint16_t* q,
   for (int t = 0; t < n; ++t) {
     double p = exp(s[t] - m);
     l += p;
-    const uint16_t* vr = v + rows[t];
-    for (int d = 0; d < D; ++d) o_unnorm[d] += p * L[vr[d]];
+    for (int d = 0; d < D; ++d) o_unnorm[d] += p * kv_elem(v, rows[t] + d);
   }
   free(s);
   *m_out = m;
   *l_out = l;
 }
 
+void orc_attend_rows(int D, double scale, int kind, const uint16_t* q,
+                     const uint16_t* k, const uint16_t* v, const int64_t* rows, int n,
+                     double* o_unnorm, double* m_out, double* l_out) {
+  const kv_view kk = kv16(k, kind), vv = kv16(v, kind);
+  attend_rows_view(D, scale, kind, q, &kk, &vv, rows, n, o_unnorm, m_out, l_out);
+}
+
 /* Normalised output and natural-log lse for one query. */
-static void attend(int D, double scale, int kind, const uint16_t* q, const uint16_t* k,
-                   const uint16_t* v, const int64_t* rows, int n, double* out,
+static void attend(int D, double scale, int kind, const uint16_t* q, const kv_view* k,
+                   const kv_view* v, const int64_t* rows, int n, double* out,
                    double* lse) {
   double m, l;
-  orc_attend_rows(D, scale, kind, q, k, v, rows, n, out, &m, &l);
+  attend_rows_view(D, scale, kind, q, k, v, rows, n, out, &m, &l);
   if (n <= 0) {
     if (lse) *lse = -INFINITY;
     return;
@@ -150,11 +199,11 @@ static void attend(int D, double scale, int kind, const uint16_t* q, const uint1
 /* slot t % page.                                                             */
 /* ------------------------------------------------------------------------- */
 
-int orc_decode_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int layout,
-                    int S, int page, int max_pages,
-                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const int32_t* seqlens, const int32_t* cu_seqlens,
-                    const int32_t* block_table, double* out, double* lse, int nthreads) {
+static int decode_attn_view(int B, int Hq, int Hkv, int D, double scale, int kind, int layout,
+                            int S, int page, int max_pages, const uint16_t* q,
+                            const kv_view* k, const kv_view* v, const int32_t* seqlens,
+                            const int32_t* cu_seqlens, const int32_t* block_table, double* out,
+                            double* lse, int nthreads) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return -1;
   if (layout == 1 && !cu_seqlens) return -1;
   if (layout == 2 && (!seqlens || !block_table || page <= 0)) return -1;
@@ -194,18 +243,37 @@ int orc_decode_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int l
   return bad ? -1 : 0;
 }
 
+int orc_decode_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int layout,
+                    int S, int page, int max_pages,
+                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int32_t* seqlens, const int32_t* cu_seqlens,
+                    const int32_t* block_table, double* out, double* lse, int nthreads) {
+  const kv_view kk = kv16(k, kind), vv = kv16(v, kind);
+  return decode_attn_view(B, Hq, Hkv, D, scale, kind, layout, S, page, max_pages, q, &kk, &vv,
+                          seqlens, cu_seqlens, block_table, out, lse, nthreads);
+}
+
+int orc_decode_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind, int layout,
+                         int S, int page, int max_pages, const uint16_t* q, const uint8_t* k,
+                         const uint8_t* v, double k_scale, double v_scale,
+                         const int32_t* seqlens, const int32_t* cu_seqlens,
+                         const int32_t* block_table, double* out, double* lse, int nthreads) {
+  const kv_view kk = {k, 1, k_scale, NULL}, vv = {v, 1, v_scale, NULL};
+  return decode_attn_view(B, Hq, Hkv, D, scale, kind, layout, S, page, max_pages, q, &kk, &vv,
+                          seqlens, cu_seqlens, block_table, out, lse, nthreads);
+}
+
 /* ------------------------------------------------------------------------- */
 /* CLO hybrid attention: cache buffer + persistent cache, read in place.      */
 /* CLO page, section 7 (hybrid attention kernel) and section 2 (persistent    */
 /* cache for hard-to-reuse heads).                                            */
 /* ------------------------------------------------------------------------- */
 
-int orc_hybrid_attn(int B, int Hq, int Hkv, int D, double scale, int kind,
-                    int P_slots, int pers_cap, int buf_cap,
-                    const uint16_t* q, const uint16_t* pers_k, const uint16_t* pers_v,
-                    const int32_t* pers_len, const uint16_t* buf_k, const uint16_t* buf_v,
-                    const int32_t* buf_len, const int32_t* head_map,
-                    double* out, double* lse, int nthreads) {
+static int hybrid_attn_view(int B, int Hq, int Hkv, int D, double scale, int kind,
+                            int P_slots, int pers_cap, int buf_cap, const uint16_t* q,
+                            const kv_view* pk, const kv_view* pv, const int32_t* pers_len,
+                            const kv_view* bk, const kv_view* bv, const int32_t* buf_len,
+                            const int32_t* head_map, double* out, double* lse, int nthreads) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || !head_map) return -1;
   const int G = Hq / Hkv;
   set_threads(nthreads);
@@ -215,19 +283,19 @@ int orc_hybrid_attn(int B, int Hq, int Hkv, int D, double scale, int kind,
     const int b = (int)(pair / Hq), j = (int)(pair % Hq);
     const int g = j / G;
     const int slot = head_map[g];
-    const uint16_t *K, *V;
+    const kv_view *K, *V;
     int n;
     int64_t base;
     if (slot >= 0) {
       if (slot >= P_slots) { bad = 1; continue; }
       n = pers_len[b];
       if (n > pers_cap) { bad = 1; continue; }
-      K = pers_k; V = pers_v;
+      K = pk; V = pv;
       base = ((int64_t)b * P_slots + slot) * pers_cap;
     } else {
       n = buf_len[(int64_t)b * Hkv + g];
       if (n > buf_cap) { bad = 1; continue; }
-      K = buf_k; V = buf_v;
+      K = bk; V = bv;
       base = ((int64_t)b * Hkv + g) * buf_cap;
     }
     if (n < 0) { bad = 1; continue; }
@@ -238,6 +306,30 @@ int orc_hybrid_attn(int B, int Hq, int Hkv, int D, double scale, int kind,
     free(rows);
   }
   return bad ? -1 : 0;
+}
+
+int orc_hybrid_attn(int B, int Hq, int Hkv, int D, double scale, int kind,
+                    int P_slots, int pers_cap, int buf_cap,
+                    const uint16_t* q, const uint16_t* pers_k, const uint16_t* pers_v,
+                    const int32_t* pers_len, const uint16_t* buf_k, const uint16_t* buf_v,
+                    const int32_t* buf_len, const int32_t* head_map,
+                    double* out, double* lse, int nthreads) {
+  const kv_view pk = kv16(pers_k, kind), pv = kv16(pers_v, kind);
+  const kv_view bk = kv16(buf_k, kind), bv = kv16(buf_v, kind);
+  return hybrid_attn_view(B, Hq, Hkv, D, scale, kind, P_slots, pers_cap, buf_cap, q, &pk, &pv,
+                          pers_len, &bk, &bv, buf_len, head_map, out, lse, nthreads);
+}
+
+int orc_hybrid_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind,
+                         int P_slots, int pers_cap, int buf_cap, const uint16_t* q,
+                         const uint8_t* pers_k, const uint8_t* pers_v, const int32_t* pers_len,
+                         const uint8_t* buf_k, const uint8_t* buf_v, const int32_t* buf_len,
+                         const int32_t* head_map, double k_scale, double v_scale, double* out,
+                         double* lse, int nthreads) {
+  const kv_view pk = {pers_k, 1, k_scale, NULL}, pv = {pers_v, 1, v_scale, NULL};
+  const kv_view bk = {buf_k, 1, k_scale, NULL}, bv = {buf_v, 1, v_scale, NULL};
+  return hybrid_attn_view(B, Hq, Hkv, D, scale, kind, P_slots, pers_cap, buf_cap, q, &pk, &pv,
+                          pers_len, &bk, &bv, buf_len, head_map, out, lse, nthreads);
 }
 
 /* ------------------------------------------------------------------------- */

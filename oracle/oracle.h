@@ -29,6 +29,11 @@ double orc_widen(uint16_t bits, int kind);
 /* Widen n values (used by the pins that check the widening against numpy). */
 void orc_widen_array(const uint16_t* src, double* dst, size_t n, int kind);
 
+/* Exact value of an OCP e4m3 ("fn") code: bias 7, subnormal f * 2^-9, the
+ * all-ones exponent-and-fraction pattern is NaN, largest magnitude 448. */
+double orc_widen_e4m3(uint8_t code);
+void orc_widen_e4m3_array(const uint8_t* src, double* dst, size_t n);
+
 /*
  * Decode attention, one query token per sequence, grouped KV heads.
  * Definition: KVPR page, section A3, the MHA equation softmax(Q K^T / sqrt(d)) V,
@@ -46,6 +51,17 @@ int orc_decode_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int l
                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* seqlens, const int32_t* cu_seqlens,
                     const int32_t* block_table, double* out, double* lse, int nthreads);
+
+/*
+ * The same with K and V stored as e4m3 codes (one byte per element, same
+ * layouts): element = code value * k_scale (K) or * v_scale (V).  q and the
+ * output keep `kind`.  (CLO page, open questions: FP8 KV caches.)
+ */
+int orc_decode_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind, int layout,
+                         int S, int page, int max_pages, const uint16_t* q, const uint8_t* k,
+                         const uint8_t* v, double k_scale, double v_scale,
+                         const int32_t* seqlens, const int32_t* cu_seqlens,
+                         const int32_t* block_table, double* out, double* lse, int nthreads);
 
 /*
  * Attention of one query over an explicit list of rows (element offsets into
@@ -69,6 +85,14 @@ int orc_hybrid_attn(int B, int Hq, int Hkv, int D, double scale, int kind,
                     const int32_t* pers_len, const uint16_t* buf_k, const uint16_t* buf_v,
                     const int32_t* buf_len, const int32_t* head_map,
                     double* out, double* lse, int nthreads);
+
+/* The hybrid attention with e4m3 K and V (element = code * k_scale / v_scale). */
+int orc_hybrid_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind,
+                         int P_slots, int pers_cap, int buf_cap, const uint16_t* q,
+                         const uint8_t* pers_k, const uint8_t* pers_v, const int32_t* pers_len,
+                         const uint8_t* buf_k, const uint8_t* buf_v, const int32_t* buf_len,
+                         const int32_t* head_map, double k_scale, double v_scale, double* out,
+                         double* lse, int nthreads);
 
 /*
  * Eqs. 7-9 of the CLO page (threshold chain), in fp64:
