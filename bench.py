@@ -61,7 +61,7 @@ def measured_traffic(per_launch_algorithmic):
 
 
 WORKLOADS = ("llama3-8b-32k", "llama2-7b-paged", "clo-llama3-8b-128k", "clo-qwen2.5-14b-128k",
-             "kvpr-opt13b", "kvpr-overlap")
+             "kvpr-opt13b", "kvpr-overlap", "llama3-8b-32k-fp8")
 
 
 def prewarm(torch, dev, ms):
@@ -122,9 +122,12 @@ def common(args, workload, metric, unit, value, ms, dtype, data, config, higher=
             "config": dict({"workload": workload}, **config), "prewarm_ms": args.prewarm_ms}
 
 
-def bench_llama3(args, K, np, torch, dev, stream):
+def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
     import kvgen
     d = kvgen.ragged_llama(seed=args.seed)
+    if fp8:  # e4m3 K/V codes with per-tensor scales
+        d = kvgen.fp8_kv(d)
+    kv_bytes = 1 if fp8 else 2
     B, Hq, Hkv, D = d["B"], d["Hq"], d["Hkv"], d["D"]
     lens = np.diff(d["cu_seqlens"]).astype(np.int64)
     T = int(lens.sum())
@@ -132,14 +135,15 @@ def bench_llama3(args, K, np, torch, dev, stream):
     k = torch.from_numpy(d["k"]).to(dev)
     v = torch.from_numpy(d["v"]).to(dev)
     cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+    fmt = dict(kv_format=K.KVDEC_KV_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if fp8 else {}
     desc = K.attn_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
                        layout=K.KVDEC_RAGGED, max_seqlen=int(lens.max()), softmax_scale=d["scale"],
-                       split_tokens=args.split_tokens, kv_rows=T)
+                       split_tokens=args.split_tokens, kv_rows=T, **fmt)
     ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc), device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     # algorithmic bytes of one step: attended K and V rows, q, out, lse, cu_seqlens
-    step_bytes = T * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2 + B * Hq * 4 + (B + 1) * 4
+    step_bytes = T * Hkv * D * kv_bytes * 2 + B * Hq * D * 2 * 2 + B * Hq * 4 + (B + 1) * 4
 
     def step():
         K.kvdec_decode_attn(desc, q, k, v, None, cu, None, out, lse, ws, stream=stream)
@@ -148,27 +152,45 @@ def bench_llama3(args, K, np, torch, dev, stream):
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    r = common(args, "llama3-8b-32k-ragged-decode-attention",
-               "decode-attn achieved HBM TB/s (% of peak) + KV tokens·heads/s, Llama3-8B 32K",
-               "TB/s", round(gbs / 1e3, 4), ms, "f16",
-               "synthetic (seeded; shapes and distributions of the Llama3-8B 32K decode workload)",
-               {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-                "context_lengths": "uniform [16384, 32768]", "total_tokens": T, "layout": "ragged",
-                "split_tokens": args.split_tokens or "auto"})
+    config = {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+              "context_lengths": "uniform [16384, 32768]", "total_tokens": T, "layout": "ragged",
+              "split_tokens": args.split_tokens or "auto"}
+    if fp8:
+        config.update(kv_format="e4m3 (per-tensor scales)", k_scale=d["k_scale"], v_scale=d["v_scale"])
+        r = common(args, "llama3-8b-32k-ragged-decode-attention-e4m3-kv",
+                   "decode-attn over e4m3 K/V: achieved HBM TB/s (% of peak) + KV tokens·heads/s, Llama3-8B 32K",
+                   "TB/s", round(gbs / 1e3, 4), ms, "f16 q/out, e4m3 K/V, fp32 accumulate",
+                   "synthetic (seeded; the Llama3-8B 32K decode workload, K/V cast to e4m3 with amax scales)",
+                   config)
+    else:
+        r = common(args, "llama3-8b-32k-ragged-decode-attention",
+                   "decode-attn achieved HBM TB/s (% of peak) + KV tokens·heads/s, Llama3-8B 32K",
+                   "TB/s", round(gbs / 1e3, 4), ms, "f16",
+                   "synthetic (seeded; shapes and distributions of the Llama3-8B 32K decode workload)",
+                   config)
     r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
     r["kv_token_heads_per_s"] = round(T * Hkv / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-                                 step_bytes, kern_us, measured_traffic(step_bytes))
+                                 step_bytes, kern_us, None if fp8 else measured_traffic(step_bytes))
     r["roofline"]["launches_timed"] = launches
     if not args.no_cpu_baseline:
         import oracle
-        cs = oracle_seconds(lambda: oracle.decode_attn(d["q"], d["k"], d["v"], num_kv_heads=Hkv,
-                                                       layout=oracle.RAGGED, scale=d["scale"],
-                                                       cu_seqlens=d["cu_seqlens"]))
-        r["cpu_baseline"] = {"value": round(step_bytes / cs / 1e12, 6), "unit": "TB/s",
-                             "cores": oracle.max_threads(), "kind": "oracle",
-                             "sample": f"the full workload (all {B} sequences, {T} tokens), median of 3 runs, "
-                                       f"{cs:.2f} s each"}
+        if fp8:  # a bounded sample: the first 4 sequences
+            n = 4
+            cu4 = d["cu_seqlens"][:n + 1]
+            sub_bytes = int(cu4[-1]) * Hkv * D * kv_bytes * 2 + n * Hq * D * 4
+            cs = oracle_seconds(lambda: oracle.decode_attn(
+                d["q"][:n], d["k"][:cu4[-1]], d["v"][:cu4[-1]], num_kv_heads=Hkv, layout=oracle.RAGGED,
+                scale=d["scale"], cu_seqlens=cu4, k_scale=d["k_scale"], v_scale=d["v_scale"]))
+            sample = f"the first {n} of {B} sequences ({int(cu4[-1])} tokens), median of 3 runs, {cs:.2f} s each"
+        else:
+            sub_bytes = step_bytes
+            cs = oracle_seconds(lambda: oracle.decode_attn(d["q"], d["k"], d["v"], num_kv_heads=Hkv,
+                                                           layout=oracle.RAGGED, scale=d["scale"],
+                                                           cu_seqlens=d["cu_seqlens"]))
+            sample = f"the full workload (all {B} sequences, {T} tokens), median of 3 runs, {cs:.2f} s each"
+        r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
+                             "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
     return r
 
 
@@ -513,6 +535,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.workload == "llama3-8b-32k":
         r = bench_llama3(args, K, np, torch, dev, stream)
+    elif args.workload == "llama3-8b-32k-fp8":
+        r = bench_llama3(args, K, np, torch, dev, stream, fp8=True)
     elif args.workload == "llama2-7b-paged":
         r = bench_paged(args, K, np, torch, dev, stream)
     elif args.workload.startswith("clo-"):

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 4
+#define KVDEC_ABI_VERSION 5
 
 typedef enum {
   KVDEC_OK = 0,
@@ -46,6 +46,12 @@ typedef enum {
 
 typedef enum { KVDEC_F16 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 typedef enum { KVDEC_DENSE = 0, KVDEC_RAGGED = 1, KVDEC_PAGED = 2 } kvdec_layout;
+/* Storage of K and V: the query's dtype, or e4m3 codes (OCP 8-bit float,
+ * "fn" variant: bias 7, no infinities, largest magnitude 448), one byte per
+ * element in the same layouts, each tensor with one scale (element = code
+ * value * scale).  The CLO page raises FP8 KV caches as its natural next step:
+ * they halve the bytes each token and head moves. */
+typedef enum { KVDEC_KV_SAME = 0, KVDEC_KV_E4M3 = 1 } kvdec_kv_format;
 
 /*
  * Decode attention descriptor.
@@ -84,6 +90,12 @@ typedef enum { KVDEC_DENSE = 0, KVDEC_RAGGED = 1, KVDEC_PAGED = 2 } kvdec_layout
  *                  the pool; DENSE: ignored.  The kernel clamps cu_seqlens into
  *                  [0, T] and page ids into [0, P), so malformed metadata reads
  *                  wrong rows instead of faulting.
+ *   kv_format      kvdec_kv_format of K and V (0: the dtype above)
+ *   k_scale, v_scale  KVDEC_KV_E4M3 only: finite and > 0; K = k_scale * code,
+ *                  V = v_scale * code.  k_scale enters the scores
+ *                  (softmax_scale * k_scale * q . code), v_scale the output
+ *                  (applied with the final normalisation).  Codes that are NaN
+ *                  give NaN outputs.
  */
 typedef struct {
   int32_t batch, num_q_heads, num_kv_heads, head_dim;
@@ -94,6 +106,8 @@ typedef struct {
   int32_t page_size, max_pages_per_seq;
   int32_t split_tokens;
   int64_t kv_rows;
+  int32_t kv_format;
+  float k_scale, v_scale;
 } kvdec_attn_desc;
 
 /* Workspace bytes kvdec_decode_attn needs for this descriptor on the current
@@ -129,8 +143,10 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* desc, const void* q, const
  * hybrid attention kernel reads both buffers in place, with no gather into one
  * buffer; section 2: hard-to-reuse heads keep their full KV resident).
  *
- * base: batch, heads, head_dim, softmax_scale, dtype, split_tokens as for
- * kvdec_attn_desc (layout, max_seqlen, page fields are ignored).
+ * base: batch, heads, head_dim, softmax_scale, dtype, split_tokens, kv_format
+ * and the scales as for kvdec_attn_desc (layout, max_seqlen, page fields are
+ * ignored); with KVDEC_KV_E4M3 both the persistent and the buffer K/V are
+ * codes under the same two scales.
  *   pers_k, pers_v [B, num_pers_slots, pers_cap, 128]; pers_len [B] int32
  *   buf_k,  buf_v  [B, Hkv, buf_cap, 128];             buf_len [B * Hkv] int32
  *   head_map [Hkv] int32: slot >= 0 reads persistent slot `slot` (rows

@@ -151,6 +151,18 @@ def fp8_kv(d, keys=("k", "v")):
     return out
 
 
+def fp8_hybrid(d):
+    """A copy of a ``clo_hybrid`` workload with e4m3 persistent and buffer K/V:
+    one K scale and one V scale shared by both sources (amax over the two)."""
+    out = dict(d)
+    ks = max(e4m3_scale(d["pers_k"]), e4m3_scale(d["buf_k"]))
+    vs = max(e4m3_scale(d["pers_v"]), e4m3_scale(d["buf_v"]))
+    for name, sc in (("pers_k", ks), ("buf_k", ks), ("pers_v", vs), ("buf_v", vs)):
+        out[name] = to_e4m3(d[name], sc)
+    out["k_scale"], out["v_scale"] = float(ks), float(vs)
+    return out
+
+
 def dense_small(seed=0, B=1, Hq=8, Hkv=2, S=1024, D=D_HEAD, seqlens=None):
     """Dense KV [B, S, Hkv, D].  Draw order: q, K, V (all N(0,1) -> fp16)."""
     dr = Draws(seed)

@@ -4,7 +4,8 @@ The compute lives in the HIP library ``libkvdec.so`` (C ABI in include/kvdec.h);
 this package is its thin ctypes binding (``_lib``) and build script (``build``).
 """
 from ._lib import (  # noqa: F401
-    KVDEC_BF16, KVDEC_DENSE, KVDEC_F16, KVDEC_PAGED, KVDEC_RAGGED, KVDEC_W_IN_OUT, KVDEC_W_OUT_IN,
+    KVDEC_BF16, KVDEC_DENSE, KVDEC_F16, KVDEC_KV_E4M3, KVDEC_KV_SAME, KVDEC_PAGED, KVDEC_RAGGED,
+    KVDEC_W_IN_OUT, KVDEC_W_OUT_IN,
     AttnDesc, HybridDesc,
     KvdecError, alloc_workspace, attn_desc, hybrid_desc, kvdec_decode_attn,
     kvdec_decode_attn_workspace, kvdec_headcache_lookup, kvdec_headcache_lookup_ahead,

@@ -19,6 +19,7 @@ KVDEC_OK, KVDEC_ERR_INVALID, KVDEC_ERR_UNSUPPORTED, KVDEC_ERR_WORKSPACE, KVDEC_E
 KVDEC_F16, KVDEC_BF16 = 0, 1
 KVDEC_DENSE, KVDEC_RAGGED, KVDEC_PAGED = 0, 1, 2
 KVDEC_W_IN_OUT, KVDEC_W_OUT_IN = 0, 1
+KVDEC_KV_SAME, KVDEC_KV_E4M3 = 0, 1
 
 _DTYPES = {torch.float16: KVDEC_F16, torch.bfloat16: KVDEC_BF16}
 
@@ -37,6 +38,7 @@ class AttnDesc(ctypes.Structure):
         ("layout", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("split_tokens", ctypes.c_int32), ("kv_rows", ctypes.c_int64),
+        ("kv_format", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
 
 
@@ -116,12 +118,16 @@ def _stream(stream):
 
 
 def attn_desc(*, batch, num_q_heads, num_kv_heads, dtype, layout, max_seqlen, head_dim=128,
-              softmax_scale=None, page_size=0, max_pages_per_seq=0, split_tokens=0, kv_rows=0):
+              softmax_scale=None, page_size=0, max_pages_per_seq=0, split_tokens=0, kv_rows=0,
+              kv_format=KVDEC_KV_SAME, k_scale=1.0, v_scale=1.0):
+    """dtype: of q and out (and of K/V unless kv_format is KVDEC_KV_E4M3, where
+    K and V are uint8 e4m3 codes times k_scale / v_scale)."""
     if softmax_scale is None:
         softmax_scale = head_dim ** -0.5
     return AttnDesc(batch, num_q_heads, num_kv_heads, head_dim, softmax_scale,
                     _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype), layout,
-                    max_seqlen, page_size, max_pages_per_seq, split_tokens, kv_rows)
+                    max_seqlen, page_size, max_pages_per_seq, split_tokens, kv_rows,
+                    int(kv_format), float(k_scale), float(v_scale))
 
 
 def hybrid_desc(*, num_pers_slots, pers_cap, buf_cap, **kw):

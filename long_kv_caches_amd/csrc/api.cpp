@@ -58,8 +58,8 @@ static constexpr int kChunkQuantum = kTile * kWaves;  // 64
 
 static int round_up(int64_t x, int q) { return (int)(((x + q - 1) / q) * q); }
 
-static Plan plan_attn(int dtype, int G, int src, int64_t pairs, int64_t n_units, int64_t est_tokens,
-                      int max_len, int split_tokens) {
+static Plan plan_attn(int dtype, int kv8, int G, int src, int64_t pairs, int64_t n_units,
+                      int64_t est_tokens, int max_len, int split_tokens) {
   Plan p = {};
   p.max_len = std::max(max_len, 0);
   const int64_t est_tiles = pairs * ((std::max(max_len, 1) + kTile - 1) / kTile);
@@ -69,7 +69,7 @@ static Plan plan_attn(int dtype, int G, int src, int64_t pairs, int64_t n_units,
     // at least one wave per line head: with fewer, no column exists and
     // some heads would never be run
     const int64_t LH = pairs / std::max<int64_t>(n_units, 1);
-    p.n_blocks = (int)std::max<int64_t>(balanced_blocks(dtype, G, src, est_tiles),
+    p.n_blocks = (int)std::max<int64_t>(balanced_blocks(dtype, kv8, G, src, est_tiles),
                                         (LH + kWaves - 1) / kWaves);
     p.n_cu = device_cu_count();
     // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
@@ -106,6 +106,11 @@ static kvdec_status check_common(const kvdec_attn_desc* d, bool check_layout) {
   if (!isfinite(d->softmax_scale)) return fail(KVDEC_ERR_INVALID, "softmax_scale not finite");
   if (d->split_tokens < 0 || d->split_tokens % kChunkQuantum != 0)
     return fail(KVDEC_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 64");
+  if (d->kv_format != KVDEC_KV_SAME && d->kv_format != KVDEC_KV_E4M3)
+    return fail(KVDEC_ERR_UNSUPPORTED, "unknown kv_format %d", d->kv_format);
+  if (d->kv_format == KVDEC_KV_E4M3 &&
+      !(isfinite(d->k_scale) && isfinite(d->v_scale) && d->k_scale > 0.f && d->v_scale > 0.f))
+    return fail(KVDEC_ERR_INVALID, "e4m3 K/V need finite k_scale, v_scale > 0");
   if (check_layout) {
     if (d->layout != KVDEC_DENSE && d->layout != KVDEC_RAGGED && d->layout != KVDEC_PAGED)
       return fail(KVDEC_ERR_INVALID, "unknown layout %d", d->layout);
@@ -128,8 +133,8 @@ static kvdec_status check_common(const kvdec_attn_desc* d, bool check_layout) {
 static Plan plan_decode(const kvdec_attn_desc* d) {
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
   const int src = d->layout == KVDEC_DENSE ? SRC_DENSE : d->layout == KVDEC_RAGGED ? SRC_RAGGED : SRC_PAGED;
-  return plan_attn(d->dtype, d->num_q_heads / d->num_kv_heads, src, pairs, d->batch,
-                   pairs * (int64_t)d->max_seqlen, d->max_seqlen, d->split_tokens);
+  return plan_attn(d->dtype, d->kv_format == KVDEC_KV_E4M3, d->num_q_heads / d->num_kv_heads, src,
+                   pairs, d->batch, pairs * (int64_t)d->max_seqlen, d->max_seqlen, d->split_tokens);
 }
 
 static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
@@ -137,8 +142,9 @@ static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
   const int64_t est = (int64_t)d->batch *
                       ((int64_t)h->num_pers_slots * h->pers_cap + (int64_t)d->num_kv_heads * h->buf_cap);
-  return plan_attn(d->dtype, d->num_q_heads / d->num_kv_heads, SRC_HYBRID, pairs, pairs, est,
-                   std::max(h->pers_cap, h->buf_cap), d->split_tokens);
+  return plan_attn(d->dtype, d->kv_format == KVDEC_KV_E4M3, d->num_q_heads / d->num_kv_heads,
+                   SRC_HYBRID, pairs, pairs, est, std::max(h->pers_cap, h->buf_cap),
+                   d->split_tokens);
 }
 
 // Partial slots and prefix entries the plan needs in the workspace.
@@ -174,7 +180,11 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->n_blocks = p.n_blocks;
   a->n_units = p.n_units;
   a->n_cu = p.n_cu;
-  a->scale_log2 = (float)((double)d->softmax_scale * 1.4426950408889634074);
+  a->kv8 = d->kv_format == KVDEC_KV_E4M3;
+  // e4m3 K: scale * q . (k_scale * code) = (scale * k_scale) * q . code
+  a->scale_log2 = (float)((double)d->softmax_scale * (a->kv8 ? (double)d->k_scale : 1.0) *
+                          1.4426950408889634074);
+  a->out_scale = a->kv8 ? d->v_scale : 1.f;
   a->dtype = d->dtype;
 }
 
@@ -365,8 +375,8 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* d, const void* q, const vo
   AttnArgs a = {};
   fill_common(d, p, &a);
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
+  a.k = k;
+  a.v = v;
   a.seqlens = seqlens;
   a.cu_seqlens = cu_seqlens;
   a.block_table = block_table;
@@ -424,10 +434,10 @@ kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* h, const void* q,
   fill_common(d, p, &a);
   a.src = SRC_HYBRID;
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(pers_k);
-  a.v = static_cast<const uint16_t*>(pers_v);
-  a.k2 = static_cast<const uint16_t*>(buf_k);
-  a.v2 = static_cast<const uint16_t*>(buf_v);
+  a.k = pers_k;
+  a.v = pers_v;
+  a.k2 = buf_k;
+  a.v2 = buf_v;
   a.pers_len = pers_len;
   a.buf_len = buf_len;
   a.head_map = head_map;

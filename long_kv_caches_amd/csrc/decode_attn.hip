@@ -41,7 +41,15 @@
 // In both, a second small kernel merges the partials of each pair in a fixed
 // order (so results do not depend on timing); the kernel boundary orders the
 // partial writes before the merge reads, with no grid-wide fence or atomic.
+//
+// K and V may also be e4m3 codes, one byte per element, each tensor with one
+// scale (the CLO page's open question on FP8 KV caches).  The lane layout is
+// the same, a lane's piece of a row is then 8 bytes, and a tile is half the
+// bytes.  K codes are widened exactly to the query's 16-bit type for the
+// v_dot2 scores (k_scale is folded into the score scale), V codes to fp32
+// for the P.V FMAs (v_scale is applied with the final normalisation).
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -51,13 +59,31 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Attention kinds: bit 0 is the 16-bit type of q and out (KIND_F16 or
+// KIND_BF16); bit 1 is set when K and V are e4m3 codes.
+constexpr int KIND_KV8 = 2;
+template <int KIND>
+constexpr int kQKind = KIND & 1;
+template <int KIND>
+constexpr bool kKv8 = (KIND & KIND_KV8) != 0;
+template <int KIND>
+constexpr int kKvBytes = kKv8<KIND> ? 1 : 2;  // bytes per K/V element
+// A lane's piece of one K or V row: 8 elements.
+template <int KIND>
+using KvPiece = std::conditional_t<kKv8<KIND>, u32x2, u32x4>;
+
+// Address of K/V element `elems` of a tensor starting at base.
+template <int KIND>
+__device__ __forceinline__ const char* kv_at(const void* base, int64_t elems) {
+  return static_cast<const char*>(base) + elems * kKvBytes<KIND>;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct SeqView {
   int len;
-  const uint16_t* kb;  // strided sources: row of token t at kb + t * stride
-  const uint16_t* vb;
-  int64_t stride;
+  const char* kb;  // row of token t of the pair starts at kb (+ t rows)
+  const char* vb;
 };
 
 // Length of pair (b, g), per thread (no uniformity assumed).
@@ -81,37 +107,35 @@ __device__ __forceinline__ int pair_len(const AttnArgs& a, int b, int g) {
 }
 
 // Rows of pair (b, g), for a wave that handles this pair.
-template <int SRC>
+template <int KIND, int SRC>
 __device__ __forceinline__ SeqView locate(const AttnArgs& a, int b, int g) {
   SeqView s;
-  s.stride = (int64_t)a.Hkv * kHeadDim;
   // Values loaded from memory are the same for the whole wave; say so, so
   // that buffer descriptors built from them stay in scalar registers.
   s.len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
   if constexpr (SRC == SRC_DENSE) {
     const int64_t base = ((int64_t)b * a.S * a.Hkv + g) * kHeadDim;
-    s.kb = a.k + base;
-    s.vb = a.v + base;
+    s.kb = kv_at<KIND>(a.k, base);
+    s.vb = kv_at<KIND>(a.v, base);
   } else if constexpr (SRC == SRC_RAGGED) {
     const int start = __builtin_amdgcn_readfirstlane(min(max(a.cu_seqlens[b], 0), a.S));
     const int64_t base = ((int64_t)start * a.Hkv + g) * kHeadDim;
-    s.kb = a.k + base;
-    s.vb = a.v + base;
+    s.kb = kv_at<KIND>(a.k, base);
+    s.vb = kv_at<KIND>(a.v, base);
   } else if constexpr (SRC == SRC_PAGED) {
-    s.kb = a.k;
-    s.vb = a.v;
+    s.kb = kv_at<KIND>(a.k, 0);
+    s.vb = kv_at<KIND>(a.v, 0);
   } else {  // SRC_HYBRID
     const int slot = __builtin_amdgcn_readfirstlane(a.head_map[g]);
-    s.stride = kHeadDim;
     if (slot >= 0) {
       const int64_t base = ((int64_t)b * a.P_slots + min(slot, max(a.P_slots - 1, 0))) *
                            a.pers_cap * kHeadDim;
-      s.kb = a.k + base;
-      s.vb = a.v + base;
+      s.kb = kv_at<KIND>(a.k, base);
+      s.vb = kv_at<KIND>(a.v, base);
     } else {
       const int64_t base = ((int64_t)b * a.Hkv + g) * a.buf_cap * kHeadDim;
-      s.kb = a.k2 + base;
-      s.vb = a.v2 + base;
+      s.kb = kv_at<KIND>(a.k2, base);
+      s.vb = kv_at<KIND>(a.v2, base);
     }
   }
   return s;
@@ -150,16 +174,18 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int64_t head0, int n, 
 }
 
 // Byte offsets, within a tile, of the four rows of this lane: rows 4*lg + i,
-// piece n.
+// piece n (8 elements).
+template <int KIND>
 __device__ __forceinline__ void tile_row_offsets(uint32_t row_bytes, int lane, uint32_t (&row_off)[4]) {
   const int n = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) row_off[i] = (4 * lg + i) * row_bytes + 16 * n;
+  for (int i = 0; i < 4; ++i) row_off[i] = (4 * lg + i) * row_bytes + 8 * kKvBytes<KIND> * n;
 }
 
-template <int SRC>
+// Bytes from one token row of a pair to the next.
+template <int KIND, int SRC>
 __device__ __forceinline__ uint32_t tile_row_bytes(const AttnArgs& a) {
-  return SRC == SRC_PAGED ? kHeadDim * 2 : SRC == SRC_HYBRID ? kHeadDim * 2 : (uint32_t)a.Hkv * kHeadDim * 2;
+  return (SRC == SRC_PAGED || SRC == SRC_HYBRID ? 1u : (uint32_t)a.Hkv) * kHeadDim * kKvBytes<KIND>;
 }
 
 // Loads K and V of the tile whose first row is t0 of pair (b, g) into kf, vf.
@@ -167,45 +193,100 @@ __device__ __forceinline__ uint32_t tile_row_bytes(const AttnArgs& a) {
 // (scalar registers) and whose size covers only rows below len, so rows past
 // the end of the sequence, and a tile with active == false, read as zeros with
 // no memory traffic.
-template <int SRC>
-__device__ __forceinline__ void load_kv_tile(const AttnArgs& a, int b, int g, const uint16_t* kb,
-                                             const uint16_t* vb, int len, int t0, bool active,
-                                             const uint32_t (&row_off)[4], u32x4 (&kf)[4],
-                                             u32x4 (&vf)[4]) {
-  const uint32_t row_bytes = tile_row_bytes<SRC>(a);
+template <int KIND, int SRC>
+__device__ __forceinline__ void load_kv_tile(const AttnArgs& a, int b, int g, const char* kb,
+                                             const char* vb, int len, int t0, bool active,
+                                             const uint32_t (&row_off)[4], KvPiece<KIND> (&kf)[4],
+                                             KvPiece<KIND> (&vf)[4]) {
+  const uint32_t row_bytes = tile_row_bytes<KIND, SRC>(a);
   const int rows = active ? min(len - t0, kTile) : 0;
-  int64_t row0;  // element offset of the tile's first row
+  int64_t row0;  // byte offset of the tile's first row
   if constexpr (SRC == SRC_PAGED) {
     int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
     pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
-    row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;  // never straddles pages
+    // never straddles pages
+    row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim * kKvBytes<KIND>;
   } else {
-    row0 = (int64_t)t0 * (row_bytes / 2);
+    row0 = (int64_t)t0 * row_bytes;
   }
   const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
+  if constexpr (kKv8<KIND>) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, row_off[i]);
+    for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b64_nt(rk, row_off[i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, row_off[i]);
+    for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b64_nt(rv, row_off[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, row_off[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, row_off[i]);
+  }
+}
+
+// The 8 K elements of a lane's piece as four packed 16-bit pairs of the
+// query's type (e4m3 widens exactly to fp16 and to bf16).
+template <int KIND>
+__device__ __forceinline__ void k_pairs(const KvPiece<KIND>& k, uint32_t (&w)[4]) {
+  if constexpr (kKv8<KIND>) {
+    if constexpr (kQKind<KIND> == KIND_F16) {
+      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.x, 1.0f, false));
+      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.x, 1.0f, true));
+      w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.y, 1.0f, false));
+      w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.y, 1.0f, true));
+    } else {
+      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.x, 1.0f, false));
+      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.x, 1.0f, true));
+      w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.y, 1.0f, false));
+      w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.y, 1.0f, true));
+    }
+  } else {
+    w[0] = k.x;
+    w[1] = k.y;
+    w[2] = k.z;
+    w[3] = k.w;
+  }
+}
+
+// The 8 V elements of a lane's piece in fp32 (exact for every storage type).
+template <int KIND>
+__device__ __forceinline__ void v_floats(const KvPiece<KIND>& v, float (&vv)[8]) {
+  if constexpr (kKv8<KIND>) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false), a1 = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, true);
+    const f2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, false), a3 = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
+    vv[0] = a0.x; vv[1] = a0.y; vv[2] = a1.x; vv[3] = a1.y;
+    vv[4] = a2.x; vv[5] = a2.y; vv[6] = a3.x; vv[7] = a3.y;
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[2 * e] = lo_f32<kQKind<KIND>>(w[e]);
+      vv[2 * e + 1] = hi_f32<kQKind<KIND>>(w[e]);
+    }
+  }
 }
 
 // Online-softmax update of st with the tile whose first row is t0 (rows at or
 // past len are masked out; the tile holds at least one row below len).
 template <int KIND, int G>
 __device__ __forceinline__ void process_tile(const AttnArgs& a, const u32x4 (&qf)[G],
-                                             const u32x4 (&kf)[4], const u32x4 (&vf)[4], int t0,
-                                             int len, int lg, WaveState<G>& st) {
+                                             const KvPiece<KIND> (&kf)[4],
+                                             const KvPiece<KIND> (&vf)[4], int t0, int len, int lg,
+                                             WaveState<G>& st) {
+  constexpr int QK = kQKind<KIND>;
   float sc[4][G];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bool valid = t0 + 4 * lg + i < len;
+    uint32_t kw[4];
+    k_pairs<KIND>(kf[i], kw);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part = dot2<KIND>(kf[i][e], qf[j][e], part);
+      for (int e = 0; e < 4; ++e) part = dot2<QK>(kw[e], qf[j][e], part);
       const float full = row_sum16(part);
       sc[i][j] = valid ? full * a.scale_log2 : -INFINITY;
     }
@@ -237,11 +318,7 @@ __device__ __forceinline__ void process_tile(const AttnArgs& a, const u32x4 (&qf
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float vv[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vv[2 * e] = lo_f32<KIND>(vf[i][e]);
-      vv[2 * e + 1] = hi_f32<KIND>(vf[i][e]);
-    }
+    v_floats<KIND>(vf[i], vv);
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -257,19 +334,20 @@ __device__ __forceinline__ void run_tiles(const AttnArgs& a, int b, int g, const
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   uint32_t row_off[4];
-  tile_row_offsets(tile_row_bytes<SRC>(a), lane, row_off);
-  auto load = [&](int k, u32x4 (&kf)[4], u32x4 (&vf)[4]) {
-    load_kv_tile<SRC>(a, b, g, sq.kb, sq.vb, sq.len, (tile_first + k * tile_step) * kTile, k < count,
-                      row_off, kf, vf);
+  tile_row_offsets<KIND>(tile_row_bytes<KIND, SRC>(a), lane, row_off);
+  using KP = KvPiece<KIND>;
+  auto load = [&](int k, KP (&kf)[4], KP (&vf)[4]) {
+    load_kv_tile<KIND, SRC>(a, b, g, sq.kb, sq.vb, sq.len, (tile_first + k * tile_step) * kTile,
+                            k < count, row_off, kf, vf);
   };
-  auto process = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4], int k) {
+  auto process = [&](const KP (&kf)[4], const KP (&vf)[4], int k) {
     process_tile<KIND, G>(a, qf, kf, vf, (tile_first + k * tile_step) * kTile, sq.len, lg, st);
   };
 
   // Ping-pong: loads are unconditional (a tile past the run reads nothing), so
   // no branch or register copy forces an early wait on the prefetch.
   if (count <= 0) return;
-  u32x4 ka[4], va[4], kb[4], vb[4];
+  KP ka[4], va[4], kb[4], vb[4];
   load(0, ka, va);
   for (int k = 0;; k += 2) {
     load(k + 1, kb, vb);
@@ -288,12 +366,12 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int64_t head0, c
   if (lane < 16) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float inv = 1.f / st.l[j];
+      const float inv = kKv8<KIND> ? a.out_scale / st.l[j] : 1.f / st.l[j];
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)to_bits<KIND>(st.o[j][2 * e] * inv) |
-               ((uint32_t)to_bits<KIND>(st.o[j][2 * e + 1] * inv) << 16);
+        w[e] = (uint32_t)to_bits<kQKind<KIND>>(st.o[j][2 * e] * inv) |
+               ((uint32_t)to_bits<kQKind<KIND>>(st.o[j][2 * e + 1] * inv) << 16);
       store_b128(a.out + (head0 + j) * kHeadDim + 8 * lane, u32x4{w[0], w[1], w[2], w[3]});
     }
   }
@@ -382,9 +460,10 @@ __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot
       o3 += v.w;
       L += s_l[rr];
     }
-    const float inv = 1.f / L;
-    const uint32_t w0 = (uint32_t)to_bits<KIND>(o0 * inv) | ((uint32_t)to_bits<KIND>(o1 * inv) << 16);
-    const uint32_t w1 = (uint32_t)to_bits<KIND>(o2 * inv) | ((uint32_t)to_bits<KIND>(o3 * inv) << 16);
+    constexpr int QK = kQKind<KIND>;
+    const float inv = kKv8<KIND> ? a.out_scale / L : 1.f / L;
+    const uint32_t w0 = (uint32_t)to_bits<QK>(o0 * inv) | ((uint32_t)to_bits<QK>(o1 * inv) << 16);
+    const uint32_t w1 = (uint32_t)to_bits<QK>(o2 * inv) | ((uint32_t)to_bits<QK>(o3 * inv) << 16);
     *reinterpret_cast<uint2*>(a.out + (head0 + j) * kHeadDim + 4 * c) = make_uint2(w0, w1);
     if (c == 0 && a.lse) a.lse[head0 + j] = (M + __builtin_log2f(L)) * kLn2;
   }
@@ -408,7 +487,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
   const int c = bid % a.n_chunks;
   const int b = bid / a.n_chunks;
 
-  const SeqView sq = locate<SRC>(a, b, g);
+  const SeqView sq = locate<KIND, SRC>(a, b, g);
   const int len = sq.len;
   const int n_c = (len + a.chunk - 1) / a.chunk;
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
@@ -460,7 +539,8 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
       den = __builtin_fmaf(wt, sm_l[w][j], den);
     }
     if (n_c == 1) {
-      a.out[(head0 + j) * kHeadDim + d] = to_bits<KIND>(num / den);
+      a.out[(head0 + j) * kHeadDim + d] =
+          to_bits<kQKind<KIND>>(kKv8<KIND> ? num * (a.out_scale / den) : num / den);
       if (d == 0 && a.lse) a.lse[head0 + j] = (M + __builtin_log2f(den)) * kLn2;
     } else {
       a.ws_o[(item * G + j) * kHeadDim + d] = num;
@@ -609,12 +689,12 @@ struct Seg {
   int b, g, len;
   int slot;    // partial slot: (column + unit) * LH + line head
   bool whole;  // the run is the whole pair
-  const uint16_t* kb;
-  const uint16_t* vb;
+  const char* kb;
+  const char* vb;
 };
 
 // The run that starts at line tile x of column `item` (ending at hi), head h.
-template <int SRC>
+template <int KIND, int SRC>
 __device__ __forceinline__ Seg seg_at(const AttnArgs& a, const UnitTable& ut, int x, int item, int hi,
                                       int h) {
   int lo_u = 0, hi_u = a.n_units;  // largest u with pref[u] <= x
@@ -639,25 +719,25 @@ __device__ __forceinline__ Seg seg_at(const AttnArgs& a, const UnitTable& ut, in
   const int aux = uniform_i32(ut.aux[u]);
   if constexpr (SRC == SRC_DENSE) {
     const int64_t base = ((int64_t)sg.b * a.S * a.Hkv + sg.g) * kHeadDim;
-    sg.kb = a.k + base;
-    sg.vb = a.v + base;
+    sg.kb = kv_at<KIND>(a.k, base);
+    sg.vb = kv_at<KIND>(a.v, base);
   } else if constexpr (SRC == SRC_RAGGED) {
     const int64_t base = ((int64_t)aux * a.Hkv + sg.g) * kHeadDim;
-    sg.kb = a.k + base;
-    sg.vb = a.v + base;
+    sg.kb = kv_at<KIND>(a.k, base);
+    sg.vb = kv_at<KIND>(a.v, base);
   } else if constexpr (SRC == SRC_PAGED) {
-    sg.kb = a.k;
-    sg.vb = a.v;
+    sg.kb = kv_at<KIND>(a.k, 0);
+    sg.vb = kv_at<KIND>(a.v, 0);
   } else {  // SRC_HYBRID: aux is the persistent slot, or < 0 for the cache buffer
     if (aux >= 0) {
       const int64_t base = ((int64_t)sg.b * a.P_slots + min(aux, max(a.P_slots - 1, 0))) *
                            a.pers_cap * kHeadDim;
-      sg.kb = a.k + base;
-      sg.vb = a.v + base;
+      sg.kb = kv_at<KIND>(a.k, base);
+      sg.vb = kv_at<KIND>(a.v, base);
     } else {
       const int64_t base = ((int64_t)sg.b * a.Hkv + sg.g) * a.buf_cap * kHeadDim;
-      sg.kb = a.k2 + base;
-      sg.vb = a.v2 + base;
+      sg.kb = kv_at<KIND>(a.k2, base);
+      sg.vb = kv_at<KIND>(a.v2, base);
     }
   }
   return sg;
@@ -690,11 +770,12 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   set_progress_priority(3);
 
   uint32_t row_off[4];
-  tile_row_offsets(tile_row_bytes<SRC>(a), lane, row_off);
+  tile_row_offsets<KIND>(tile_row_bytes<KIND, SRC>(a), lane, row_off);
+  using KP = KvPiece<KIND>;
 
   // Load side: run ls, next tile to load lx; `more` is false once the share
   // is loaded.
-  Seg ls = seg_at<SRC>(a, ut, L.first(lk), lk, x_end, lh);
+  Seg ls = seg_at<KIND, SRC>(a, ut, L.first(lk), lk, x_end, lh);
   int lx = ls.x0;
   bool more = true;
   // Process side: run ps, next tile to process px.
@@ -712,15 +793,15 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
       more = false;
       return;
     }
-    ls = seg_at<SRC>(a, ut, lx, lk, x_end, lh);  // the next unit
+    ls = seg_at<KIND, SRC>(a, ut, lx, lk, x_end, lh);  // the next unit
     load_q<G>(a, (int64_t)ls.b * a.Hq + (int64_t)ls.g * G, lane & 15, qn);
   };
-  auto load = [&](u32x4 (&kf)[4], u32x4 (&vf)[4]) {
-    load_kv_tile<SRC>(a, ls.b, ls.g, ls.kb, ls.vb, ls.len, (ls.t + lx - ls.x0) * kTile, more, row_off,
-                      kf, vf);
+  auto load = [&](KP (&kf)[4], KP (&vf)[4]) {
+    load_kv_tile<KIND, SRC>(a, ls.b, ls.g, ls.kb, ls.vb, ls.len, (ls.t + lx - ls.x0) * kTile, more,
+                            row_off, kf, vf);
   };
   // Processes tile px; returns false when nothing is left to process.
-  auto step = [&](const u32x4 (&kf)[4], const u32x4 (&vf)[4]) -> bool {
+  auto step = [&](const KP (&kf)[4], const KP (&vf)[4]) -> bool {
     process_tile<KIND, G>(a, qf, kf, vf, (ps.t + px - ps.x0) * kTile, ps.len, lg, st);
     ++done;
     if ((4 * done) / share != (4 * (done - 1)) / share) set_progress_priority(3 - (4 * done) / share);
@@ -743,7 +824,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
     return true;
   };
 
-  u32x4 ka[4], va[4], kb[4], vb[4];
+  KP ka[4], va[4], kb[4], vb[4];
   load(ka, va);
   for (;;) {
     advance();
@@ -888,10 +969,15 @@ int device_cu_count() {
   return cus;
 }
 
-int balanced_blocks(int dtype, int G, int src, int64_t est_tiles) {
+int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles) {
   if (G < 1 || G > kMaxGroup) return 1;
-  const int occ = dtype == KIND_F16 ? dispatch_g<KIND_F16, OccF>(G, src)
-                                    : dispatch_g<KIND_BF16, OccF>(G, src);
+  int occ;
+  switch ((dtype == KIND_F16 ? KIND_F16 : KIND_BF16) | (kv8 ? KIND_KV8 : 0)) {
+    case KIND_F16: occ = dispatch_g<KIND_F16, OccF>(G, src); break;
+    case KIND_BF16: occ = dispatch_g<KIND_BF16, OccF>(G, src); break;
+    case KIND_F16 | KIND_KV8: occ = dispatch_g<KIND_F16 | KIND_KV8, OccF>(G, src); break;
+    default: occ = dispatch_g<KIND_BF16 | KIND_KV8, OccF>(G, src); break;
+  }
   const int64_t cap = (int64_t)device_cu_count() * occ;
   // at least kMinTilesPerWave tiles per wave when the work is small
   const int64_t need = (est_tiles + (int64_t)kWaves * kMinTilesPerWave - 1) / ((int64_t)kWaves * kMinTilesPerWave);
@@ -917,8 +1003,12 @@ bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream) {
-  return a.dtype == KIND_F16 ? dispatch_g<KIND_F16, LaunchF>(a.G, a, stream)
-                             : dispatch_g<KIND_BF16, LaunchF>(a.G, a, stream);
+  switch ((a.dtype == KIND_F16 ? KIND_F16 : KIND_BF16) | (a.kv8 ? KIND_KV8 : 0)) {
+    case KIND_F16: return dispatch_g<KIND_F16, LaunchF>(a.G, a, stream);
+    case KIND_BF16: return dispatch_g<KIND_BF16, LaunchF>(a.G, a, stream);
+    case KIND_F16 | KIND_KV8: return dispatch_g<KIND_F16 | KIND_KV8, LaunchF>(a.G, a, stream);
+    default: return dispatch_g<KIND_BF16 | KIND_KV8, LaunchF>(a.G, a, stream);
+  }
 }
 
 }  // namespace kvdec

@@ -8,6 +8,7 @@
 namespace kvdec {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +44,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // 16-byte buffer load marked non-temporal (streamed once).
 __device__ __forceinline__ u32x4 buffer_load_b128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+
+// 8-byte buffer load marked non-temporal.
+__device__ __forceinline__ u32x2 buffer_load_b64_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2);
 }
 
 __device__ __forceinline__ void store_b128(void* p, u32x4 v) {

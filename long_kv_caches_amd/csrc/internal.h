@@ -28,10 +28,10 @@ enum Source : int { SRC_DENSE = 0, SRC_RAGGED = 1, SRC_PAGED = 2, SRC_HYBRID = 3
 
 struct AttnArgs {
   const uint16_t* q;
-  const uint16_t* k;            // dense / ragged / paged pool; hybrid: persistent slots
-  const uint16_t* v;
-  const uint16_t* k2;           // hybrid: cache buffer
-  const uint16_t* v2;
+  const void* k;                // dense / ragged / paged pool; hybrid: persistent slots
+  const void* v;
+  const void* k2;               // hybrid: cache buffer
+  const void* v2;
   const int32_t* seqlens;
   const int32_t* cu_seqlens;
   const int32_t* block_table;
@@ -55,9 +55,11 @@ struct AttnArgs {
   int n_blocks;                 // balanced: persistent workgroups
   int n_cu;                     // balanced: CUs of the device (workgroups of the first round)
   int n_units;                  // balanced: units of the tile line
-  float scale_log2;             // softmax_scale * log2(e)
+  float scale_log2;             // softmax_scale * log2(e) (* k_scale for e4m3 K)
+  float out_scale;              // e4m3 V: v_scale, applied with the final normalisation
   int src;
   int dtype;
+  int kv8;                      // K and V are e4m3 codes, one byte per element
 };
 
 // Bytes of workspace for `slots` partials of group size G plus n_pref ints.
@@ -68,7 +70,7 @@ bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64
                           AttnArgs* a);
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
-int balanced_blocks(int dtype, int G, int src, int64_t est_tiles);
+int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -30,7 +30,8 @@ def say(msg):
 
 
 def dev(a, bf16=False):
-    """numpy -> cuda tensor.  float16 stays fp16; uint16 with bf16=True is bf16 bits."""
+    """numpy -> cuda tensor.  float16 stays fp16; uint16 with bf16=True is bf16
+    bits; uint8 (e4m3 codes) stays uint8."""
     t = torch.from_numpy(np.ascontiguousarray(a))
     if a.dtype == np.uint16:
         t = t.view(torch.int16).view(torch.bfloat16 if bf16 else torch.float16)
@@ -89,10 +90,12 @@ def decode_on_gpu(d, split_tokens=0, bf16=False, want_lse=True, repeat=1, dev_in
     cuda tensor and a numpy array; with repeat > 1 returns a list of outs."""
     layout = LAYOUTS[d["layout"]]
     B, Hq, Hkv = d["B"], d["Hq"], d["Hkv"]
+    fp8 = d["k"].dtype == np.uint8  # e4m3 codes with d["k_scale"], d["v_scale"]
     if dev_inputs is None:
         conv = to_bf16_bits if bf16 else (lambda x: x)
-        dev_inputs = dict(q=dev(conv(d["q"]), bf16), k=dev(conv(d["k"]), bf16),
-                          v=dev(conv(d["v"]), bf16))
+        kv = (lambda x: x) if fp8 else conv
+        dev_inputs = dict(q=dev(conv(d["q"]), bf16), k=dev(kv(d["k"]), bf16),
+                          v=dev(kv(d["v"]), bf16))
     q, k, v = dev_inputs["q"], dev_inputs["k"], dev_inputs["v"]
     seqlens = cu = bt = None
     kv_rows, page, max_pages = 0, 0, 0
@@ -109,9 +112,11 @@ def decode_on_gpu(d, split_tokens=0, bf16=False, want_lse=True, repeat=1, dev_in
         bt = torch.from_numpy(d["block_table"]).cuda()
         max_seqlen = int(np.max(d["seqlens"])) if B else 0
         kv_rows, page, max_pages = d["k"].shape[0], d["page"], d["block_table"].shape[1]
+    fmt = dict(kv_format=K.KVDEC_KV_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if fp8 else {}
     desc = K.attn_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=q.dtype, layout=layout,
                        max_seqlen=max_seqlen, softmax_scale=d["scale"], page_size=page,
-                       max_pages_per_seq=max_pages, split_tokens=split_tokens, kv_rows=kv_rows)
+                       max_pages_per_seq=max_pages, split_tokens=split_tokens, kv_rows=kv_rows,
+                       **fmt)
     ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc))
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda") if want_lse else None
     outs = []

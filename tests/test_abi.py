@@ -6,6 +6,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import long_kv_caches_amd as K
@@ -28,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 4
+    assert _lib.lib.kvdec_abi_version() == 5
 
 
 def test_status_strings():
@@ -214,3 +215,43 @@ def test_kvpr_split_and_load_validation():
     assert L(2, 9, 8, 512, 4, 128, *args, S1, S2) == K._lib.KVDEC_ERR_INVALID  # l > s'
     assert L(2, 4, 8, 512, 4, 128, *args[:5], 7 * 512, *args[6:], S1, S2) == K._lib.KVDEC_ERR_INVALID
     assert "s_prime" in K.last_error()
+
+
+def test_e4m3_kv_format_validation():
+    D = K.attn_desc(batch=2, num_q_heads=8, num_kv_heads=2, dtype=torch.float16,
+                    layout=K.KVDEC_DENSE, max_seqlen=64)
+    n = ctypes.c_size_t()
+    W = _lib.lib.kvdec_decode_attn_workspace
+    D.kv_format = 7
+    assert W(ctypes.byref(D), ctypes.byref(n)) == K._lib.KVDEC_ERR_UNSUPPORTED
+    D.kv_format = K.KVDEC_KV_E4M3
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        D.k_scale, D.v_scale = ks, vs
+        assert W(ctypes.byref(D), ctypes.byref(n)) == K._lib.KVDEC_ERR_INVALID
+        assert "scale" in K.last_error()
+    D.k_scale, D.v_scale = 0.01, 0.02
+    assert W(ctypes.byref(D), ctypes.byref(n)) == 0
+
+
+def test_descriptor_layout_matches_the_header(tmp_path):
+    """The ctypes descriptors have the C structs' size and field offsets."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = [f for f, _ in _lib.AttnDesc._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "kvdec.h"', "int main(void) {",
+             'printf("%zu %zu\\n", sizeof(kvdec_attn_desc), sizeof(kvdec_hybrid_desc));']
+    lines += [f'printf("%zu\\n", offsetof(kvdec_attn_desc, {f}));' for f in fields]
+    lines += ["return 0; }"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                           "-I", "/opt/rocm/include", str(src), "-o", str(exe)])
+    out = subprocess.check_output([str(exe)]).decode().split()
+    assert int(out[0]) == ctypes.sizeof(_lib.AttnDesc)
+    assert int(out[1]) == ctypes.sizeof(_lib.HybridDesc)
+    for f, off in zip(fields, out[2:]):
+        assert int(off) == getattr(_lib.AttnDesc, f).offset, f

@@ -14,10 +14,12 @@ pytestmark = pytest.mark.gpu
 def hybrid_on_gpu(d, split_tokens=0, head_map=None):
     hm = d["head_map"] if head_map is None else head_map
     B, Hq, Hkv = d["B"], d["Hq"], d["Hkv"]
+    fp8 = d["pers_k"].dtype == np.uint8
+    fmt = dict(kv_format=K.KVDEC_KV_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if fp8 else {}
     desc = K.hybrid_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
                          softmax_scale=d["scale"], split_tokens=split_tokens,
                          num_pers_slots=d["pers_k"].shape[1], pers_cap=d["pers_k"].shape[2],
-                         buf_cap=d["buf_k"].shape[2])
+                         buf_cap=d["buf_k"].shape[2], **fmt)
     ws = K.alloc_workspace(K.kvdec_sparse_hybrid_attn_workspace(desc))
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -32,7 +34,8 @@ def hybrid_on_gpu(d, split_tokens=0, head_map=None):
 def hybrid_oracle(d, head_map=None):
     hm = d["head_map"] if head_map is None else head_map
     return oracle.hybrid_attn(d["q"], d["pers_k"], d["pers_v"], d["pers_len"], d["buf_k"],
-                              d["buf_v"], d["buf_len"], hm, scale=d["scale"])
+                              d["buf_v"], d["buf_len"], hm, scale=d["scale"],
+                              k_scale=d.get("k_scale"), v_scale=d.get("v_scale"))
 
 
 @pytest.mark.parametrize("model", ["llama3-8b", "qwen2.5-14b"])
