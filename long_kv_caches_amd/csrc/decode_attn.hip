@@ -72,6 +72,12 @@ constexpr int kKvBytes = kKv8<KIND> ? 1 : 2;  // bytes per K/V element
 template <int KIND>
 using KvPiece = std::conditional_t<kKv8<KIND>, u32x2, u32x4>;
 
+// e4m3 K/V with three or more query heads per KV head take the matrix-core
+// tile path (below); one or two heads keep the VALU path, whose per-tile work
+// is small there and which holds more waves per SIMD.
+template <int KIND, int G>
+constexpr bool kUsesMfma = kKv8<KIND> && G >= 3;
+
 // Address of K/V element `elems` of a tensor starting at base.
 template <int KIND>
 __device__ __forceinline__ const char* kv_at(const void* base, int64_t elems) {
@@ -326,39 +332,6 @@ __device__ __forceinline__ void process_tile(const AttnArgs& a, const u32x4 (&qf
   }
 }
 
-// Streams tiles tile_first + k * tile_step (k < count) of pair (b, g) into st.
-template <int KIND, int G, int SRC>
-__device__ __forceinline__ void run_tiles(const AttnArgs& a, int b, int g, const SeqView& sq,
-                                          const u32x4 (&qf)[G], int tile_first, int count,
-                                          int tile_step, WaveState<G>& st) {
-  const int lane = threadIdx.x & 63;
-  const int lg = lane >> 4;
-  uint32_t row_off[4];
-  tile_row_offsets<KIND>(tile_row_bytes<KIND, SRC>(a), lane, row_off);
-  using KP = KvPiece<KIND>;
-  auto load = [&](int k, KP (&kf)[4], KP (&vf)[4]) {
-    load_kv_tile<KIND, SRC>(a, b, g, sq.kb, sq.vb, sq.len, (tile_first + k * tile_step) * kTile,
-                            k < count, row_off, kf, vf);
-  };
-  auto process = [&](const KP (&kf)[4], const KP (&vf)[4], int k) {
-    process_tile<KIND, G>(a, qf, kf, vf, (tile_first + k * tile_step) * kTile, sq.len, lg, st);
-  };
-
-  // Ping-pong: loads are unconditional (a tile past the run reads nothing), so
-  // no branch or register copy forces an early wait on the prefetch.
-  if (count <= 0) return;
-  KP ka[4], va[4], kb[4], vb[4];
-  load(0, ka, va);
-  for (int k = 0;; k += 2) {
-    load(k + 1, kb, vb);
-    process(ka, va, k);
-    if (k + 1 >= count) break;
-    load(k + 2, ka, va);
-    process(kb, vb, k + 1);
-    if (k + 2 >= count) break;
-  }
-}
-
 // Final output of G heads from a finished wave state (lanes of row group 0).
 template <int KIND, int G>
 __device__ __forceinline__ void store_output(const AttnArgs& a, int64_t head0, const WaveState<G>& st,
@@ -470,6 +443,315 @@ __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot
 }
 
 // ---------------------------------------------------------------------------
+// Tile paths.  A path is how a wave holds q, a tile and its softmax state:
+//   VecPath  -- the VALU path above (lanes own row pieces of K and V);
+//   MfmaPath -- matrix cores for the scores and P.V (e4m3 K/V), below.
+// Both present the same functions to the schedules.
+// ---------------------------------------------------------------------------
+
+template <int KIND, int G>
+struct VecPath {
+  using Q = u32x4[G];
+  using State = WaveState<G>;
+  struct Tile {
+    KvPiece<KIND> k[4], v[4];
+  };
+  struct Offs {
+    uint32_t row[4];
+  };
+  template <int SRC>
+  __device__ static void offsets(const AttnArgs& a, int lane, Offs& o) {
+    tile_row_offsets<KIND>(tile_row_bytes<KIND, SRC>(a), lane, o.row);
+  }
+  __device__ static void load_q(const AttnArgs& a, int64_t head0, int lane, Q& q) {
+    kvdec::load_q<G>(a, head0, lane & 15, q);
+  }
+  template <int SRC>
+  __device__ static void load(const AttnArgs& a, int b, int g, const char* kb, const char* vb, int len,
+                              int t0, bool active, const Offs& o, Tile& t) {
+    load_kv_tile<KIND, SRC>(a, b, g, kb, vb, len, t0, active, o.row, t.k, t.v);
+  }
+  __device__ static void process(const AttnArgs& a, const Q& q, const Tile& t, int t0, int len,
+                                 int lane, State& st) {
+    process_tile<KIND, G>(a, q, t.k, t.v, t0, len, lane >> 4, st);
+  }
+  __device__ static void store_output(const AttnArgs& a, int64_t head0, const State& st, int lane) {
+    kvdec::store_output<KIND, G>(a, head0, st, lane);
+  }
+  __device__ static void store_partial(const AttnArgs& a, int64_t slot, const State& st, int lane) {
+    kvdec::store_partial<G>(a, slot, st, lane);
+  }
+  // The finished state into the chunk kernel's LDS merge arrays.
+  __device__ static void to_lds(const State& st, int lane, float (*so)[kHeadDim], float* sm,
+                                float* sl) {
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) so[j][8 * lane + e] = st.o[j][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        sm[j] = st.m[j];
+        sl[j] = st.l[j];
+      }
+    }
+  }
+};
+
+// Matrix-core path, for e4m3 K/V (3 <= G <= 8 query heads, padded to 16).
+//   Scores: S[token][head] by four v_mfma_f32_16x16x32 (f16 or bf16, the
+//   query's type): A = K (lane l: token l%16, dims 32*(l/16) .. +31 of the
+//   row, widened from its 32 codes), B = q (lane l: head l%16, the same
+//   dims).  The dot product only needs K and q to agree on which dim each
+//   k index is, so each lane reads 32 contiguous bytes of one row.
+//   Result: lane l holds head n = l%16 for tokens 4*(l/16) + i.
+//   Softmax: per lane for its head's four tokens; the max across the four
+//   lane groups by permlane swaps; P is rounded to fp16 once and the running
+//   sum adds the rounded values, so the output stays a convex combination of
+//   V rows.
+//   P.V: eight v_mfma_f32_16x16x16_f16: A = P exactly as the scores left it
+//   (lane l: head l%16, tokens 4*(l/16) + i), B = V (lane l: tokens
+//   4*(l/16) + i, dim 8*(l%16) + c for product c): V is loaded as in the VALU
+//   path (rows 4*(l/16) .. +3, 8-byte piece l%16) and its 4 x 8 codes are
+//   transposed with byte permutes, then widened to fp16 (exact).
+//   Output: o[c][i] is head 4*(l/16) + i, dim 8*(l%16) + c.
+template <int QK>
+__device__ __forceinline__ f32x4 mfma_scores(u32x4 k, u32x4 q, f32x4 c) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  if constexpr (QK == KIND_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, k), __builtin_bit_cast(h8, q), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, k), __builtin_bit_cast(b8, q),
+                                                   c, 0, 0, 0);
+}
+
+// Two e4m3 codes (bytes 0-1, or 2-3 with hi) widened to a packed pair of the
+// 16-bit type QK (exact).
+template <int QK>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, bool hi) {
+  if constexpr (QK == KIND_F16)
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  else
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+
+struct MState {
+  float m, l;    // this lane's head (lane % 16): running max (log2 units), sum of its tokens
+  f32x4 o[8];    // o[c][i]: head 4*(lane/16) + i, dim 8*(lane%16) + c
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void finish() { l = rowgroup_sum(l); }
+};
+
+template <int KIND, int G>
+struct MfmaPath {
+  static_assert(kKv8<KIND> && G <= 8, "matrix-core path: e4m3 K/V, at most 8 heads");
+  // Registers: 126 VGPRs + 32 AGPRs (the accumulators), three waves per SIMD;
+  // capping it at four waves spills.
+  using Q = u32x4[4];
+  using State = MState;
+  struct Tile {
+    u32x4 k[2];  // 32 codes of one row
+    u32x2 v[4];  // rows 4*(l/16) + i, 8 codes each
+  };
+  struct Offs {
+    uint32_t krow;    // this lane's K bytes within a tile
+    uint32_t row[4];  // this lane's V pieces within a tile
+  };
+  template <int SRC>
+  __device__ static void offsets(const AttnArgs& a, int lane, Offs& o) {
+    const uint32_t rb = tile_row_bytes<KIND, SRC>(a);
+    o.krow = (lane & 15) * rb + 32 * (lane >> 4);
+    tile_row_offsets<KIND>(rb, lane, o.row);
+  }
+  __device__ static void load_q(const AttnArgs& a, int64_t head0, int lane, Q& q) {
+    const int n = lane & 15;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      q[c] = n < G ? load_b128(a.q + (head0 + n) * kHeadDim + 32 * (lane >> 4) + 8 * c)
+                   : u32x4{0, 0, 0, 0};
+  }
+  template <int SRC>
+  __device__ static void load(const AttnArgs& a, int b, int g, const char* kb, const char* vb, int len,
+                              int t0, bool active, const Offs& o, Tile& t) {
+    const uint32_t row_bytes = tile_row_bytes<KIND, SRC>(a);
+    const int rows = active ? min(len - t0, kTile) : 0;
+    int64_t row0;  // byte offset of the tile's first row
+    if constexpr (SRC == SRC_PAGED) {
+      int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
+      pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));
+      row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;
+    } else {
+      row0 = (int64_t)t0 * row_bytes;
+    }
+    const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
+    t.k[0] = buffer_load_b128_nt(rk, o.krow);
+    t.k[1] = buffer_load_b128_nt(rk, o.krow + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load_b64_nt(rv, o.row[i]);
+  }
+  __device__ static void process(const AttnArgs& a, const Q& q, const Tile& t, int t0, int len,
+                                 int lane, State& st) {
+    constexpr int QK = kQKind<KIND>;
+    const int n = lane & 15, grp = lane >> 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w0 = t.k[c >> 1][2 * (c & 1)], w1 = t.k[c >> 1][2 * (c & 1) + 1];
+      const u32x4 kk = {e4m3_pair<QK>(w0, false), e4m3_pair<QK>(w0, true), e4m3_pair<QK>(w1, false),
+                        e4m3_pair<QK>(w1, true)};
+      s = mfma_scores<QK>(kk, q[c], s);
+    }
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = t0 + 4 * grp + i < len ? s[i] * a.scale_log2 : -INFINITY;
+    const float tmax = rowgroup_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float m_new = fmaxf(st.m, tmax);  // finite: every tile has a valid token
+    const float alpha = fast_exp2(st.m - m_new);
+    const bool grew = n < G && m_new > st.m;
+    st.m = m_new;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 ph;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ph[i] = (_Float16)(n < G ? fast_exp2(sc[i] - m_new) : 0.f);
+    st.l = st.l * alpha + (((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]));
+    if (__ballot(grew)) {
+      // rows of o are heads 4 * grp + i; their factors sit in lanes 4 * grp + i
+      float ai[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[c][i] *= ai[i];
+    }
+    // V codes of dim 8n + c for rows 0..3, one dword per c (byte i = row i)
+    uint32_t col[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t r0 = t.v[0][h], r1 = t.v[1][h], r2 = t.v[2][h], r3 = t.v[3][h];
+      const uint32_t t01a = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+      const uint32_t t01b = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+      const uint32_t t23a = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+      const uint32_t t23b = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+      col[4 * h + 0] = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+      col[4 * h + 1] = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+      col[4 * h + 2] = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+      col[4 * h + 3] = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+      const u2 vb = {e4m3_pair<KIND_F16>(col[c], false), e4m3_pair<KIND_F16>(col[c], true)};
+      st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(h4, vb), st.o[c], 0, 0, 0);
+    }
+  }
+  // Normaliser of each of this lane's output rows (heads 4 * grp + i).
+  __device__ static void row_sums(const State& st, int lane, float (&li)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) li[i] = __shfl(st.l, 4 * (lane >> 4) + i, 64);
+  }
+  __device__ static void store_output(const AttnArgs& a, int64_t head0, const State& st, int lane) {
+    constexpr int QK = kQKind<KIND>;
+    const int n = lane & 15, grp = lane >> 4;
+    float li[4];
+    row_sums(st, lane, li);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * grp + i;
+      if (j < G) {
+        const float inv = a.out_scale / li[i];
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)to_bits<QK>(st.o[2 * e][i] * inv) |
+                 ((uint32_t)to_bits<QK>(st.o[2 * e + 1][i] * inv) << 16);
+        store_b128(a.out + (head0 + j) * kHeadDim + 8 * n, u32x4{w[0], w[1], w[2], w[3]});
+      }
+    }
+    if (grp == 0 && n < G && a.lse) a.lse[head0 + n] = (st.m + __builtin_log2f(st.l)) * kLn2;
+  }
+  __device__ static void store_partial(const AttnArgs& a, int64_t slot, const State& st, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * grp + i;
+      if (j < G) {
+        float* dst = a.ws_o + (slot * G + j) * kHeadDim + 8 * n;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dst[c] = st.o[c][i];
+      }
+    }
+    if (grp == 0 && n < G) {
+      a.ws_ml[(slot * G + n) * 2] = st.m;
+      a.ws_ml[(slot * G + n) * 2 + 1] = st.l;
+    }
+  }
+  __device__ static void to_lds(const State& st, int lane, float (*so)[kHeadDim], float* sm,
+                                float* sl) {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * grp + i;
+      if (j < G)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) so[j][8 * n + c] = st.o[c][i];
+    }
+    if (grp == 0 && n < G) {
+      sm[n] = st.m;
+      sl[n] = st.l;
+    }
+  }
+};
+
+template <int KIND, int G>
+using PathOf = std::conditional_t<kUsesMfma<KIND, G>, MfmaPath<KIND, G>, VecPath<KIND, G>>;
+
+// Streams tiles tile_first + k * tile_step (k < count) of pair (b, g) into st.
+template <class P, int SRC>
+__device__ __forceinline__ void run_tiles(const AttnArgs& a, int b, int g, const SeqView& sq,
+                                          const typename P::Q& q, int tile_first, int count,
+                                          int tile_step, typename P::State& st) {
+  const int lane = threadIdx.x & 63;
+  typename P::Offs offs;
+  P::template offsets<SRC>(a, lane, offs);
+  using T = typename P::Tile;
+  auto load = [&](int k, T& t) {
+    P::template load<SRC>(a, b, g, sq.kb, sq.vb, sq.len, (tile_first + k * tile_step) * kTile,
+                          k < count, offs, t);
+  };
+  auto process = [&](const T& t, int k) {
+    P::process(a, q, t, (tile_first + k * tile_step) * kTile, sq.len, lane, st);
+  };
+
+  // Ping-pong: loads are unconditional (a tile past the run reads nothing), so
+  // no branch or register copy forces an early wait on the prefetch.
+  if (count <= 0) return;
+  T ta, tb;
+  load(0, ta);
+  for (int k = 0;; k += 2) {
+    load(k + 1, tb);
+    process(ta, k);
+    if (k + 1 >= count) break;
+    load(k + 2, ta);
+    process(tb, k + 1);
+    if (k + 2 >= count) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fixed-chunk schedule: one workgroup per (b, g, chunk).
 // ---------------------------------------------------------------------------
 
@@ -479,7 +761,6 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;
 
   int bid = blockIdx.x;
   const int g = bid % a.Hkv;
@@ -497,32 +778,21 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
   }
   if (c >= n_c) return;
 
-  u32x4 qf[G];
-  load_q<G>(a, head0, n, qf);
+  using P = PathOf<KIND, G>;
+  typename P::Q qf;
+  P::load_q(a, head0, lane, qf);
   const int tile0 = c * (a.chunk / kTile);
   const int n_tiles = (min(len, (c + 1) * a.chunk) - c * a.chunk + kTile - 1) / kTile;
   const int mine = n_tiles > wave ? (n_tiles - 1 - wave) / kWaves + 1 : 0;
-  WaveState<G> st;
+  typename P::State st;
   st.init();
-  run_tiles<KIND, G, SRC>(a, b, g, sq, qf, tile0 + wave, mine, kWaves, st);
+  run_tiles<P, SRC>(a, b, g, sq, qf, tile0 + wave, mine, kWaves, st);
   st.finish();
 
   // Merge the four waves through LDS.
   __shared__ float sm_o[kWaves][G][kHeadDim];
   __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
-  if (lane < 16) {
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][j][8 * n + e] = st.o[j][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      sm_m[wave][j] = st.m[j];
-      sm_l[wave][j] = st.l[j];
-    }
-  }
+  P::to_lds(st, lane, sm_o[wave], sm_m[wave], sm_l[wave]);
   __syncthreads();
 
   const int64_t item = ((int64_t)b * a.Hkv + g) * a.n_chunks + c;
@@ -757,7 +1027,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   if (blockIdx.x == 0)
     for (int u = threadIdx.x; u <= a.n_units; u += 256) a.ws_pref[u] = ut.pref[u];
 
-  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const int lane = threadIdx.x & 63;
   const int LH = line_heads<SRC>(a);
   const ItemLine L = item_line(a, uniform_i32(ut.pref[a.n_units]), LH);
   const int gw = uniform_i32((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6));
@@ -769,9 +1039,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   int done = 0;
   set_progress_priority(3);
 
-  uint32_t row_off[4];
-  tile_row_offsets<KIND>(tile_row_bytes<KIND, SRC>(a), lane, row_off);
-  using KP = KvPiece<KIND>;
+  using P = PathOf<KIND, G>;
+  using T = typename P::Tile;
+  typename P::Offs offs;
+  P::template offsets<SRC>(a, lane, offs);
 
   // Load side: run ls, next tile to load lx; `more` is false once the share
   // is loaded.
@@ -781,9 +1052,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   // Process side: run ps, next tile to process px.
   Seg ps = ls;
   int px = lx;
-  u32x4 qf[G], qn[G];
-  load_q<G>(a, (int64_t)ps.b * a.Hq + (int64_t)ps.g * G, lane & 15, qf);
-  WaveState<G> st;
+  typename P::Q qf, qn;
+  constexpr int kQWords = sizeof(typename P::Q) / sizeof(u32x4);
+  P::load_q(a, (int64_t)ps.b * a.Hq + (int64_t)ps.g * G, lane, qf);
+  typename P::State st;
   st.init();
 
   auto advance = [&]() {
@@ -794,15 +1066,15 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
       return;
     }
     ls = seg_at<KIND, SRC>(a, ut, lx, lk, x_end, lh);  // the next unit
-    load_q<G>(a, (int64_t)ls.b * a.Hq + (int64_t)ls.g * G, lane & 15, qn);
+    P::load_q(a, (int64_t)ls.b * a.Hq + (int64_t)ls.g * G, lane, qn);
   };
-  auto load = [&](KP (&kf)[4], KP (&vf)[4]) {
-    load_kv_tile<KIND, SRC>(a, ls.b, ls.g, ls.kb, ls.vb, ls.len, (ls.t + lx - ls.x0) * kTile, more,
-                            row_off, kf, vf);
+  auto load = [&](T& t) {
+    P::template load<SRC>(a, ls.b, ls.g, ls.kb, ls.vb, ls.len, (ls.t + lx - ls.x0) * kTile, more,
+                          offs, t);
   };
   // Processes tile px; returns false when nothing is left to process.
-  auto step = [&](const KP (&kf)[4], const KP (&vf)[4]) -> bool {
-    process_tile<KIND, G>(a, qf, kf, vf, (ps.t + px - ps.x0) * kTile, ps.len, lg, st);
+  auto step = [&](const T& t) -> bool {
+    P::process(a, qf, t, (ps.t + px - ps.x0) * kTile, ps.len, lane, st);
     ++done;
     if ((4 * done) / share != (4 * (done - 1)) / share) set_progress_priority(3 - (4 * done) / share);
     if (++px < ps.x1) return true;
@@ -812,27 +1084,27 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const int64_t head0 = (int64_t)ps.b * a.Hq + (int64_t)ps.g * G;
-    if (ps.whole) store_output<KIND, G>(a, head0, st, lane_s);
-    else store_partial<G>(a, ps.slot, st, lane_s);
+    if (ps.whole) P::store_output(a, head0, st, lane_s);
+    else P::store_partial(a, ps.slot, st, lane_s);
     st.init();
     if (!more) return false;
     // The loaded tile after the finished run starts run ls.
     ps = ls;
     px = ps.x0;
 #pragma unroll
-    for (int j = 0; j < G; ++j) qf[j] = qn[j];
+    for (int j = 0; j < kQWords; ++j) qf[j] = qn[j];
     return true;
   };
 
-  KP ka[4], va[4], kb[4], vb[4];
-  load(ka, va);
+  T ta, tb;
+  load(ta);
   for (;;) {
     advance();
-    load(kb, vb);
-    if (!step(ka, va)) break;
+    load(tb);
+    if (!step(ta)) break;
     advance();
-    load(ka, va);
-    if (!step(kb, vb)) break;
+    load(ta);
+    if (!step(tb)) break;
   }
 }
 

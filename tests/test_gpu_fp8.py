@@ -2,7 +2,9 @@
 against the fp64 oracle on the same codes and scales.
 
 The oracle decodes the codes exactly, so the tolerances are those of the
-16-bit path (fp32 accumulation, one rounding of the output).  A single key
+16-bit path (fp32 accumulation, one rounding of the output; the matrix-core
+path used from three query heads per KV head on also rounds each softmax
+weight to fp16 once, about 2^-11 relative, well inside them).  A single key
 returns v_scale * V exactly, which checks the kernel's decoding of every code.
 """
 import numpy as np
@@ -67,7 +69,7 @@ def test_ragged_tiles_tails_and_empty(split):
     _parity(d, "ragged tails", split_tokens=split)
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (24, 8), (40, 8), (64, 8)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 8), (40, 8), (64, 8)])
 def test_group_sizes(hq, hkv):
     d = kvgen.fp8_kv(kvgen.ragged_llama(seed=43, lens=[300, 2000, 45], Hq=hq, Hkv=hkv))
     _parity(d, f"G={hq // hkv}")
