@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_32k_traffic.json")
+TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_32k_e4m3_traffic.json")
 KERNEL_SOURCES = ["long_kv_caches_amd/csrc/decode_attn.hip", "long_kv_caches_amd/csrc/device_common.h",
                   "long_kv_caches_amd/csrc/internal.h", "long_kv_caches_amd/csrc/api.cpp"]
 
@@ -47,11 +48,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_algorithmic):
+def measured_traffic(per_launch_algorithmic, path=None):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -171,7 +172,8 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
     r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
     r["kv_token_heads_per_s"] = round(T * Hkv / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-                                 step_bytes, kern_us, None if fp8 else measured_traffic(step_bytes))
+                                 step_bytes, kern_us,
+                                 measured_traffic(step_bytes, TRAFFIC_FILE_FP8 if fp8 else TRAFFIC_FILE))
     r["roofline"]["launches_timed"] = launches
     if not args.no_cpu_baseline:
         import oracle
