@@ -21,6 +21,8 @@ Workload shapes:
   * ``clo_ahead``    -- CLO one-layer-ahead lookup: hidden states x [B, h] of
     the previous layer, the next layer's W_Q [Hq*D, h] (nn.Linear layout), and
     hidden states of the step the labels came from (x plus a per-sequence drift).
+  * ``clo_gather``   -- a full dense cache (Llama3-8B or Qwen2.5-14B heads,
+    batch 4, 128K) for CLO-style top-k sparse attention gathered in place.
   * ``kvpr_layer``   -- KVPR OPT-13B layer: h 5120, 40 heads, batch 32,
     s' 1024, split l 256, bf16 X and W, fp16 resident cache rows.
 """
@@ -413,6 +415,41 @@ def clo_ahead(seed=0, model="llama3-8b", B=4, h=None, Hq=None, Hkv=None, D=D_HEA
     return dict(model=model, B=B, Hq=Hq, Hkv=Hkv, D=D, h=h, s=s, weights=s.astype(np.float32),
                 x_prev=cast(x32), x_label=cast(x32 + scale[:, None] * noise), w_q=w,
                 drift=scale, eta=0.8, n_exp=3.0)
+
+
+def clo_gather(seed=0, model="llama3-8b", B=4, S=131072, frac=0.1, D=D_HEAD, lens=None):
+    """A full GPU-resident cache for index-gather sparse attention.
+
+    Draw order (``Draws(seed + 3000017)``): per-(KV head, channel) K outlier
+    scale ~ LogNormal(0, 0.5) (``ctl``), lengths ~ U{S/2..S} unless given
+    (``ctl``), q [B, Hq, D] ~ N(0,1), K = N(0,1) * scale, V ~ N(0,1), all in
+    the dense layout [B, S, Hkv, D]; top_k = round(frac * S).
+    """
+    Hq, Hkv = CLO_MODELS[model]
+    dr = Draws(seed + 3_000_017)
+    sigma = dr.ctl.lognormal(0.0, 0.5, size=(Hkv, D)).astype(np.float32)
+    if lens is None:
+        lens = dr.ctl.integers(S // 2, S + 1, size=B)
+    lens = np.asarray(lens, np.int32)
+    q = dr.normal((B, Hq, D))
+    k = dr.normal((B, S, Hkv, D), scale=sigma)
+    v = dr.normal((B, S, Hkv, D))
+    return dict(model=model, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, q=q, k=k, v=v, seqlens=lens,
+                top_k=int(round(frac * S)), scale=1.0 / math.sqrt(D))
+
+
+def random_indices(seed, B, Hkv, lens, top_k):
+    """Sorted random token selections without replacement per (b, g):
+    min(top_k, len_b) of [0, len_b), in the layout [B, Hkv, top_k] (-1 pad)."""
+    rng = Draws(seed).ctl
+    idx = np.full((B, Hkv, top_k), -1, np.int32)
+    n = np.zeros(B * Hkv, np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            m = min(top_k, int(lens[b]))
+            idx[b, g, :m] = np.sort(rng.choice(int(lens[b]), size=m, replace=False))
+            n[b * Hkv + g] = m
+    return idx, n
 
 
 # ---------------------------------------------------------------------------

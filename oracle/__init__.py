@@ -77,6 +77,12 @@ def _load():
     lib.orc_kvpr_time.restype = f64
     lib.orc_kvpr_best_split.argtypes = [f64, ctypes.c_int, ctypes.c_int, f64, f64, f64, f64, P]
     lib.orc_kvpr_best_split.restype = ctypes.c_int
+    lib.orc_topk_scores.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, i32]
+    lib.orc_topk_scores.restype = i32
+    lib.orc_topk_select.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, i32, P, P, i32]
+    lib.orc_topk_select.restype = i32
+    lib.orc_gather_attn.argtypes = [i32, i32, i32, i32, f64, i32, i32, P, P, P, P, P, i32, P, P, i32]
+    lib.orc_gather_attn.restype = i32
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i32
     _lib = lib
@@ -213,6 +219,54 @@ def hybrid_attn(q, pers_k, pers_v, pers_len, buf_k, buf_v, buf_len, head_map, *,
                                      _ptr(lse), nthreads)
     if rc != 0:
         raise ValueError("orc_hybrid_attn: bad arguments")
+    return out, lse
+
+
+def topk_scores(q, k, *, num_kv_heads, seqlens=None, kind=F16, nthreads=0):
+    """CLO top-k scores in fp64: s[b, g, t] = sum over KV head g's query heads
+    of q_j . K_t (t < len_b, else 0), and m[b, g, t] = sum |q_jd K_td|.
+    k is the dense cache [B, S, Hkv, D]."""
+    q = _u16(q); k = _u16(k)
+    B, Hq, D = q.shape
+    S = k.shape[1]
+    s = np.zeros((B, num_kv_heads, S), np.float64)
+    m = np.zeros_like(s)
+    rc = _load().orc_topk_scores(B, Hq, num_kv_heads, D, kind, S, _ptr(q), _ptr(k),
+                                 _ptr(_i32(seqlens)), _ptr(s), _ptr(m), nthreads)
+    if rc != 0:
+        raise ValueError("orc_topk_scores: bad arguments")
+    return s, m
+
+
+def topk_select(q, k, top_k, *, num_kv_heads, seqlens=None, kind=F16, nthreads=0):
+    """Exact top-k per (sequence, KV head) of the scores above (ties: smaller
+    token), ascending.  Returns (idx [B, Hkv, top_k] int32, idx_len [B * Hkv])."""
+    q = _u16(q); k = _u16(k)
+    B, Hq, D = q.shape
+    S = k.shape[1]
+    idx = np.full((B, num_kv_heads, max(top_k, 0)), -1, np.int32)
+    n = np.zeros(B * num_kv_heads, np.int32)
+    rc = _load().orc_topk_select(B, Hq, num_kv_heads, D, kind, S, _ptr(q), _ptr(k),
+                                 _ptr(_i32(seqlens)), int(top_k), _ptr(idx), _ptr(n), nthreads)
+    if rc != 0:
+        raise ValueError("orc_topk_select: bad arguments")
+    return idx, n
+
+
+def gather_attn(q, k, v, idx, idx_len, *, num_kv_heads, scale, kind=F16, nthreads=0):
+    """Attention of each query head over the token rows idx[b, g, :idx_len] of
+    the dense cache [B, S, Hkv, D] (CLO top-k sparse attention, gathered in place)."""
+    q = _u16(q); k = _u16(k); v = _u16(v)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, Hq, D = q.shape
+    S = k.shape[1]
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    rc = _load().orc_gather_attn(B, Hq, num_kv_heads, D, float(scale), kind, S, _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(idx), _ptr(_i32(idx_len)), idx.shape[2], _ptr(out),
+                                 _ptr(lse), nthreads)
+    if rc != 0:
+        raise ValueError("orc_gather_attn: bad arguments")
     return out, lse
 
 

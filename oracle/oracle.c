@@ -333,6 +333,133 @@ int orc_hybrid_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Index-gather sparse attention over a GPU-resident full cache.              */
+/* CLO page: top-k sparse attention (10% of the tokens) with HATA's hashed     */
+/* retrieval; here the exact scores stand in for the hashes.  Eq. 6: q.k =    */
+/* |q| |k| cos(q, k), so the ranking of the keys does not depend on |q|.      */
+/* Reading: one selection per KV head, ranking its tokens by the sum over its */
+/* query heads of q_j . K_t; ties go to the smaller token index; the selected */
+/* indices are returned in ascending order.                                   */
+/* ------------------------------------------------------------------------- */
+
+int orc_topk_scores(int B, int Hq, int Hkv, int D, int kind, int S, const uint16_t* q,
+                    const uint16_t* k, const int32_t* seqlens, double* scores, double* mags,
+                    int nthreads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || S < 0) return -1;
+  const int G = Hq / Hkv;
+  const double* L = lut(kind);
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+  for (long pair = 0; pair < (long)B * Hkv; ++pair) {
+    const int b = (int)(pair / Hkv), g = (int)(pair % Hkv);
+    int n = seqlens ? seqlens[b] : S;
+    if (n > S) n = S;
+    for (int t = 0; t < S; ++t) {
+      double acc = 0.0, mag = 0.0;
+      if (t < n) {
+        const uint16_t* kr = k + (((int64_t)b * S + t) * Hkv + g) * D;
+        for (int j = g * G; j < (g + 1) * G; ++j) {
+          const uint16_t* qr = q + ((int64_t)b * Hq + j) * D;
+          for (int d = 0; d < D; ++d) {
+            acc += L[qr[d]] * L[kr[d]];
+            mag += fabs(L[qr[d]] * L[kr[d]]);
+          }
+        }
+      }
+      scores[pair * S + t] = acc;
+      if (mags) mags[pair * S + t] = mag;
+    }
+  }
+  return 0;
+}
+
+typedef struct {
+  double s;
+  int t;
+} scored_token;
+
+/* Larger score first; equal scores: smaller token first. */
+static int by_score_desc(const void* pa, const void* pb) {
+  const scored_token* a = (const scored_token*)pa;
+  const scored_token* b = (const scored_token*)pb;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->t > b->t) - (a->t < b->t);
+}
+
+static int by_index(const void* pa, const void* pb) {
+  const int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+int orc_topk_select(int B, int Hq, int Hkv, int D, int kind, int S, const uint16_t* q,
+                    const uint16_t* k, const int32_t* seqlens, int kk, int32_t* idx,
+                    int32_t* idx_len, int nthreads) {
+  if (kk < 0 || B < 0 || Hkv <= 0 || S < 0) return -1;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)((int64_t)B * Hkv * (S > 0 ? S : 1)));
+  if (!sc) return -1;
+  if (orc_topk_scores(B, Hq, Hkv, D, kind, S, q, k, seqlens, sc, NULL, nthreads) != 0) {
+    free(sc);
+    return -1;
+  }
+#pragma omp parallel for schedule(dynamic)
+  for (long pair = 0; pair < (long)B * Hkv; ++pair) {
+    const int b = (int)(pair / Hkv);
+    int n = seqlens ? seqlens[b] : S;
+    if (n > S) n = S;
+    if (n < 0) n = 0;
+    scored_token* v = (scored_token*)malloc(sizeof(scored_token) * (size_t)(n > 0 ? n : 1));
+    for (int t = 0; t < n; ++t) {
+      v[t].s = sc[pair * S + t];
+      v[t].t = t;
+    }
+    qsort(v, (size_t)n, sizeof *v, by_score_desc);
+    const int m = n < kk ? n : kk;
+    int32_t* out = idx + pair * (int64_t)kk;
+    for (int i = 0; i < m; ++i) out[i] = v[i].t;
+    qsort(out, (size_t)m, sizeof *out, by_index);
+    idx_len[pair] = m;
+    free(v);
+  }
+  free(sc);
+  return 0;
+}
+
+int orc_gather_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int S,
+                    const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                    const int32_t* idx_len, int max_k, double* out, double* lse, int nthreads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || max_k < 0) return -1;
+  const int G = Hq / Hkv;
+  const kv_view kk = kv16(k, kind), vv = kv16(v, kind);
+  set_threads(nthreads);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+  for (long pair = 0; pair < (long)B * Hq; ++pair) {
+    const int b = (int)(pair / Hq), j = (int)(pair % Hq);
+    const int g = j / G;
+    const int n = idx_len[(int64_t)b * Hkv + g];
+    if (n < 0 || n > max_k) {
+      bad = 1;
+      continue;
+    }
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    const int32_t* ix = idx + ((int64_t)b * Hkv + g) * max_k;
+    for (int t = 0; t < n; ++t) {
+      if (ix[t] < 0 || ix[t] >= S) bad = 1;
+      rows[t] = (((int64_t)b * S + ix[t]) * Hkv + g) * D;
+    }
+    if (bad) {
+      free(rows);
+      continue;
+    }
+    const int64_t qo = ((int64_t)b * Hq + j) * D;
+    attend(D, scale, kind, q + qo, &kk, &vv, rows, n, out + qo, lse ? lse + (int64_t)b * Hq + j : NULL);
+    free(rows);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* CLO threshold chain, Eqs. 7-9.                                             */
 /* ------------------------------------------------------------------------- */
 

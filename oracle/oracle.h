@@ -95,6 +95,27 @@ int orc_hybrid_attn_e4m3(int B, int Hq, int Hkv, int D, double scale, int kind,
                          double* lse, int nthreads);
 
 /*
+ * Index-gather sparse attention (CLO page: top-k sparse attention over a
+ * fraction of the tokens, HATA's hashes replaced by exact scores; Eq. 6).
+ * K, V: the dense cache [B, S, Hkv, D]; seqlens[B] (NULL => S).
+ * orc_topk_scores: s[b, g, t] = sum over the group's query heads of q_j . K_t
+ *   (t < len_b; 0 beyond), and mags = sum |q_jd K_td| (may be NULL).
+ * orc_topk_select: per (b, g) the min(kk, len_b) tokens of largest s (ties:
+ *   smaller t), ascending, into idx[b, g, 0:kk]; counts into idx_len[b*Hkv+g].
+ * orc_gather_attn: attention of each query head over the rows idx[b, g,
+ *   0:idx_len[b*Hkv+g]] (row stride max_k) of its KV head.
+ */
+int orc_topk_scores(int B, int Hq, int Hkv, int D, int kind, int S, const uint16_t* q,
+                    const uint16_t* k, const int32_t* seqlens, double* scores, double* mags,
+                    int nthreads);
+int orc_topk_select(int B, int Hq, int Hkv, int D, int kind, int S, const uint16_t* q,
+                    const uint16_t* k, const int32_t* seqlens, int kk, int32_t* idx,
+                    int32_t* idx_len, int nthreads);
+int orc_gather_attn(int B, int Hq, int Hkv, int D, double scale, int kind, int S,
+                    const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                    const int32_t* idx_len, int max_k, double* out, double* lse, int nthreads);
+
+/*
  * Eqs. 7-9 of the CLO page (threshold chain), in fp64:
  *   theta* = arccos(eta); lambda_i = s_i^n; theta_i = lambda_i theta* + (1-lambda_i) pi;
  *   tau_i = cos(theta_i).
