@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 5
+#define KVDEC_ABI_VERSION 6
 
 typedef enum {
   KVDEC_OK = 0,
@@ -167,6 +167,61 @@ kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* desc, const void*
                                       const void* buf_v, const int32_t* buf_len,
                                       const int32_t* head_map, void* out, float* lse,
                                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Index-gather sparse attention (CLO page: decoding attends to a top-k
+ * selection of each head's tokens, 10% of them; the selection's indices point
+ * into the full cache, read in place with no compacted copy).
+ *
+ * base: batch, heads, head_dim, softmax_scale, dtype, split_tokens, kv_format
+ * and scales as for kvdec_attn_desc; max_seqlen is the cache's rows per
+ * sequence S (layout, page fields and kv_rows are ignored).
+ *   k, v     the dense cache [B, S, Hkv, 128] (dtype, or e4m3 codes)
+ *   idx      [B, Hkv, max_k] int32 token rows of each (sequence, KV head);
+ *            entries past idx_len are never read; rows are clamped into
+ *            [0, S), so malformed indices read wrong rows instead of faulting
+ *   idx_len  [B * Hkv] int32 in [0, max_k]
+ * For each query head j of KV head g:
+ *   out[b, j] = softmax_t(softmax_scale * q[b, j] . K[b, idx_t, g]) V[b, idx_t, g]
+ * over t < idx_len[b * Hkv + g] (out = 0, lse = -inf when empty).  The order
+ * of the indices does not matter.  Requires S * Hkv * 128 * (bytes per
+ * element) <= 2^31.
+ */
+typedef struct {
+  kvdec_attn_desc base;
+  int32_t max_k;
+} kvdec_gather_desc;
+
+kvdec_status kvdec_gather_attn_workspace(const kvdec_gather_desc* desc, size_t* bytes /*(host)*/);
+kvdec_status kvdec_gather_attn(const kvdec_gather_desc* desc, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const int32_t* idx_len,
+                               void* out, float* lse, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
+ * Exact top-k token selection for kvdec_gather_attn (CLO page: top-k sparse
+ * attention with HATA's hashed retrieval; the exact scores stand in for the
+ * hashes.  Eq. 6: q.k = |q| |k| cos(q, k), so the selection does not depend
+ * on |q|).  For each sequence b and KV head g, tokens t < len_b are ranked by
+ *   s_t = sum over g's query heads j of q[b, j] . K[b, t, g]   (fp32)
+ * and the min(top_k, len_b) largest are written to idx[b, g, :] in ascending
+ * token order (ties go to the smaller t), their count to idx_len[b*Hkv+g].
+ *   q [B, Hq, 128], k [B, S, Hkv, 128] (dtype); seqlens [B] int32 or NULL (all S)
+ *   idx [B, Hkv, top_k] int32 (entries past idx_len are not written)
+ * Requires S <= 262144, top_k >= 0, 16-bit K.  The workspace (16-byte
+ * aligned) holds the scores: B * Hkv rows of S rounded up to 4 floats.
+ */
+typedef struct {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t dtype;
+  int32_t max_seqlen;
+  int32_t top_k;
+} kvdec_topk_desc;
+
+kvdec_status kvdec_topk_select_workspace(const kvdec_topk_desc* desc, size_t* bytes /*(host)*/);
+kvdec_status kvdec_topk_select(const kvdec_topk_desc* desc, const void* q, const void* k,
+                               const int32_t* seqlens, int32_t* idx, int32_t* idx_len,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * CLO head-wise approximate cache lookup fused with the query-label update

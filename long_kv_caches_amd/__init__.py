@@ -13,4 +13,6 @@ from ._lib import (  # noqa: F401
     kvdec_kernel_timing, kvdec_kernel_timing_read, kvdec_kv_recompute, kvdec_kvpr_load_layer,
     kvdec_kvpr_split, kvdec_sparse_hybrid_attn,
     kvdec_sparse_hybrid_attn_workspace, last_error, status_string,
+    GatherDesc, TopkDesc, gather_desc, topk_desc, kvdec_gather_attn, kvdec_gather_attn_workspace,
+    kvdec_topk_select, kvdec_topk_select_workspace,
 )

@@ -42,6 +42,16 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class GatherDesc(ctypes.Structure):
+    _fields_ = [("base", AttnDesc), ("max_k", ctypes.c_int32)]
+
+
+class TopkDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
 class HybridDesc(ctypes.Structure):
     _fields_ = [("base", AttnDesc), ("num_pers_slots", ctypes.c_int32),
                 ("pers_cap", ctypes.c_int32), ("buf_cap", ctypes.c_int32)]
@@ -61,6 +71,10 @@ def _load():
                                       sz, P], st),
         "kvdec_headcache_lookup": ([i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P], st),
         "kvdec_headcache_lookup_ahead": ([i32] * 6 + [P] * 11 + [P], st),
+        "kvdec_gather_attn_workspace": ([P, ctypes.POINTER(ctypes.c_size_t)], st),
+        "kvdec_gather_attn": ([P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], st),
+        "kvdec_topk_select_workspace": ([P, ctypes.POINTER(ctypes.c_size_t)], st),
+        "kvdec_topk_select": ([P, P, P, P, P, P, P, ctypes.c_size_t, P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
         "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, i32, P, P, i64, P], st),
         "kvdec_kvpr_split": ([i64, i64, i64, i64, i32, ctypes.c_double, ctypes.c_double,
@@ -83,6 +97,8 @@ def _load():
 lib = _load()
 EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
             "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_lookup_ahead",
+            "kvdec_gather_attn_workspace", "kvdec_gather_attn", "kvdec_topk_select_workspace",
+            "kvdec_topk_select",
             "kvdec_headcache_thresholds",
             "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
             "kvdec_kernel_timing_read", "kvdec_status_string",
@@ -134,6 +150,45 @@ def hybrid_desc(*, num_pers_slots, pers_cap, buf_cap, **kw):
     kw.setdefault("layout", KVDEC_DENSE)
     kw.setdefault("max_seqlen", 0)
     return HybridDesc(attn_desc(**kw), num_pers_slots, pers_cap, buf_cap)
+
+
+def gather_desc(*, max_k, **kw):
+    """base fields as attn_desc (max_seqlen = the cache's rows per sequence)."""
+    kw.setdefault("layout", KVDEC_DENSE)
+    return GatherDesc(attn_desc(**kw), max_k)
+
+
+def topk_desc(*, batch, num_q_heads, num_kv_heads, dtype, max_seqlen, top_k, head_dim=128):
+    return TopkDesc(batch, num_q_heads, num_kv_heads, head_dim,
+                    _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype), max_seqlen, top_k)
+
+
+def kvdec_gather_attn_workspace(desc: GatherDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvdec_gather_attn_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def kvdec_gather_attn(desc, q, k, v, idx, idx_len, out, lse, workspace, stream=None):
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kvdec_gather_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                 _ptr(idx_len), _ptr(out), _ptr(lse), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def kvdec_topk_select_workspace(desc: TopkDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvdec_topk_select_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def kvdec_topk_select(desc, q, k, seqlens, idx, idx_len, workspace, stream=None):
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kvdec_topk_select(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(seqlens), _ptr(idx),
+                                 _ptr(idx_len), ws_ptr, ws_n, _stream(stream)))
+    return idx
 
 
 def kvdec_decode_attn_workspace(desc: AttnDesc) -> int:

@@ -449,6 +449,123 @@ kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* h, const void* q,
   return run_attn(d, p, a, ws, ws_bytes, stream);
 }
 
+static kvdec_status check_gather(const kvdec_gather_desc* gd) {
+  if (!gd) return fail(KVDEC_ERR_INVALID, "desc is NULL");
+  kvdec_status st = check_common(&gd->base, false);
+  if (st != KVDEC_OK) return st;
+  const kvdec_attn_desc* d = &gd->base;
+  if (d->max_seqlen < 0) return fail(KVDEC_ERR_INVALID, "max_seqlen < 0");
+  if (gd->max_k < 0) return fail(KVDEC_ERR_INVALID, "max_k < 0");
+  const int64_t elem = d->kv_format == KVDEC_KV_E4M3 ? 1 : 2;
+  if ((int64_t)d->max_seqlen * d->num_kv_heads * kHeadDim * elem > (int64_t(1) << 31))
+    return fail(KVDEC_ERR_UNSUPPORTED, "S * Hkv * 128 * element bytes must be <= 2^31");
+  return ok();
+}
+
+static Plan plan_gather(const kvdec_gather_desc* gd) {
+  const kvdec_attn_desc* d = &gd->base;
+  const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
+  return plan_attn(d->dtype, d->kv_format == KVDEC_KV_E4M3, d->num_q_heads / d->num_kv_heads,
+                   SRC_GATHER, pairs, pairs, pairs * (int64_t)gd->max_k, gd->max_k, d->split_tokens);
+}
+
+kvdec_status kvdec_gather_attn_workspace(const kvdec_gather_desc* gd, size_t* bytes) {
+  if (!bytes) return fail(KVDEC_ERR_INVALID, "bytes is NULL");
+  kvdec_status st = check_gather(gd);
+  if (st != KVDEC_OK) return st;
+  *bytes = attn_ws(&gd->base, plan_gather(gd));
+  return ok();
+}
+
+kvdec_status kvdec_gather_attn(const kvdec_gather_desc* gd, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const int32_t* idx_len,
+                               void* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  kvdec_status st = check_gather(gd);
+  if (st != KVDEC_OK) return st;
+  const kvdec_attn_desc* d = &gd->base;
+  if (d->batch == 0) return ok();
+  if (!q || !out || !idx_len) return fail(KVDEC_ERR_INVALID, "q, out and idx_len must be non-NULL");
+  if (gd->max_k > 0 && d->max_seqlen > 0 && (!k || !v || !idx))
+    return fail(KVDEC_ERR_INVALID, "k, v and idx must be non-NULL");
+  const Plan p = plan_gather(gd);
+  AttnArgs a = {};
+  fill_common(d, p, &a);
+  a.src = SRC_GATHER;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.idx_len = idx_len;
+  a.max_k = gd->max_k;
+  a.S = std::max(d->max_seqlen, 1);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  // with no cache rows or no index slots every pair is empty: the kernels
+  // then read neither k, v nor idx
+  if (d->max_seqlen == 0 || gd->max_k == 0) a.max_k = 0;
+  return run_attn(d, p, a, ws, ws_bytes, stream);
+}
+
+static kvdec_status check_topk(const kvdec_topk_desc* d) {
+  if (!d) return fail(KVDEC_ERR_INVALID, "desc is NULL");
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(KVDEC_ERR_INVALID, "bad batch / head counts");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(KVDEC_ERR_INVALID, "num_q_heads %% num_kv_heads != 0");
+  if (d->head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->dtype != KVDEC_F16 && d->dtype != KVDEC_BF16)
+    return fail(KVDEC_ERR_UNSUPPORTED, "dtype must be KVDEC_F16 or KVDEC_BF16");
+  if (d->max_seqlen < 0 || d->max_seqlen > kTopkMaxLen)
+    return fail(KVDEC_ERR_UNSUPPORTED, "max_seqlen must be in [0, %d]", kTopkMaxLen);
+  if (d->top_k < 0) return fail(KVDEC_ERR_INVALID, "top_k < 0");
+  if ((int64_t)d->batch * d->num_kv_heads > 65535)
+    return fail(KVDEC_ERR_UNSUPPORTED, "batch * num_kv_heads must be <= 65535");
+  return ok();
+}
+
+kvdec_status kvdec_topk_select_workspace(const kvdec_topk_desc* d, size_t* bytes) {
+  if (!bytes) return fail(KVDEC_ERR_INVALID, "bytes is NULL");
+  kvdec_status st = check_topk(d);
+  if (st != KVDEC_OK) return st;
+  *bytes = (size_t)d->batch * d->num_kv_heads * ((d->max_seqlen + 3) & ~3) * sizeof(float);
+  return ok();
+}
+
+kvdec_status kvdec_topk_select(const kvdec_topk_desc* d, const void* q, const void* k,
+                               const int32_t* seqlens, int32_t* idx, int32_t* idx_len, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  kvdec_status st = check_topk(d);
+  if (st != KVDEC_OK) return st;
+  if (d->batch == 0) return ok();
+  if (!idx_len) return fail(KVDEC_ERR_INVALID, "idx_len must be non-NULL");
+  const size_t need = (size_t)d->batch * d->num_kv_heads * ((d->max_seqlen + 3) & ~3) * sizeof(float);
+  if (d->max_seqlen > 0) {
+    if (!q || !k) return fail(KVDEC_ERR_INVALID, "q and k must be non-NULL");
+    if (d->top_k > 0 && !idx) return fail(KVDEC_ERR_INVALID, "idx must be non-NULL");
+    if (!ws || ws_bytes < need)
+      return fail(KVDEC_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (reinterpret_cast<uintptr_t>(ws) & 15)
+      return fail(KVDEC_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  TopkArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.seqlens = d->max_seqlen > 0 ? seqlens : nullptr;
+  a.scores = static_cast<float*>(ws);
+  a.idx = idx;
+  a.idx_len = idx_len;
+  a.B = d->batch;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.S = d->max_seqlen;
+  a.S4 = (d->max_seqlen + 3) & ~3;
+  a.top_k = d->top_k;
+  a.dtype = d->dtype;
+  return hip_status(launch_topk(a, stream), "top-k selection launch");
+}
+
 kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
                                     const void* q, void* labels, const float* weights,
                                     const float* tau, uint8_t* hit, float* agg, float* cos,

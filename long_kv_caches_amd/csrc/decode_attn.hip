@@ -104,6 +104,8 @@ __device__ __forceinline__ int pair_len(const AttnArgs& a, int b, int g) {
     len = min(max(a.cu_seqlens[b + 1], start), a.S) - start;
   } else if constexpr (SRC == SRC_PAGED) {
     len = min(a.seqlens[b], a.max_pages * a.page);
+  } else if constexpr (SRC == SRC_GATHER) {
+    len = min(a.idx_len[b * a.Hkv + g], a.max_k);
   } else {  // SRC_HYBRID
     const int slot = a.head_map[g];
     if (slot >= 0) len = slot < a.P_slots ? min(a.pers_len[b], a.pers_cap) : 0;
@@ -119,7 +121,7 @@ __device__ __forceinline__ SeqView locate(const AttnArgs& a, int b, int g) {
   // Values loaded from memory are the same for the whole wave; say so, so
   // that buffer descriptors built from them stay in scalar registers.
   s.len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
-  if constexpr (SRC == SRC_DENSE) {
+  if constexpr (SRC == SRC_DENSE || SRC == SRC_GATHER) {
     const int64_t base = ((int64_t)b * a.S * a.Hkv + g) * kHeadDim;
     s.kb = kv_at<KIND>(a.k, base);
     s.vb = kv_at<KIND>(a.v, base);
@@ -194,6 +196,25 @@ __device__ __forceinline__ uint32_t tile_row_bytes(const AttnArgs& a) {
   return (SRC == SRC_PAGED || SRC == SRC_HYBRID ? 1u : (uint32_t)a.Hkv) * kHeadDim * kKvBytes<KIND>;
 }
 
+// Gather source: token indices t0 + first .. t0 + first + count - 1 of pair
+// (b, g)'s index row (count 1 or 4), those at or past `rows` read as 0.
+__device__ __forceinline__ u32x4 gather_rows(const AttnArgs& a, int b, int g, int t0, int rows,
+                                            int first, int count) {
+  const int32_t* ix = a.idx + ((int64_t)b * a.Hkv + g) * a.max_k + t0;
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(uniform_ptr(ix), uniform_u32((uint32_t)max(rows, 0) * 4u));
+  if (count == 4) return __builtin_amdgcn_raw_buffer_load_b128(ri, 4 * first, 0, 0);
+  return u32x4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, 4 * first, 0, 0), 0u, 0u, 0u};
+}
+
+// Byte offset of a gathered row's piece: the token index clamped into the
+// cache, or an offset past the descriptor (zeros) for an invalid row.
+constexpr uint32_t kOutsideRows = 0x80000000u;
+__device__ __forceinline__ uint32_t gather_offset(const AttnArgs& a, uint32_t token, bool valid,
+                                                  uint32_t row_bytes, uint32_t piece) {
+  const int t = min(max((int)token, 0), a.S - 1);
+  return valid ? (uint32_t)t * row_bytes + piece : kOutsideRows;
+}
+
 // Loads K and V of the tile whose first row is t0 of pair (b, g) into kf, vf.
 // The rows come through buffer resources whose base is the tile's first row
 // (scalar registers) and whose size covers only rows below len, so rows past
@@ -206,6 +227,31 @@ __device__ __forceinline__ void load_kv_tile(const AttnArgs& a, int b, int g, co
                                              KvPiece<KIND> (&vf)[4]) {
   const uint32_t row_bytes = tile_row_bytes<KIND, SRC>(a);
   const int rows = active ? min(len - t0, kTile) : 0;
+  if constexpr (SRC == SRC_GATHER) {
+    // Rows of the tile come from the pair's index row; the descriptors cover
+    // the pair's whole cache (a.S rows), and a row past the tile's valid ones
+    // gets an offset outside them, so it reads zeros.
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    const u32x4 tix = gather_rows(a, b, g, t0, rows, 4 * lg, 4);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, uniform_u32((uint32_t)a.S * row_bytes));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, uniform_u32((uint32_t)a.S * row_bytes));
+    uint32_t off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      off[i] = gather_offset(a, tix[i], 4 * lg + i < rows, row_bytes, 8 * kKvBytes<KIND> * (lane & 15));
+    if constexpr (kKv8<KIND>) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b64_nt(rk, off[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b64_nt(rv, off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = buffer_load_b128_nt(rk, off[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[i] = buffer_load_b128_nt(rv, off[i]);
+    }
+    return;
+  }
   int64_t row0;  // byte offset of the tile's first row
   if constexpr (SRC == SRC_PAGED) {
     int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
@@ -586,6 +632,20 @@ struct MfmaPath {
                               int t0, bool active, const Offs& o, Tile& t) {
     const uint32_t row_bytes = tile_row_bytes<KIND, SRC>(a);
     const int rows = active ? min(len - t0, kTile) : 0;
+    if constexpr (SRC == SRC_GATHER) {
+      const int lane = threadIdx.x & 63, n = lane & 15, grp = lane >> 4;
+      const uint32_t kt = gather_rows(a, b, g, t0, rows, n, 1)[0];
+      const u32x4 vt = gather_rows(a, b, g, t0, rows, 4 * grp, 4);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, uniform_u32((uint32_t)a.S * row_bytes));
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, uniform_u32((uint32_t)a.S * row_bytes));
+      const uint32_t ko = gather_offset(a, kt, n < rows, row_bytes, 32 * grp);
+      t.k[0] = buffer_load_b128_nt(rk, ko);
+      t.k[1] = buffer_load_b128_nt(rk, ko == kOutsideRows ? ko : ko + 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        t.v[i] = buffer_load_b64_nt(rv, gather_offset(a, vt[i], 4 * grp + i < rows, row_bytes, 8 * n));
+      return;
+    }
     int64_t row0;  // byte offset of the tile's first row
     if constexpr (SRC == SRC_PAGED) {
       int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
@@ -851,8 +911,13 @@ __global__ __launch_bounds__(256) void decode_chunk_merge_kernel(AttnArgs a) {
 // beside it, so that finding a unit needs no global load.
 template <int SRC>
 __device__ __forceinline__ int line_heads(const AttnArgs& a) {
-  return SRC == SRC_HYBRID ? 1 : a.Hkv;
+  return SRC == SRC_HYBRID || SRC == SRC_GATHER ? 1 : a.Hkv;
 }
+
+// Sources whose units are single (sequence, KV head) pairs, as their lengths
+// differ per KV head.
+template <int SRC>
+constexpr bool kPairUnits = SRC == SRC_HYBRID || SRC == SRC_GATHER;
 
 struct UnitTable {
   int* pref;  // [n_units + 1]
@@ -869,8 +934,8 @@ __device__ void build_units(const AttnArgs& a, const UnitTable& ut) {
   const int u0 = min(nu, tid * per), u1 = min(nu, u0 + per);
   int local = 0;
   for (int u = u0; u < u1; ++u) {
-    const int b = SRC == SRC_HYBRID ? u / a.Hkv : u;
-    const int g = SRC == SRC_HYBRID ? u % a.Hkv : 0;
+    const int b = kPairUnits<SRC> ? u / a.Hkv : u;
+    const int g = kPairUnits<SRC> ? u % a.Hkv : 0;
     const int len = pair_len<SRC>(a, b, g);
     ut.len[u] = len;
     if constexpr (SRC == SRC_RAGGED) ut.aux[u] = min(max(a.cu_seqlens[b], 0), a.S);
@@ -981,13 +1046,13 @@ __device__ __forceinline__ Seg seg_at(const AttnArgs& a, const UnitTable& ut, in
   sg.x0 = x;
   sg.x1 = uniform_i32(min(hi, uend));
   sg.t = x - ubase;
-  sg.b = SRC == SRC_HYBRID ? u / a.Hkv : u;
-  sg.g = SRC == SRC_HYBRID ? u % a.Hkv : h;
+  sg.b = kPairUnits<SRC> ? u / a.Hkv : u;
+  sg.g = kPairUnits<SRC> ? u % a.Hkv : h;
   sg.len = uniform_i32(ut.len[u]);
   sg.slot = (item + u) * LH + h;
   sg.whole = x == ubase && sg.x1 == uend;
   const int aux = uniform_i32(ut.aux[u]);
-  if constexpr (SRC == SRC_DENSE) {
+  if constexpr (SRC == SRC_DENSE || SRC == SRC_GATHER) {
     const int64_t base = ((int64_t)sg.b * a.S * a.Hkv + sg.g) * kHeadDim;
     sg.kb = kv_at<KIND>(a.k, base);
     sg.vb = kv_at<KIND>(a.v, base);
@@ -1117,7 +1182,7 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(AttnArgs a) 
   const int j = blockIdx.x % G, p = blockIdx.x / G;
   const int b = p / a.Hkv, g = p % a.Hkv;
   const int LH = line_heads<SRC>(a);
-  const int u = SRC == SRC_HYBRID ? p : b, h = SRC == SRC_HYBRID ? 0 : g;
+  const int u = kPairUnits<SRC> ? p : b, h = kPairUnits<SRC> ? 0 : g;
   const int ubase = a.ws_pref[u], uend = a.ws_pref[u + 1];
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
   if (uend == ubase) {
@@ -1183,6 +1248,7 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
     case SRC_DENSE: return launch_src<KIND, G, SRC_DENSE>(a, stream);
     case SRC_RAGGED: return launch_src<KIND, G, SRC_RAGGED>(a, stream);
     case SRC_PAGED: return launch_src<KIND, G, SRC_PAGED>(a, stream);
+    case SRC_GATHER: return launch_src<KIND, G, SRC_GATHER>(a, stream);
     default: return launch_src<KIND, G, SRC_HYBRID>(a, stream);
   }
 }
@@ -1193,6 +1259,7 @@ int occupancy_g(int src) {
     case SRC_DENSE: return balanced_occupancy<KIND, G, SRC_DENSE>();
     case SRC_RAGGED: return balanced_occupancy<KIND, G, SRC_RAGGED>();
     case SRC_PAGED: return balanced_occupancy<KIND, G, SRC_PAGED>();
+    case SRC_GATHER: return balanced_occupancy<KIND, G, SRC_GATHER>();
     default: return balanced_occupancy<KIND, G, SRC_HYBRID>();
   }
 }

@@ -24,7 +24,7 @@ constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-r
 enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };
 
 // Where the K/V rows of one (sequence, KV head) pair live.
-enum Source : int { SRC_DENSE = 0, SRC_RAGGED = 1, SRC_PAGED = 2, SRC_HYBRID = 3 };
+enum Source : int { SRC_DENSE = 0, SRC_RAGGED = 1, SRC_PAGED = 2, SRC_HYBRID = 3, SRC_GATHER = 4 };
 
 struct AttnArgs {
   const uint16_t* q;
@@ -38,6 +38,8 @@ struct AttnArgs {
   const int32_t* pers_len;
   const int32_t* buf_len;
   const int32_t* head_map;
+  const int32_t* idx;           // gather: [B, Hkv, max_k] token rows of each pair
+  const int32_t* idx_len;       // gather: [B * Hkv]
   uint16_t* out;
   float* lse;
   float* ws_o;                  // [slots, G, 128] unnormalised partial outputs
@@ -48,6 +50,7 @@ struct AttnArgs {
                                 // paged: pages P in the pool
   int page, max_pages;          // paged
   int P_slots, pers_cap, buf_cap;  // hybrid
+  int max_k;                    // gather: index row stride (and the longest pair)
   int mode;                     // Mode
   int max_len;                  // lengths are clamped to this (the grid's coverage)
   int chunk;                    // chunks: tokens per work item, a multiple of kTile * kWaves
@@ -75,6 +78,20 @@ int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);
 int device_cu_count();
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t stream);
+
+// Exact top-k selection (topk.hip).
+constexpr int kTopkMaxLen = 262144;  // rows per sequence the selection handles
+struct TopkArgs {
+  const uint16_t* q;       // [B, Hq, 128]
+  const uint16_t* k;       // [B, S, Hkv, 128]
+  const int32_t* seqlens;  // [B] or NULL (all S)
+  float* scores;           // [B * Hkv, S4] workspace, S4 = S rounded up to 4
+  int32_t* idx;            // [B * Hkv, top_k]
+  int32_t* idx_len;        // [B * Hkv]
+  int B, Hq, Hkv, G, S, S4, top_k;
+  int dtype;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 // Profiling events around the main kernel launch of a call (no-ops unless
 // kvdec_kernel_timing is enabled on the calling thread).

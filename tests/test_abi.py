@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 5
+    assert _lib.lib.kvdec_abi_version() == 6
 
 
 def test_status_strings():
@@ -255,3 +255,29 @@ def test_descriptor_layout_matches_the_header(tmp_path):
     assert int(out[1]) == ctypes.sizeof(_lib.HybridDesc)
     for f, off in zip(fields, out[2:]):
         assert int(off) == getattr(_lib.AttnDesc, f).offset, f
+
+
+def test_gather_and_topk_validation():
+    n = ctypes.c_size_t()
+    gd = K.gather_desc(batch=2, num_q_heads=8, num_kv_heads=2, dtype=torch.float16, max_seqlen=100,
+                       max_k=10)
+    assert _lib.lib.kvdec_gather_attn_workspace(ctypes.byref(gd), ctypes.byref(n)) == 0
+    gd.max_k = -1
+    assert _lib.lib.kvdec_gather_attn_workspace(ctypes.byref(gd), ctypes.byref(n)) == 1
+    gd.max_k = 10
+    gd.base.max_seqlen = 1 << 23  # S * Hkv * 256 B > 2^31
+    assert _lib.lib.kvdec_gather_attn_workspace(ctypes.byref(gd), ctypes.byref(n)) == 2
+    gd.base.max_seqlen = 100
+    G = _lib.lib.kvdec_gather_attn
+    assert G(ctypes.byref(gd), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert "idx" in K.last_error()
+    td = K.topk_desc(batch=2, num_q_heads=8, num_kv_heads=2, dtype=torch.float16, max_seqlen=100,
+                     top_k=10)
+    assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 0
+    assert n.value == 2 * 2 * 100 * 4  # S = 100 is a multiple of 4
+    T = _lib.lib.kvdec_topk_select
+    assert T(ctypes.byref(td), FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 3  # workspace
+    td.max_seqlen = 300000
+    assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 2
+    td.max_seqlen, td.top_k = 100, -1
+    assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 1
