@@ -440,7 +440,7 @@ def bench_kvpr(args, K, np, torch, dev, stream):
                "synthetic (seeded; X ~ N(0,1), W ~ N(0, 1/h), bf16)",
                {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "split_point": l,
                 "context": s, "flops_per_step": flops, "w_layout": "out_in (nn.Linear)"})
-    r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel_k64", "achieved": round(kern_tflops, 2),
+    r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel_wide", "achieved": round(kern_tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
                      "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
     io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)
@@ -554,7 +554,7 @@ def bench_kvpr_overlap(args, K, np, torch, dev, stream):
     r["model_ms_at_split"] = round(t_model * 1e3, 4)
     r["by_split_point"] = rows
     r["speedup_vs_transfer_only"] = round(rows["0"]["ms"] / t_best, 3)
-    r["roofline"] = {"bound": "pcie", "kernel": "kvdec_kvpr_load_layer (copies + kv_recompute_kernel_k64)",
+    r["roofline"] = {"bound": "pcie", "kernel": "kvdec_kvpr_load_layer (copies + kv_recompute_kernel_wide)",
                      "achieved": round((b * l_best * h * 2 + 2 * b * (s - l_best) * h * 2) / (t_best * 1e-3) / 1e9, 2),
                      "peak": round(v_com / 1e9, 2), "unit": "GB/s", "frac": None, "traffic": None,
                      "note": "bytes that crossed PCIe per ms of layer load, against the measured "

@@ -94,6 +94,20 @@ def test_opt13b_full_size_sampled_rows_then_attention(w_layout):
     check_close(host_f64(out), ro, "attention (GPU rows)")
 
 
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+def test_wide_tiles_ragged_rows(w_layout):
+    """b*l = 2100 rows and h = 4096 make a grid of 9 x 32 tiles of 256 x 256, the
+    size at which [out, in] weights take the one-workgroup-per-CU kernel.  The
+    last row tile holds 52 rows and two batch boundaries fall inside tiles."""
+    d = kvgen.kvpr_layer(seed=8, b=3, h=4096, H=32, s=708, l=700)
+    say(f"[recompute] b=3 l=700 h=4096 (256 x 256 tiles, ragged) w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
+    edges = [0, 1, 255, 256, 699, 700, 1399, 1400, 2047, 2048, 2098, 2099]
+    pick = np.random.default_rng(9).choice(2100, 24, replace=False)
+    rows = np.unique(np.concatenate([edges, pick])).astype(np.int32)
+    _check_rows(d, kc, vc, rows=rows)
+
+
 def test_end_to_end_against_fp64_recompute():
     d = kvgen.kvpr_layer(seed=4, b=2, h=1024, H=8, s=200, l=120)
     say("[recompute] end to end vs fp64 X.W")
