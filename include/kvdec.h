@@ -356,10 +356,13 @@ kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_
                                    hipStream_t copy_stream);
 
 /* Kernel timing, a profiling aid.  While enabled on the calling thread, every
- * call above records a pair of HIP events on its stream right before and
- * right after its main kernel launch: the split kernel of an attention call
- * (not the merge kernel), the lookup kernel of kvdec_headcache_lookup (not
- * the compaction kernel), the GEMM of kvdec_kv_recompute and of
+ * call above launches its main kernel with a pair of HIP events that the
+ * runtime stamps from that kernel's own dispatch (hipExtLaunchKernel): its
+ * start and its end, with no extra packets on the stream.  Main kernels: the
+ * split kernel of an attention call (not the merge kernel), the lookup kernel
+ * of kvdec_headcache_lookup (not the compaction kernel), the projection of
+ * kvdec_headcache_lookup_ahead, each of the two kernels of
+ * kvdec_topk_select, the GEMM of kvdec_kv_recompute and of
  * kvdec_kvpr_load_layer.
  * kvdec_kernel_timing(1) starts a new measurement (the library keeps and
  * reuses its events); kvdec_kernel_timing(0) stops recording.

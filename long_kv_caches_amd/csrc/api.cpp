@@ -212,7 +212,8 @@ struct TimingState {
 };
 static thread_local TimingState g_timing;
 
-void timing_begin(hipStream_t stream) {
+void timing_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   TimingState& t = g_timing;
   if (!t.on || t.err != hipSuccess) return;
   if (t.used == t.pool.size()) {
@@ -224,13 +225,9 @@ void timing_begin(hipStream_t stream) {
     }
     t.pool.emplace_back(e0, e1);
   }
-  t.err = hipEventRecord(t.pool[t.used].first, stream);
-}
-
-void timing_end(hipStream_t stream) {
-  TimingState& t = g_timing;
-  if (!t.on || t.err != hipSuccess || t.used == t.pool.size()) return;
-  if ((t.err = hipEventRecord(t.pool[t.used].second, stream)) == hipSuccess) ++t.used;
+  *start = t.pool[t.used].first;
+  *stop = t.pool[t.used].second;
+  ++t.used;
 }
 
 // Checks the kvdec_headcache_lookup arguments and fills a.

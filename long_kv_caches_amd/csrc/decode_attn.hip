@@ -1218,18 +1218,15 @@ hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
   const dim3 block(256);
   if (a.mode == MODE_BALANCED) {
     const size_t lds = (size_t)(3 * a.n_units + 1) * sizeof(int);
-    timing_begin(stream);
-    decode_balanced_kernel<KIND, G, SRC><<<dim3((unsigned)a.n_blocks), block, lds, stream>>>(a);
-    timing_end(stream);
+    launch_timed(decode_balanced_kernel<KIND, G, SRC>, dim3((unsigned)a.n_blocks), block, (uint32_t)lds,
+                 stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv));
-  timing_begin(stream);
-  decode_chunk_kernel<KIND, G, SRC><<<grid, block, 0, stream>>>(a);
-  timing_end(stream);
+  launch_timed(decode_chunk_kernel<KIND, G, SRC>, grid, block, 0u, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
   decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);

@@ -222,14 +222,10 @@ template <int KIND, int P>
 hipError_t launch_lookup_kind(const LookupArgs& a, hipStream_t stream) {
   const int N = a.B * a.Hkv;
   if (N <= kOneBlockGroups) {
-    timing_begin(stream);
-    lookup_one_block_kernel<KIND, P><<<1, kScanThreads, 0, stream>>>(a);
-    timing_end(stream);
+    launch_timed(lookup_one_block_kernel<KIND, P>, dim3(1), dim3(kScanThreads), 0u, stream, a);
     return hipGetLastError();
   }
-  timing_begin(stream);
-  lookup_grid_kernel<KIND, P><<<(N + 3) / 4, 256, 0, stream>>>(a);
-  timing_end(stream);
+  launch_timed(lookup_grid_kernel<KIND, P>, dim3((N + 3) / 4), dim3(256), 0u, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.miss_list) return e;
   compact_kernel<<<1, kScanThreads, 0, stream>>>(a.hit, N, a.miss_list, a.miss_count);
@@ -337,17 +333,15 @@ void launch_qproj_kind(const QProjArgs& a, hipStream_t stream) {
   int R = (a.N + groups - 1) / groups;
   R = R < 1 ? 1 : (R > kQMaxR ? kQMaxR : R);
   const unsigned blocks = (unsigned)((a.N + R - 1) / R);
-  if (wide) qproj_kernel<KIND, 16><<<blocks, 16 * 64, 0, stream>>>(a, R);
-  else qproj_kernel<KIND, 8><<<blocks, 8 * 64, 0, stream>>>(a, R);
+  if (wide) launch_timed(qproj_kernel<KIND, 16>, dim3(blocks), dim3(16 * 64), 0u, stream, a, R);
+  else launch_timed(qproj_kernel<KIND, 8>, dim3(blocks), dim3(8 * 64), 0u, stream, a, R);
 }
 
 }  // namespace
 
 hipError_t launch_qproj(const QProjArgs& a, hipStream_t stream) {
-  timing_begin(stream);
   if (a.dtype == KIND_F16) launch_qproj_kind<KIND_F16>(a, stream);
   else launch_qproj_kind<KIND_BF16>(a, stream);
-  timing_end(stream);
   return hipGetLastError();
 }
 

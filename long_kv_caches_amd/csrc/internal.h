@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include "kvdec.h"
 
@@ -93,10 +94,21 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
-// Profiling events around the main kernel launch of a call (no-ops unless
-// kvdec_kernel_timing is enabled on the calling thread).
-void timing_begin(hipStream_t stream);
-void timing_end(hipStream_t stream);
+// Profiling events of the next main-kernel launch of a call: a start/stop
+// pair from the calling thread's pool when kvdec_kernel_timing is enabled on
+// it, else two nulls.
+void timing_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches a call's main kernel.  With timing enabled, HIP stamps the events
+// from the kernel's own dispatch (its start and its end), so they add no
+// packets to the stream and read the kernel's execution time.
+template <typename... KArgs, typename... Args>
+inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds,
+                         hipStream_t stream, const Args&... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  timing_events(&e0, &e1);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, e0, e1, 0u, args...);
+}
 
 struct LookupArgs {
   const uint16_t* q;

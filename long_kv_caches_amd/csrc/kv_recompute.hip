@@ -457,15 +457,13 @@ constexpr int64_t kWideMinBlocks = 256;
 hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
   const int M = a.b * a.l, N = 2 * a.h;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
-  timing_begin(stream);
   const int64_t wide_blocks = (int64_t)((M + WT - 1) / WT) * (N / WT);
   if (a.w_layout == KVDEC_W_OUT_IN && wide_blocks >= kWideMinBlocks)
-    kv_recompute_kernel_wide<<<(unsigned)wide_blocks, 256, 0, stream>>>(a);
+    launch_timed(kv_recompute_kernel_wide, dim3((unsigned)wide_blocks), dim3(256), 0u, stream, a);
   else if (a.w_layout == KVDEC_W_OUT_IN)
-    kv_recompute_kernel_k64<<<(unsigned)blocks, 256, 0, stream>>>(a);
+    launch_timed(kv_recompute_kernel_k64, dim3((unsigned)blocks), dim3(256), 0u, stream, a);
   else
-    kv_recompute_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
-  timing_end(stream);
+    launch_timed(kv_recompute_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, a);
   return hipGetLastError();
 }
 

@@ -284,16 +284,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const int pairs = a.B * a.Hkv;
   if (a.S > 0) {  // with no rows every selection is empty: only the counts are written
     const dim3 sgrid((unsigned)((a.S + 4 * kTile - 1) / (4 * kTile)), (unsigned)pairs);
-    timing_begin(stream);
-    if (a.dtype == KIND_F16) topk_score_kernel<KIND_F16><<<sgrid, 256, 0, stream>>>(a);
-    else topk_score_kernel<KIND_BF16><<<sgrid, 256, 0, stream>>>(a);
-    timing_end(stream);
+    if (a.dtype == KIND_F16) launch_timed(topk_score_kernel<KIND_F16>, sgrid, dim3(256), 0u, stream, a);
+    else launch_timed(topk_score_kernel<KIND_BF16>, sgrid, dim3(256), 0u, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  timing_begin(stream);
-  topk_select_kernel<<<(unsigned)pairs, kSelThreads, 0, stream>>>(a);
-  timing_end(stream);
+  launch_timed(topk_select_kernel, dim3((unsigned)pairs), dim3(kSelThreads), 0u, stream, a);
   return hipGetLastError();
 }
 
