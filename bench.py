@@ -9,8 +9,11 @@ in-workgroup merge and the split-K merge into the fp16 output and lse.
 
 Prints ONE JSON line.  `value` is achieved HBM throughput (algorithmic bytes /
 time per step, TB/s) with inputs resident in HBM; `roofline` prices the same
-bytes against the 8 TB/s HBM3E peak; `cpu_baseline` times the fp64 CPU oracle
-on the same workload.
+bytes against the 8 TB/s HBM3E peak (and, as `frac_of_stream_read`, against
+`stream_read`: the HBM read rate of the library's streaming-read reference
+kernel on the same box); `isolated_call` times single calls with L2 and the
+MALL flushed before each (p10 / p50 / p90); `cpu_baseline` times the fp64 CPU
+oracle on the same workload.
 
 Other workloads (one JSON line each, same fields): --workload llama2-7b-paged
 (batch-1024 paged MHA), clo-llama3-8b-128k / clo-qwen2.5-14b-128k (CLO hybrid
@@ -20,6 +23,7 @@ merged cache).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload W]
                        [--split-tokens N] [--calibrate-copy] [--no-cpu-baseline]
+                       [--no-stream-read]
 """
 from __future__ import annotations
 
@@ -112,6 +116,51 @@ def time_steps(step, steps, warmup, stream, K, torch, prewarm_ms=0.0):
     return ms, kern_ms_total * 1e3 / max(launches, 1), launches
 
 
+def isolated_calls(step, stream, torch, dev, amount, unit, reps=50, flush_bytes=1 << 30):
+    """Per-call times with the caches cold: before each call (outside its event
+    pair) a 1 GiB buffer is written on the same stream, which evicts L2 and the
+    256 MB MALL.  Returns p10 / p50 / p90 in us and the rate at the median
+    (`amount` per call in `unit`: bytes -> TB/s, FLOPs -> TFLOP/s)."""
+    import numpy as np
+    flush = torch.empty(flush_bytes // 4, dtype=torch.int32, device=dev)
+    times = []
+    for r in range(reps):
+        flush.fill_(r)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    p10, p50, p90 = (float(x) for x in np.percentile(times, [10, 50, 90]))
+    rate = amount / (p50 * 1e-6) / 1e12
+    return {"reps": reps, "flush_bytes_before_each": flush_bytes, "us_p10": round(p10, 2),
+            "us_p50": round(p50, 2), "us_p90": round(p90, 2),
+            ("tbs_at_p50" if unit == "bytes" else "tflops_at_p50"): round(rate, 4)}
+
+
+def stream_read_reference(K, torch, dev, stream, nbytes=2 << 30, reps=20):
+    """The library's streaming-read reference kernel over a 2 GiB buffer (larger
+    than L2 and the MALL): the HBM read rate one kernel reaches on this machine,
+    by its kernel events."""
+    buf = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        K.kvdec_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    K.kvdec_kernel_timing(True)
+    for _ in range(reps):
+        K.kvdec_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    ms, n = K.kvdec_kernel_timing_read()
+    K.kvdec_kernel_timing(False)
+    del buf
+    return {"kernel": "stream_read_kernel", "bytes": nbytes, "launches": n,
+            "tbs": round(nbytes / (ms / max(n, 1) * 1e-3) / 1e12, 4)}
+
+
 def oracle_seconds(fn, reps=3):
     times = []
     for _ in range(reps):
@@ -187,6 +236,7 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
                                  step_bytes, kern_us,
                                  measured_traffic(step_bytes, TRAFFIC_FILE_FP8 if fp8 else TRAFFIC_FILE))
     r["roofline"]["launches_timed"] = launches
+    r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
     if not args.no_cpu_baseline:
         import oracle
         if fp8:  # a bounded sample: the first 4 sequences
@@ -247,6 +297,7 @@ def bench_paged(args, K, np, torch, dev, stream):
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
                                  step_bytes, kern_us)
     r["roofline"]["launches_timed"] = launches
+    r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes", reps=20)
     if not args.no_cpu_baseline:
         import oracle
         n = 64  # a bounded sample: the first 64 sequences
@@ -300,6 +351,7 @@ def bench_clo(args, K, np, torch, dev, stream, model):
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
                                  step_bytes, kern_us)
     r["roofline"]["launches_timed"] = launches
+    r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
 
     # the fused head-cache lookup on the same queries (launch-bound at this size)
     tau = K.kvdec_headcache_thresholds(kvgen.group_importance(d["s"], Hkv).astype(np.float32),
@@ -361,9 +413,12 @@ def bench_clo(args, K, np, torch, dev, stream, model):
 
 def bench_gather(args, K, np, torch, dev, stream):
     """Index-gather sparse attention over a full 128K cache: the exact top-k
-    selection (10% per KV head) and the attention over the selected rows."""
+    selection (10% per KV head) and the attention over the selected rows.
+    Batch 8, so that the selected rows (about 430 MB) do not fit in the 256 MB
+    MALL from one step to the next (at batch 4, 215 MB, steps ran 13% faster
+    than single calls with the caches flushed)."""
     import kvgen
-    d = kvgen.clo_gather(seed=args.seed)
+    d = kvgen.clo_gather(seed=args.seed, B=8)
     B, Hq, Hkv, D, S, top_k = d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["top_k"]
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     q, k, v, sl = to(d["q"]), to(d["k"]), to(d["v"]), to(d["seqlens"])
@@ -388,7 +443,7 @@ def bench_gather(args, K, np, torch, dev, stream):
     ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch, args.prewarm_ms)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     r = common(args, "clo-gather-llama3-8b-128k-sparse-attention",
-               "index-gather sparse attn achieved HBM TB/s (top-10% rows of a full 128K cache), Llama3-8B batch 4",
+               "index-gather sparse attn achieved HBM TB/s (top-10% rows of a full 128K cache), Llama3-8B batch 8",
                "TB/s", round(gbs / 1e3, 4), ms, "f16",
                "synthetic (seeded; full dense cache, lengths uniform in [64K, 128K], selection = exact top-k of the summed group scores)",
                {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "cache_rows": S,
@@ -398,6 +453,7 @@ def bench_gather(args, K, np, torch, dev, stream):
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
                                  step_bytes, kern_us)
     r["roofline"]["launches_timed"] = launches
+    r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
 
     def select():
         K.kvdec_topk_select(td, q, k, sl, idx, n, tws, stream=stream)
@@ -455,6 +511,7 @@ def bench_kvpr(args, K, np, torch, dev, stream):
     r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel_wide", "achieved": round(kern_tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
                      "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
+    r["isolated_call"] = isolated_calls(step, stream, torch, dev, flops, "flops", reps=20)
     io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)
     r["w_in_out"] = {"ms_per_step": round(io_ms, 4), "tflops": round(flops / (io_ms * 1e-3) / 1e12, 2),
                      "kernel_us": round(io_kern_us, 2),
@@ -594,6 +651,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read reference (HBM read rate of one kernel on this box)")
     ap.add_argument("--prewarm-ms", type=float, default=200.0,
                     help="device copies before the warmup steps, to bring the unlocked clocks up")
     args = ap.parse_args()
@@ -624,6 +683,10 @@ def main():
         r = bench_kvpr_overlap(args, K, np, torch, dev, stream)
     else:
         r = bench_kvpr(args, K, np, torch, dev, stream)
+    if r["roofline"]["bound"] == "hbm" and not args.no_stream_read:
+        ref = stream_read_reference(K, torch, dev, stream)
+        r["stream_read"] = ref
+        r["roofline"]["frac_of_stream_read"] = round(r["roofline"]["achieved"] / (ref["tbs"] * 1e3), 4)
     print(json.dumps(r), flush=True)
 
 

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 6
+#define KVDEC_ABI_VERSION 7
 
 typedef enum {
   KVDEC_OK = 0,
@@ -372,6 +372,17 @@ kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_
  * recorded stops further recording and is reported here as KVDEC_ERR_HIP. */
 kvdec_status kvdec_kernel_timing(int enable);
 kvdec_status kvdec_kernel_timing_read(double* total_ms, int64_t* launches);
+
+/* Streaming-read reference, a measurement aid (no part of the method).
+ * Reads `bytes` bytes at device pointer `src` once, with 16-byte loads, and
+ * may write one uint32 at device pointer `sink` (a value that depends on all
+ * the words read; the write happens only for one value of it).  Its rate on a
+ * buffer larger than the caches (L2, 256 MB MALL) is the HBM read bandwidth
+ * one kernel reaches on this GPU, the second denominator reported beside the
+ * published peak.  bytes > 0 and a multiple of 16; src 16-byte aligned; both
+ * pointers non-NULL.  Asynchronous on `stream`; it is a main kernel for
+ * kvdec_kernel_timing.  KVDEC_ERR_INVALID on bad arguments (nothing launched). */
+kvdec_status kvdec_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 const char* kvdec_status_string(kvdec_status status);
 const char* kvdec_last_error(void);

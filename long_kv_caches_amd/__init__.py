@@ -14,5 +14,5 @@ from ._lib import (  # noqa: F401
     kvdec_kvpr_split, kvdec_sparse_hybrid_attn,
     kvdec_sparse_hybrid_attn_workspace, last_error, status_string,
     GatherDesc, TopkDesc, gather_desc, topk_desc, kvdec_gather_attn, kvdec_gather_attn_workspace,
-    kvdec_topk_select, kvdec_topk_select_workspace,
+    kvdec_topk_select, kvdec_topk_select_workspace, kvdec_stream_read,
 )

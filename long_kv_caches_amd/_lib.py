@@ -82,6 +82,7 @@ def _load():
         "kvdec_kvpr_load_layer": ([i32, i32, i32, i32, i32, i32, P, i64, P, P, P, i64, P, P, i32, P,
                                    P, i64, P, P], st),
         "kvdec_kernel_timing": ([ctypes.c_int], st),
+        "kvdec_stream_read": ([P, sz, P, P], st),
         "kvdec_kernel_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
         "kvdec_status_string": ([st], ctypes.c_char_p),
         "kvdec_last_error": ([], ctypes.c_char_p),
@@ -101,7 +102,7 @@ EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hy
             "kvdec_topk_select",
             "kvdec_headcache_thresholds",
             "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
-            "kvdec_kernel_timing_read", "kvdec_status_string",
+            "kvdec_kernel_timing_read", "kvdec_stream_read", "kvdec_status_string",
             "kvdec_last_error", "kvdec_abi_version")
 
 
@@ -244,6 +245,14 @@ def kvdec_kernel_timing_read():
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(lib.kvdec_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def kvdec_stream_read(src, sink, stream=None) -> None:
+    """Reads all of device tensor `src` once (the streaming-read reference); may
+    write one uint32 into device tensor `sink` (at least 4 bytes)."""
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink needs at least 4 bytes")
+    _check(lib.kvdec_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

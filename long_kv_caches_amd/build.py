@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvdec.so")
 
-SOURCES = ["api.cpp", "decode_attn.hip", "headcache.hip", "kv_recompute.hip", "topk.hip"]
+SOURCES = ["api.cpp", "decode_attn.hip", "headcache.hip", "kv_recompute.hip", "topk.hip",
+           "stream_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -313,6 +313,13 @@ kvdec_status kvdec_kernel_timing(int enable) {
   return ok();
 }
 
+kvdec_status kvdec_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(KVDEC_ERR_INVALID, "src and sink must be non-NULL");
+  if (bytes == 0 || bytes % 16 != 0) return fail(KVDEC_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(KVDEC_ERR_INVALID, "src must be 16-byte aligned");
+  return hip_status(launch_stream_read(src, bytes, sink, stream), "stream read launch");
+}
+
 kvdec_status kvdec_kernel_timing_read(double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return fail(KVDEC_ERR_INVALID, "total_ms and launches must be non-NULL");
   TimingState& t = g_timing;

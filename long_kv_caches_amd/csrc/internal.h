@@ -94,6 +94,8 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Profiling events of the next main-kernel launch of a call: a start/stop
 // pair from the calling thread's pool when kvdec_kernel_timing is enabled on
 // it, else two nulls.

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 6
+    assert _lib.lib.kvdec_abi_version() == 7
 
 
 def test_status_strings():
@@ -281,3 +281,16 @@ def test_gather_and_topk_validation():
     assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 2
     td.max_seqlen, td.top_k = 100, -1
     assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 1
+
+
+@pytest.mark.parametrize("src,nbytes,sink,needle", [
+    (None, 1024, FAKE, "non-NULL"),
+    (FAKE, 1024, None, "non-NULL"),
+    (FAKE, 0, FAKE, "multiple of 16"),
+    (FAKE, 1000, FAKE, "multiple of 16"),
+    (ctypes.c_void_p(0x10008), 1024, FAKE, "aligned"),
+])
+def test_stream_read_validation(src, nbytes, sink, needle):
+    st = _lib.lib.kvdec_stream_read(src, nbytes, sink, None)
+    assert st == K._lib.KVDEC_ERR_INVALID
+    assert needle in K.last_error()
