@@ -282,10 +282,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // data, with the clock at 1.6-1.7 GHz under this load; 2600 cycles per
 // 64-wide K step against a 2048-cycle MFMA floor.
 constexpr int WT = 256;                  // tile rows and columns
-constexpr int WS = 64 + 8;               // LDS row stride (bf16 elements)
-constexpr int WBUF = 2 * WT * WS;        // one buffer: X rows then W rows
+constexpr int WS = 64 + 8;               // LDS row stride of K-contiguous rows (bf16 elements)
+constexpr int WP = WT + 16;              // LDS row stride of [in, out] W rows (N-contiguous)
+constexpr int WBUF = 2 * WT * WS;        // one buffer: X rows, then W rows in either layout
 constexpr int WLOADS = 2 * WT * 8 / 256; // 16-byte pieces per thread per step (8 X, 8 W)
 constexpr int WES = 128 + 8;             // epilogue row stride (fp16 elements)
+static_assert(WT * WS + 64 * WP <= WBUF, "an [in, out] W step fits in a buffer");
 static_assert(4 * 128 * WES <= 2 * WBUF, "epilogue staging fits in the LDS buffers");
 
 template <int N>
@@ -307,11 +309,32 @@ __device__ __forceinline__ void sched_mfma_stage() {
   }
 }
 template <int N>
+__device__ __forceinline__ void sched_mfma_stage_tight() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+    sched_mfma_stage_tight<N - 1>();
+  }
+}
+template <int N>
 __device__ __forceinline__ void sched_mfma() {
   if constexpr (N > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     sched_mfma<N - 1>();
   }
+}
+
+// gfx950 LDS transpose read of 16-bit data.  In each group of 16 lanes, lane j
+// gets, as its element i, element j % 4 of the 8 bytes addressed by lane
+// 4 * i + j / 4 of the group (checked with an in-bounds probe on MI355X).  So
+// with lane s of a group pointing at row k0 + s / 4, columns n0 + 4 * (s % 4)
+// of an N-contiguous tile, lane j receives rows k0 .. k0 + 3 of column n0 + j:
+// four consecutive k of one column, as a K-contiguous MFMA operand wants.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+  typedef __attribute__((address_space(3))) bf16x4_t* lds_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_ptr)(const_cast<uint16_t*>(p))));
 }
 
 // Tile order: each XCD (workgroups are dealt to the 8 XCDs round robin) takes
@@ -326,7 +349,14 @@ __device__ __forceinline__ void wide_tile(int blk, int tiles_m, int tiles_n, int
   tn = cb + in % w;
 }
 
+// 256 x 256 tiles for large grids, both W layouts.  [out, in] W rows are
+// K-contiguous and are staged like X rows.  [in, out] W is staged as it lies,
+// 64 rows (one K step) of 256 contiguous outputs, and each B fragment is two
+// transpose reads of it (4 consecutive k each).
+template <int WL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void kv_recompute_kernel_wide(RecomputeArgs a) {
+  constexpr bool kInOut = WL == KVDEC_W_IN_OUT;
+  constexpr int kBReads = kInOut ? 8 : 4;  // LDS reads of one slice's B fragments
   __shared__ __attribute__((aligned(16))) uint16_t S[2 * WBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = a.b * a.l;
@@ -337,21 +367,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* W = is_v ? a.wv : a.wk;
   const int wn0 = is_v ? n0 - a.h : n0;
 
-  // Thread -> 16-byte piece ak of tile rows ar + 32 i; X rows past M re-read row M - 1.
+  // X: thread -> 16-byte piece ak of tile rows ar + 32 i (rows past M re-read
+  // row M - 1).  W [out, in]: the same for W rows (outputs) wn0 + ar + 32 i.
+  // W [in, out]: piece wc of rows (inputs) wr + 8 i of the step.
   const int ar = tid >> 3, ak = (tid & 7) * 8;
+  const int wr = tid >> 5, wc = (tid & 31) * 8;
   const uint16_t* src[WLOADS];
 #pragma unroll
   for (int i = 0; i < WLOADS / 2; ++i) {
     const int r = min(m0 + ar + 32 * i, M - 1);
     const int bi = r / a.l, t = r - bi * a.l;
     src[i] = a.x + (int64_t)bi * a.x_bstride + (int64_t)t * a.h + ak;
-    src[WLOADS / 2 + i] = W + (int64_t)(wn0 + ar + 32 * i) * a.h + ak;
+    src[WLOADS / 2 + i] = kInOut ? W + (int64_t)(wr + 8 * i) * a.h + wn0 + wc
+                                 : W + (int64_t)(wn0 + ar + 32 * i) * a.h + ak;
   }
-  auto dst = [&](int i) { return (i < WLOADS / 2 ? ar + 32 * i : WT + ar + 32 * (i - WLOADS / 2)) * WS + ak; };
+  // element offset of step k0 for piece i
+  auto koff = [&](int i, int k0) -> int64_t { return kInOut && i >= WLOADS / 2 ? (int64_t)k0 * a.h : k0; };
+  auto dst = [&](int i) {
+    if (i < WLOADS / 2) return (ar + 32 * i) * WS + ak;
+    return kInOut ? WT * WS + (wr + 8 * (i - WLOADS / 2)) * WP + wc : (WT + ar + 32 * (i - WLOADS / 2)) * WS + ak;
+  };
 
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int fa_off = (wm + (lane & 31)) * WS + 8 * (lane >> 5);
-  const int fb_off = (WT + wn + (lane & 31)) * WS + 8 * (lane >> 5);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int fb_off = kInOut ? WT * WS + (8 * (g16 >> 1) + (s16 >> 2)) * WP + wn + 16 * (g16 & 1) + 4 * (s16 & 3)
+                            : (WT + wn + (lane & 31)) * WS + 8 * (lane >> 5);
+  // A fragment i and B fragment j of K slice ks (16 k) from buffer `buf`.
+  auto frag_a = [&](const uint16_t* buf, int ks, int i) {
+    return *reinterpret_cast<const u32x4*>(&buf[fa_off + 32 * i * WS + 16 * ks]);
+  };
+  auto frag_b = [&](const uint16_t* buf, int ks, int j) {
+    if constexpr (kInOut) {
+      const uint16_t* p = buf + fb_off + 16 * ks * WP + 32 * j;
+      const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * WP);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      return *reinterpret_cast<const u32x4*>(&buf[fb_off + 32 * j * WS + 16 * ks]);
+    }
+  };
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -367,13 +421,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int i = 0; i < WLOADS; ++i) store_b128(&S[dst(i)], st[i]);
 #pragma unroll
-  for (int i = 0; i < WLOADS; ++i) st[i] = load_b128(src[i] + 64);
+  for (int i = 0; i < WLOADS; ++i) st[i] = load_b128(src[i] + koff(i, 64));
   __syncthreads();
   u32x4 fa[2][4], fb[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[0][i] = *reinterpret_cast<const u32x4*>(&S[fa_off + 32 * i * WS]);
-    fb[0][i] = *reinterpret_cast<const u32x4*>(&S[fb_off + 32 * i * WS]);
+    fa[0][i] = frag_a(S, 0, i);
+    fb[0][i] = frag_b(S, 0, i);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const uint16_t* cur = S + (kt & 1) * WBUF;
@@ -385,23 +439,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (ks < 3) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[c ^ 1][i] = *reinterpret_cast<const u32x4*>(&cur[fa_off + 32 * i * WS + 16 * (ks + 1)]);
-          fb[c ^ 1][i] = *reinterpret_cast<const u32x4*>(&cur[fb_off + 32 * i * WS + 16 * (ks + 1)]);
+          fa[c ^ 1][i] = frag_a(cur, ks + 1, i);
+          fb[c ^ 1][i] = frag_b(cur, ks + 1, i);
         }
       }
 #pragma unroll
       for (int p = 0; p < WLOADS / 4; ++p) {
         const int i = ks * (WLOADS / 4) + p;
         store_b128(&nxt[dst(i)], st[i]);
-        st[i] = load_b128(src[i] + k2);
+        st[i] = load_b128(src[i] + koff(i, k2));
       }
       if (ks == 3) {
         // every wave's writes of nxt are done and its reads of cur issued
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[0][i] = *reinterpret_cast<const u32x4*>(&nxt[fa_off + 32 * i * WS]);
-          fb[0][i] = *reinterpret_cast<const u32x4*>(&nxt[fb_off + 32 * i * WS]);
+          fa[0][i] = frag_a(nxt, 0, i);
+          fb[0][i] = frag_b(nxt, 0, i);
         }
       }
 #pragma unroll
@@ -411,12 +465,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[c][i]), __builtin_bit_cast(bf16x8, fb[c][j]), acc[i][j], 0, 0, 0);
       if (ks < 3) {
-        sched_mfma_lds_read<8>();
-        sched_mfma_stage<WLOADS / 4>();
-        sched_mfma<16 - 8 - 2 * (WLOADS / 4)>();
+        if constexpr (kInOut) {
+          sched_mfma_lds_read<4 + kBReads>();
+          sched_mfma_stage_tight<WLOADS / 4>();
+        } else {
+          sched_mfma_lds_read<4 + kBReads>();
+          sched_mfma_stage<WLOADS / 4>();
+        }
       } else {
-        sched_mfma_lds_read<8>();
-        sched_mfma<8>();
+        sched_mfma_lds_read<4 + kBReads>();
+        sched_mfma<16 - 4 - kBReads>();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -458,9 +516,12 @@ hipError_t launch_kv_recompute(const RecomputeArgs& a, hipStream_t stream) {
   const int M = a.b * a.l, N = 2 * a.h;
   const int64_t blocks = (int64_t)((M + BM - 1) / BM) * (N / BN);
   const int64_t wide_blocks = (int64_t)((M + WT - 1) / WT) * (N / WT);
-  if (a.w_layout == KVDEC_W_OUT_IN && wide_blocks >= kWideMinBlocks)
-    launch_timed(kv_recompute_kernel_wide, dim3((unsigned)wide_blocks), dim3(256), 0u, stream, a);
-  else if (a.w_layout == KVDEC_W_OUT_IN)
+  if (wide_blocks >= kWideMinBlocks) {
+    if (a.w_layout == KVDEC_W_OUT_IN)
+      launch_timed(kv_recompute_kernel_wide<KVDEC_W_OUT_IN>, dim3((unsigned)wide_blocks), dim3(256), 0u, stream, a);
+    else
+      launch_timed(kv_recompute_kernel_wide<KVDEC_W_IN_OUT>, dim3((unsigned)wide_blocks), dim3(256), 0u, stream, a);
+  } else if (a.w_layout == KVDEC_W_OUT_IN)
     launch_timed(kv_recompute_kernel_k64, dim3((unsigned)blocks), dim3(256), 0u, stream, a);
   else
     launch_timed(kv_recompute_kernel, dim3((unsigned)blocks), dim3(256), 0u, stream, a);
