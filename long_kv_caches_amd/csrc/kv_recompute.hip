@@ -9,19 +9,22 @@
 // fp16 and writes row (batch i, token t) straight into k_cache / v_cache
 // [b, s_cap, H, 128] at rows t < l (every other byte untouched).
 //
-// Tiling: a 256-thread workgroup computes a 256 x 128 tile of C; its four
-// waves each own a 128 x 64 quarter as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks
-// (accumulators in VGPRs, two waves per SIMD), so each 16-wide k slice issues
-// 8 MFMAs per wave against 6 LDS operand reads.  X rows are K-contiguous.  W
-// stored [out, in] (as a torch.nn.Linear weight) is K-contiguous too and is
-// staged exactly like X, in 64-wide K steps.  W stored [in, out] is
-// N-contiguous: each thread transposes a 4 x 4 block of it in registers (byte
-// permutes) before storing it K-contiguous in LDS, in 32-wide K steps with
-// loads two steps ahead and double-buffered LDS.  The transposed 8-byte
-// stores put rows 4 apart on the same LDS banks (measured on MI355X: that
-// kernel runs at about 40% of the MFMA rate with no global loads at all, 85%
-// with no LDS operand traffic), which is why the [out, in] layout is the
-// fast one.
+// Three kernels:
+//   kv_recompute_kernel_wide<layout>: grids of at least 256 tiles of 256 x 256
+//     (one workgroup per CU, four 128 x 128 waves, a hand-pipelined loop);
+//     either W layout, [in, out] through LDS transpose reads.
+//   kv_recompute_kernel_k64 / kv_recompute_kernel: smaller grids, 256 x 128
+//     tiles (two workgroups per CU), W [out, in] / W [in, out].
+// In the 256 x 128 kernels a 256-thread workgroup's four waves each own a
+// 128 x 64 quarter as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (accumulators in
+// VGPRs, two waves per SIMD).  X rows are K-contiguous.  W stored [out, in]
+// (as a torch.nn.Linear weight) is K-contiguous too and is staged exactly like
+// X, in 64-wide K steps.  W stored [in, out] is N-contiguous: there each thread
+// transposes a 4 x 4 block of it in registers (byte permutes) before storing
+// it K-contiguous in LDS, in 32-wide K steps with loads two steps ahead and
+// double-buffered LDS.  Its transposed 8-byte stores put rows 4 apart on the
+// same LDS banks (measured on MI355X: that kernel runs at about 40% of the
+// MFMA rate with no global loads at all, 85% with no LDS operand traffic).
 #include "device_common.h"
 #include "internal.h"
 
