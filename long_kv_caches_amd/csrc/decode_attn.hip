@@ -72,11 +72,17 @@ constexpr int kKvBytes = kKv8<KIND> ? 1 : 2;  // bytes per K/V element
 template <int KIND>
 using KvPiece = std::conditional_t<kKv8<KIND>, u32x2, u32x4>;
 
-// e4m3 K/V with three or more query heads per KV head take the matrix-core
-// tile path (below); one or two heads keep the VALU path, whose per-tile work
-// is small there and which holds more waves per SIMD.
+// The matrix-core tile path (below) takes e4m3 or fp16 K/V with three or more
+// query heads per KV head; one or two heads keep the VALU path, whose per-tile
+// work is small there and which holds more waves per SIMD.  (Measured on
+// MI355X on the 16 x 16K-32K fp16 batch: 241-242 vs 250-252 us at G = 4, 241
+// vs 246 at G = 3, 246 vs 440 at G = 8.)  bf16 K/V keep the VALU path at every
+// G: the P.V product of the matrix-core path rounds each softmax weight to the
+// MFMA's input type, and bf16's 2^-9 relative rounding is too coarse for the
+// output tolerance on short sequences (fp16's 2^-12 is not).
+constexpr int kMfma16MinG = 3;
 template <int KIND, int G>
-constexpr bool kUsesMfma = kKv8<KIND> && G >= 3;
+constexpr bool kUsesMfma = kKv8<KIND> ? G >= 3 : (kQKind<KIND> == KIND_F16 && G >= kMfma16MinG);
 
 // Address of K/V element `elems` of a tensor starting at base.
 template <int KIND>
@@ -601,21 +607,26 @@ struct MState {
 
 template <int KIND, int G>
 struct MfmaPath {
-  static_assert(kKv8<KIND> && G <= 8, "matrix-core path: e4m3 K/V, at most 8 heads");
+  static_assert((kKv8<KIND> || kQKind<KIND> == KIND_F16) && G <= 8,
+                "matrix-core path: e4m3 or fp16 K/V, at most 8 heads");
   // Registers: 126 VGPRs + 32 AGPRs (the accumulators), three waves per SIMD;
   // capping it at four waves spills.
   using Q = u32x4[4];
   using State = MState;
   // K and V are both loaded as the VALU path loads them: lane l takes the
-  // 8-byte piece l % 16 of rows 4*(l/16) + i, so each load instruction reads
-  // four whole 128-byte rows.  (The score MFMA wants row l % 16 in lane l:
-  // loading K that way touches 16 rows per instruction, half of each, and
-  // streamed about 9% slower on MI355X.)  K then goes through a small LDS
-  // slice of the wave to reach the MFMA layout.
+  // piece l % 16 (8 elements: 8 bytes of e4m3, 16 of fp16) of rows
+  // 4*(l/16) + i, so each load instruction reads four whole rows.  (The score
+  // MFMA wants row l % 16 in lane l: loading K that way touches 16 rows per
+  // instruction, part of each, and streamed about 9-12% slower on MI355X.)  K
+  // then goes through a small LDS slice of the wave to reach the MFMA layout.
   struct Tile {
-    u32x2 k[4];  // rows 4*(l/16) + i, 8 codes each
-    u32x2 v[4];
+    KvPiece<KIND> k[4];  // rows 4*(l/16) + i, 8 elements each
+    KvPiece<KIND> v[4];
   };
+  __device__ static KvPiece<KIND> load_piece(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (kKv8<KIND>) return buffer_load_b64_nt(r, off);
+    else return buffer_load_b128_nt(r, off);
+  }
   struct Offs {
     uint32_t row[4];  // this lane's pieces within a tile
   };
@@ -642,9 +653,9 @@ struct MfmaPath {
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, uniform_u32((uint32_t)a.S * row_bytes));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t off = gather_offset(a, vt[i], 4 * grp + i < rows, row_bytes, 8 * n);
-        t.k[i] = buffer_load_b64_nt(rk, off);
-        t.v[i] = buffer_load_b64_nt(rv, off);
+        const uint32_t off = gather_offset(a, vt[i], 4 * grp + i < rows, row_bytes, 8 * kKvBytes<KIND> * n);
+        t.k[i] = load_piece(rk, off);
+        t.v[i] = load_piece(rv, off);
       }
       return;
     }
@@ -652,7 +663,7 @@ struct MfmaPath {
     if constexpr (SRC == SRC_PAGED) {
       int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
       pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));
-      row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim;
+      row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim * kKvBytes<KIND>;
     } else {
       row0 = (int64_t)t0 * row_bytes;
     }
@@ -660,31 +671,40 @@ struct MfmaPath {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = buffer_load_b64_nt(rk, o.row[i]);
+    for (int i = 0; i < 4; ++i) t.k[i] = load_piece(rk, o.row[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load_b64_nt(rv, o.row[i]);
+    for (int i = 0; i < 4; ++i) t.v[i] = load_piece(rv, o.row[i]);
   }
   __device__ static void process(const AttnArgs& a, const Q& q, const Tile& t, int t0, int len,
                                  int lane, State& st) {
     constexpr int QK = kQKind<KIND>;
     const int n = lane & 15, grp = lane >> 4;
-    // K through the wave's LDS slice: rows of 144 bytes (conflict-free for
-    // the 8-byte writes of whole rows and for the 16-byte reads of 8 rows at
-    // one offset); lane l reads codes 32*(l/16) .. +31 of row l % 16.
-    constexpr int kRowWords = 36;
+    // K through the wave's LDS slice: rows of 128 + 16 (e4m3) or 256 + 16
+    // (fp16) bytes, conflict-free for the writes of whole rows and for the
+    // 16-byte reads of 8 rows at one offset; lane l reads elements
+    // 32*(l/16) .. +31 of row l % 16.
+    constexpr int kPieceWords = 2 * kKvBytes<KIND>;                // one lane's piece
+    constexpr int kRowWords = 16 * kPieceWords + 4;
     __shared__ __attribute__((aligned(16))) uint32_t s_k[kWaves][kTile * kRowWords];
     uint32_t* kl = s_k[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(&kl[(4 * grp + i) * kRowWords + 2 * n]) = t.k[i];
-    const u32x4 kr[2] = {*reinterpret_cast<const u32x4*>(&kl[n * kRowWords + 8 * grp]),
-                         *reinterpret_cast<const u32x4*>(&kl[n * kRowWords + 8 * grp + 4])};
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<KvPiece<KIND>*>(&kl[(4 * grp + i) * kRowWords + kPieceWords * n]) = t.k[i];
+    constexpr int kRuns = 2 * kKvBytes<KIND>;  // 16-byte reads of a lane's 32 elements
+    u32x4 kr[kRuns];
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) kr[r] = *reinterpret_cast<const u32x4*>(&kl[n * kRowWords + 4 * kRuns * grp + 4 * r]);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w0 = kr[c >> 1][2 * (c & 1)], w1 = kr[c >> 1][2 * (c & 1) + 1];
-      const u32x4 kk = {e4m3_pair<QK>(w0, false), e4m3_pair<QK>(w0, true), e4m3_pair<QK>(w1, false),
-                        e4m3_pair<QK>(w1, true)};
-      s = mfma_scores<QK>(kk, q[c], s);
+      if constexpr (kKv8<KIND>) {
+        const uint32_t w0 = kr[c >> 1][2 * (c & 1)], w1 = kr[c >> 1][2 * (c & 1) + 1];
+        const u32x4 kk = {e4m3_pair<QK>(w0, false), e4m3_pair<QK>(w0, true), e4m3_pair<QK>(w1, false),
+                          e4m3_pair<QK>(w1, true)};
+        s = mfma_scores<QK>(kk, q[c], s);
+      } else {
+        s = mfma_scores<QK>(kr[c], q[c], s);  // fp16 elements 8c .. 8c+7 of the lane's run
+      }
     }
     float sc[4];
 #pragma unroll
@@ -709,6 +729,18 @@ struct MfmaPath {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.o[c][i] *= ai[i];
     }
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    if constexpr (!kKv8<KIND>) {
+      // fp16 V: for dim 8n + c, rows 0..3 are half c of the lane's 4 pieces
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        const u2 vb = {__builtin_amdgcn_perm(t.v[1][c >> 1], t.v[0][c >> 1], sel),
+                       __builtin_amdgcn_perm(t.v[3][c >> 1], t.v[2][c >> 1], sel)};
+        st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(h4, vb), st.o[c], 0, 0, 0);
+      }
+      return;
+    }
     // V codes of dim 8n + c for rows 0..3, one dword per c (byte i = row i)
     uint32_t col[8];
 #pragma unroll
@@ -725,7 +757,6 @@ struct MfmaPath {
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      typedef unsigned int u2 __attribute__((ext_vector_type(2)));
       const u2 vb = {e4m3_pair<KIND_F16>(col[c], false), e4m3_pair<KIND_F16>(col[c], true)};
       st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(h4, vb), st.o[c], 0, 0, 0);
     }

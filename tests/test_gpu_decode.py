@@ -41,18 +41,20 @@ def test_dense_small_config():
     _parity(d, "dense 1x8/2x1024", split_tokens=64)
 
 
-def test_single_key_returns_v_bit_exact():
+@pytest.mark.parametrize("hq", [8, 16])  # G = 4 (VALU tile path), G = 8 (matrix-core tile path)
+def test_single_key_returns_v_bit_exact(hq):
+    G = hq // 2
     for layout in ("dense", "ragged"):
-        d = kvgen.dense_small(seed=1, B=3, Hq=8, Hkv=2, S=1)
+        d = kvgen.dense_small(seed=1, B=3, Hq=hq, Hkv=2, S=1)
         if layout == "ragged":
             d = dict(d, layout="ragged", k=d["k"].reshape(3, 2, 128), v=d["v"].reshape(3, 2, 128),
                      cu_seqlens=np.arange(4, dtype=np.int32), seqlens=np.ones(3, np.int32))
-        say(f"[decode] single key {layout}")
+        say(f"[decode] single key {layout} G={G}")
         out, lse = decode_on_gpu(d)
         got = bits(out)
         v = d["v"].reshape(3, 2, 128).view(np.uint16)
-        for j in range(8):
-            assert np.array_equal(got[:, j], v[:, j // 4]), (layout, j)
+        for j in range(hq):
+            assert np.array_equal(got[:, j], v[:, j // G]), (layout, j)
 
 
 @pytest.mark.parametrize("split", [0, 64, 128, 512])
@@ -113,7 +115,7 @@ def test_paged_bitwise_equals_ragged():
     d = kvgen.ragged_llama(seed=8, lens=[16, 17, 1000, 2047, 5000], Hq=32, Hkv=8)
     p = kvgen.ragged_to_paged(d, seed=9)
     say("[decode] paged vs ragged bitwise")
-    for split in (64, 512):
+    for split in (0, 64, 512):
         out_r, lse_r = decode_on_gpu(d, split_tokens=split)
         out_p, lse_p = decode_on_gpu(p, split_tokens=split)
         assert np.array_equal(bits(out_r), bits(out_p))
@@ -130,6 +132,15 @@ def test_page_size_32():
     d = kvgen.ragged_llama(seed=11, lens=[31, 32, 33, 900], Hq=8, Hkv=8)
     p = kvgen.ragged_to_paged(d, seed=12, page=32)
     _parity(p, "paged page_size=32", split_tokens=128)
+
+
+@pytest.mark.parametrize("split", [0, 128])
+def test_paged_matrix_core_group(split):
+    """fp16 K/V with G = 8 take the matrix-core tile path; the paged source
+    addresses its tiles in bytes of the 16-bit elements."""
+    d = kvgen.ragged_llama(seed=14, lens=[33, 700, 16, 2100], Hq=64, Hkv=8)
+    p = kvgen.ragged_to_paged(d, seed=15, page=32)
+    _parity(p, "paged G=8 page_size=32", split_tokens=split)
 
 
 def test_headline_full_size():
