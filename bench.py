@@ -370,9 +370,12 @@ def bench_clo(args, K, np, torch, dev, stream, model):
     misses_first = int(mc.item())
     lms, lkern_us, _ = time_steps(lookup, args.steps, args.warmup, stream, K, torch)
     lbytes = B * Hq * D * 2 * 2 + Hq * 4 + Hkv * 4 + B * Hkv * 1 + 4
+    events_note = ("kernel_us from HIP events stamped from the kernel's dispatch; for a kernel of a few us, "
+                   "issued one call at a time, they include the dispatch latency (the rocprofv3 kernel "
+                   "traces give the kernel's own duration)")
     r["lookup"] = {"us_per_call": round(lms * 1e3, 2), "kernel_us": round(lkern_us, 2),
                    "bytes": lbytes, "misses_on_first_call": misses_first, "groups": B * Hkv,
-                   "achieved_gbs": round(lbytes / (lkern_us * 1e-6) / 1e9, 1)}
+                   "achieved_gbs": round(lbytes / (lkern_us * 1e-6) / 1e9, 1), "note": events_note}
     # the same lookup one layer ahead: q_approx = x_{l-1} W_Q^l (GEMV over the
     # next layer's W_Q), then the lookup on it
     a = kvgen.clo_ahead(seed=args.seed, model=model, B=B)
@@ -396,7 +399,8 @@ def bench_clo(args, K, np, torch, dev, stream, model):
     r["lookup_ahead"] = {"us_per_call": round(ams * 1e3, 2), "hidden": a["h"], "w_q_layers_cycled": len(w_layers),
                          "w_q_bytes": a["w_q"].nbytes, "projection_kernel_us": round(proj_us, 2),
                          "projection_achieved_gbs": round(pbytes / (proj_us * 1e-6) / 1e9, 1),
-                         "projection_frac_of_hbm_peak": round(pbytes / (proj_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "projection_frac_of_hbm_peak": round(pbytes / (proj_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": events_note}
     if not args.no_cpu_baseline:
         import oracle
         sub_rows = sum(int(d["pers_len"][0]) if hmn[g] >= 0 else int(d["buf_len"][g]) for g in range(Hkv))
