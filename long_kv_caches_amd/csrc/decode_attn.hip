@@ -72,17 +72,14 @@ constexpr int kKvBytes = kKv8<KIND> ? 1 : 2;  // bytes per K/V element
 template <int KIND>
 using KvPiece = std::conditional_t<kKv8<KIND>, u32x2, u32x4>;
 
-// The matrix-core tile path (below) takes e4m3 or fp16 K/V with three or more
-// query heads per KV head; one or two heads keep the VALU path, whose per-tile
-// work is small there and which holds more waves per SIMD.  (Measured on
-// MI355X on the 16 x 16K-32K fp16 batch: 241-242 vs 250-252 us at G = 4, 241
-// vs 246 at G = 3, 246 vs 440 at G = 8.)  bf16 K/V keep the VALU path at every
-// G: the P.V product of the matrix-core path rounds each softmax weight to the
-// MFMA's input type, and bf16's 2^-9 relative rounding is too coarse for the
-// output tolerance on short sequences (fp16's 2^-12 is not).
-constexpr int kMfma16MinG = 3;
+// The matrix-core tile path (below) takes K/V of every format with three or
+// more query heads per KV head; one or two heads keep the VALU path, whose
+// per-tile work is small there and which holds more waves per SIMD.
+// (Measured on MI355X on the 16 x 16K-32K fp16 batch: 241-242 vs 250-252 us at
+// G = 4, 241 vs 246 at G = 3, 246 vs 440 at G = 8.)
+constexpr int kMfmaMinG = 3;
 template <int KIND, int G>
-constexpr bool kUsesMfma = kKv8<KIND> ? G >= 3 : (kQKind<KIND> == KIND_F16 && G >= kMfma16MinG);
+constexpr bool kUsesMfma = G >= kMfmaMinG;
 
 // Address of K/V element `elems` of a tensor starting at base.
 template <int KIND>
@@ -607,8 +604,13 @@ struct MState {
 
 template <int KIND, int G>
 struct MfmaPath {
-  static_assert((kKv8<KIND> || kQKind<KIND> == KIND_F16) && G <= 8,
-                "matrix-core path: e4m3 or fp16 K/V, at most 8 heads");
+  static_assert(G <= 8, "matrix-core path: at most 8 heads per KV head");
+  // bf16 V: P.V runs on bf16 MFMAs, and one bf16 rounding of a weight (2^-9
+  // relative) would be too coarse for the output tolerance on short sequences,
+  // so each weight is split into two bf16 parts, hi + lo (about 2^-17
+  // relative), with two P.V MFMAs per dim block.  fp16 and e4m3 V take one
+  // fp16 rounding (2^-12).
+  static constexpr bool kSplitP = !kKv8<KIND> && kQKind<KIND> == KIND_BF16;
   // Registers: 126 VGPRs + 32 AGPRs (the accumulators), three waves per SIMD;
   // capping it at four waves spills.
   using Q = u32x4[4];
@@ -715,10 +717,27 @@ struct MfmaPath {
     const bool grew = n < G && m_new > st.m;
     st.m = m_new;
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef short s4 __attribute__((ext_vector_type(4)));
     h4 ph;
+    s4 pb_hi, pb_lo;
+    float pw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ph[i] = (_Float16)(n < G ? fast_exp2(sc[i] - m_new) : 0.f);
-    st.l = st.l * alpha + (((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]));
+    for (int i = 0; i < 4; ++i) {
+      const float p = n < G ? fast_exp2(sc[i] - m_new) : 0.f;
+      if constexpr (kSplitP) {
+        const uint16_t hb = to_bits<KIND_BF16>(p);
+        const float hf = __builtin_bit_cast(float, (uint32_t)hb << 16);
+        const uint16_t lb = to_bits<KIND_BF16>(p - hf);  // p - hf is exact in fp32
+        pb_hi[i] = (short)hb;
+        pb_lo[i] = (short)lb;
+        pw[i] = hf + __builtin_bit_cast(float, (uint32_t)lb << 16);
+      } else {
+        ph[i] = (_Float16)p;
+        pw[i] = (float)ph[i];
+      }
+    }
+    // the running sum adds the weights exactly as P.V uses them
+    st.l = st.l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
     if (__ballot(grew)) {
       // rows of o are heads 4 * grp + i; their factors sit in lanes 4 * grp + i
       float ai[4];
@@ -731,13 +750,18 @@ struct MfmaPath {
     }
     typedef unsigned int u2 __attribute__((ext_vector_type(2)));
     if constexpr (!kKv8<KIND>) {
-      // fp16 V: for dim 8n + c, rows 0..3 are half c of the lane's 4 pieces
+      // 16-bit V: for dim 8n + c, rows 0..3 are half c of the lane's 4 pieces
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
         const u2 vb = {__builtin_amdgcn_perm(t.v[1][c >> 1], t.v[0][c >> 1], sel),
                        __builtin_amdgcn_perm(t.v[3][c >> 1], t.v[2][c >> 1], sel)};
-        st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(h4, vb), st.o[c], 0, 0, 0);
+        if constexpr (kSplitP) {
+          st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb_hi, __builtin_bit_cast(s4, vb), st.o[c], 0, 0, 0);
+          st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb_lo, __builtin_bit_cast(s4, vb), st.o[c], 0, 0, 0);
+        } else {
+          st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, __builtin_bit_cast(h4, vb), st.o[c], 0, 0, 0);
+        }
       }
       return;
     }

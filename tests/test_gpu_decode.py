@@ -101,6 +101,16 @@ def test_bf16(split):
     _parity(d, "ragged bf16", split_tokens=split, bf16=True)
 
 
+@pytest.mark.parametrize("split", [0, 256])
+@pytest.mark.parametrize("hq", [24, 64])  # G = 3 and 8: the matrix-core tile path, P split hi + lo
+def test_bf16_matrix_core_groups(hq, split):
+    """bf16 K/V with G >= 3 take the matrix-core tile path with each softmax
+    weight split into two bf16 parts; sequences of 1-5 tokens are where a
+    single bf16 rounding of the weights would show."""
+    d = kvgen.ragged_llama(seed=16, lens=[1, 2, 5, 300, 2049], Hq=hq, Hkv=8)
+    _parity(d, f"ragged bf16 G={hq // 8}", split_tokens=split, bf16=True)
+
+
 @pytest.mark.parametrize("lens", [[1], [17, 0, 3], [0, 0], [16] * 40])
 def test_tiny_lines_default_plan(lens):
     """Fewer line tiles than persistent waves (columns capped at the line length,
