@@ -184,6 +184,30 @@ def common(args, workload, metric, unit, value, ms, dtype, data, config, higher=
             "config": dict({"workload": workload}, **config), "prewarm_ms": args.prewarm_ms}
 
 
+def single_thread_oracle(d, np, oracle, seed):
+    """The oracle on one thread: the small dense config (1 sequence of 1024
+    tokens, 8 query / 2 KV heads) and a seeded 1/16 subset of the headline batch
+    (one of its 16 sequences).  Median of 3 runs each."""
+    import kvgen
+    out = {}
+    c1 = kvgen.dense_small(seed=0)
+    b1 = c1["S"] * c1["Hkv"] * c1["D"] * 4 + c1["Hq"] * c1["D"] * 4
+    t1 = oracle_seconds(lambda: oracle.decode_attn(c1["q"], c1["k"], c1["v"], num_kv_heads=c1["Hkv"],
+                                                   layout=oracle.DENSE, scale=c1["scale"], nthreads=1))
+    out["dense_1x1024_8q2kv"] = {"seconds": round(t1, 6), "gbs": round(b1 / t1 / 1e9, 3)}
+    i = int(np.random.default_rng(seed).integers(d["B"]))
+    cu = d["cu_seqlens"]
+    lo, hi = int(cu[i]), int(cu[i + 1])
+    Hkv, D, Hq = d["Hkv"], d["D"], d["Hq"]
+    b2 = (hi - lo) * Hkv * D * 4 + Hq * D * 4
+    t2 = oracle_seconds(lambda: oracle.decode_attn(d["q"][i:i + 1], d["k"][lo:hi], d["v"][lo:hi], num_kv_heads=Hkv,
+                                                   layout=oracle.RAGGED, scale=d["scale"],
+                                                   cu_seqlens=np.array([0, hi - lo], np.int32), nthreads=1))
+    out["headline_sequence_subset"] = {"sequence": i, "tokens": hi - lo, "seconds": round(t2, 4),
+                                       "gbs": round(b2 / t2 / 1e9, 3)}
+    return out
+
+
 def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
     import kvgen
     d = kvgen.ragged_llama(seed=args.seed)
@@ -255,6 +279,9 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
             sample = f"the full workload (all {B} sequences, {T} tokens), median of 3 runs, {cs:.2f} s each"
         r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
                              "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
+        r["cpu_baseline"]["gpu_speedup"] = round(r["value"] / r["cpu_baseline"]["value"], 1)
+        if not fp8:
+            r["cpu_baseline"]["single_thread"] = single_thread_oracle(d, np, oracle, args.seed)
     return r
 
 
