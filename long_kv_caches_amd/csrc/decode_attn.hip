@@ -13,17 +13,19 @@
 // (running max m, sum l, output o) for the G query heads of KV head g.
 // Lane l owns the 16-byte piece n = l % 16 (8 of the 128 elements) of rows
 // 4*(l/16) .. 4*(l/16)+3 of a tile, so every load instruction reads four whole
-// 256-byte rows (fully coalesced) for K and for V alike.  Per tile:
-//   scores  v_dot2_f32_f16 (or _bf16) partial dots of the lane's piece with q,
-//           summed over the 16 pieces of a row by four DPP row steps;
-//   softmax tile max across the four row groups by permlane16/32 swaps, exp2
-//           in log2 units (scores are pre-scaled by scale * log2 e);
-//   P.V     the probabilities are already in the lanes that hold the V rows:
-//           fp32 FMAs on the lane's 8 V elements.
-// This op is HBM-bound (4-8 flops per byte), so the score dots stay on the
-// vector ALU, where they need no operand reshuffle; no LDS is used in the
-// tile loop.  Two register buffers alternate so the next tile's loads are in
-// flight while the current one is processed.
+// 256-byte rows (fully coalesced) for K and for V alike.  Two register buffers
+// alternate so the next tile's loads are in flight while the current one is
+// processed.  This op is HBM-bound (4-8 flops per byte); two tile paths
+// process a loaded tile:
+//   VecPath (G <= 2): scores by v_dot2_f32_f16 (or _bf16) partial dots of the
+//     lane's piece with q, summed over the 16 pieces of a row by four DPP row
+//     steps; the tile max across the four row groups by permlane16/32 swaps;
+//     exp2 in log2 units (scores are pre-scaled by scale * log2 e); P.V as
+//     fp32 FMAs on the lane's 8 V elements, which sit in the lanes that hold
+//     the probabilities.  No LDS in the tile loop.
+//   MfmaPath (G >= 3): K passes through a small per-wave LDS slice into the
+//     layout of the score MFMA; P.V runs on MFMAs too (below).  From G = 3 the
+//     VALU path's per-tile work (G dots and 8G FMAs per row) costs time.
 //
 // Two schedules distribute the tiles:
 //   balanced (default) -- a persistent grid of CUs x occupancy workgroups.
@@ -46,8 +48,9 @@
 // scale (the CLO page's open question on FP8 KV caches).  The lane layout is
 // the same, a lane's piece of a row is then 8 bytes, and a tile is half the
 // bytes.  K codes are widened exactly to the query's 16-bit type for the
-// v_dot2 scores (k_scale is folded into the score scale), V codes to fp32
-// for the P.V FMAs (v_scale is applied with the final normalisation).
+// scores (k_scale is folded into the score scale), V codes to fp32 for the
+// VALU path's FMAs or to fp16 for the matrix-core P.V (v_scale is applied with
+// the final normalisation).
 #include <atomic>
 #include <type_traits>
 
@@ -494,7 +497,7 @@ __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot
 // ---------------------------------------------------------------------------
 // Tile paths.  A path is how a wave holds q, a tile and its softmax state:
 //   VecPath  -- the VALU path above (lanes own row pieces of K and V);
-//   MfmaPath -- matrix cores for the scores and P.V (e4m3 K/V), below.
+//   MfmaPath -- matrix cores for the scores and P.V (any K/V format), below.
 // Both present the same functions to the schedules.
 // ---------------------------------------------------------------------------
 
@@ -611,8 +614,9 @@ struct MfmaPath {
   // relative), with two P.V MFMAs per dim block.  fp16 and e4m3 V take one
   // fp16 rounding (2^-12).
   static constexpr bool kSplitP = !kKv8<KIND> && kQKind<KIND> == KIND_BF16;
-  // Registers: 126 VGPRs + 32 AGPRs (the accumulators), three waves per SIMD;
-  // capping it at four waves spills.
+  // Registers (accumulators in 36 AGPRs): 128 VGPRs for e4m3 K/V, three
+  // waves per SIMD (capping it at four spills); 160-166 for 16-bit K/V, two
+  // waves per SIMD.
   using Q = u32x4[4];
   using State = MState;
   // K and V are both loaded as the VALU path loads them: lane l takes the
