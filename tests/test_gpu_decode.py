@@ -144,13 +144,14 @@ def test_page_size_32():
     _parity(p, "paged page_size=32", split_tokens=128)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("split", [0, 128])
-def test_paged_matrix_core_group(split):
-    """fp16 K/V with G = 8 take the matrix-core tile path; the paged source
+def test_paged_matrix_core_group(split, bf16):
+    """16-bit K/V with G = 8 take the matrix-core tile path; the paged source
     addresses its tiles in bytes of the 16-bit elements."""
     d = kvgen.ragged_llama(seed=14, lens=[33, 700, 16, 2100], Hq=64, Hkv=8)
     p = kvgen.ragged_to_paged(d, seed=15, page=32)
-    _parity(p, "paged G=8 page_size=32", split_tokens=split)
+    _parity(p, "paged G=8 page_size=32", split_tokens=split, bf16=bf16)
 
 
 def test_headline_full_size():
