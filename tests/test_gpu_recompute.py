@@ -108,6 +108,19 @@ def test_wide_tiles_ragged_rows(w_layout):
     _check_rows(d, kc, vc, rows=rows)
 
 
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+def test_wide_tiles_shortest_k(w_layout):
+    """h = 256: four 64-wide K steps, so the loads two steps ahead clamp from
+    the first step on; b*l = 32768 rows make exactly 256 tiles of 256 x 256."""
+    d = kvgen.kvpr_layer(seed=17, b=4, h=256, H=2, s=8200, l=8192)
+    say(f"[recompute] b=4 l=8192 h=256 (256 x 256 tiles, 4 K steps) w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
+    edges = [0, 255, 256, 8191, 8192, 16383, 24576, 32767]
+    pick = np.random.default_rng(18).choice(32768, 40, replace=False)
+    rows = np.unique(np.concatenate([edges, pick])).astype(np.int32)
+    _check_rows(d, kc, vc, rows=rows)
+
+
 def test_end_to_end_against_fp64_recompute():
     d = kvgen.kvpr_layer(seed=4, b=2, h=1024, H=8, s=200, l=120)
     say("[recompute] end to end vs fp64 X.W")
