@@ -83,7 +83,7 @@ def test_empty_sequences(split):
 
 
 @pytest.mark.parametrize("split", [0, 256])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (12, 4), (40, 8), (48, 8), (56, 8), (64, 8)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (12, 4), (40, 8), (48, 8), (56, 8), (64, 8), (8, 1), (3, 1)])
 def test_group_sizes(hq, hkv, split):
     d = kvgen.ragged_llama(seed=5, lens=[1, 77, 1500, 2049], Hq=hq, Hkv=hkv)
     _parity(d, f"G={hq // hkv}", split_tokens=split)
