@@ -153,6 +153,17 @@ def test_topk_rows_not_a_multiple_of_four():
         check_topk(d, top_k, "S=3001")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (6, 2), (15, 5), (64, 64), (65, 65)])
+def test_topk_head_layouts(Hq, Hkv):
+    # the score pass walks (token, head) pieces in memory order, four pieces
+    # per load: one or two KV heads (several tokens per load), a head count
+    # that is no power of two, the largest count whose query sums fit its
+    # LDS table, and one more (one KV head at a time)
+    d = kvgen.dense_small(seed=71 + Hkv, B=3, Hq=Hq, Hkv=Hkv, S=777, seqlens=[777, 500, 3])
+    for top_k in (1, 100, 600):
+        check_topk(d, top_k, f"Hq={Hq} Hkv={Hkv} S=777")
+
+
 def test_topk_ties_go_to_smaller_tokens():
     d = _model_small("llama3-8b", 68, lens=(3000, 2000))
     d["k"][0, :, 3] = d["k"][0, 77, 3]  # every row of head 3 equal: all scores tie
