@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 7
+#define KVDEC_ABI_VERSION 8
 
 typedef enum {
   KVDEC_OK = 0,
@@ -209,7 +209,9 @@ kvdec_status kvdec_gather_attn(const kvdec_gather_desc* desc, const void* q, con
  *   q [B, Hq, 128], k [B, S, Hkv, 128] (dtype); seqlens [B] int32 or NULL (all S)
  *   idx [B, Hkv, top_k] int32 (entries past idx_len are not written)
  * Requires S <= 262144, top_k >= 0, 16-bit K.  The workspace (16-byte
- * aligned) holds the scores: B * Hkv rows of S rounded up to 4 floats.
+ * aligned, size from kvdec_topk_select_workspace, no initialisation needed)
+ * holds the scores, B * Hkv rows of S rounded up to 4 floats, and then the
+ * selection's per-pair histograms and counters.
  */
 typedef struct {
   int32_t batch, num_q_heads, num_kv_heads, head_dim;
@@ -361,8 +363,9 @@ kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_
  * start and its end, with no extra packets on the stream.  Main kernels: the
  * split kernel of an attention call (not the merge kernel), the lookup kernel
  * of kvdec_headcache_lookup (not the compaction kernel), the projection of
- * kvdec_headcache_lookup_ahead, each of the two kernels of
- * kvdec_topk_select, the GEMM of kvdec_kv_recompute and of
+ * kvdec_headcache_lookup_ahead, each of the five kernels of
+ * kvdec_topk_select (the score pass, three radix-digit passes and the
+ * compaction), the GEMM of kvdec_kv_recompute and of
  * kvdec_kvpr_load_layer.
  * kvdec_kernel_timing(1) starts a new measurement (the library keeps and
  * reuses its events); kvdec_kernel_timing(0) stops recording.

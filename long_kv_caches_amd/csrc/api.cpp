@@ -532,7 +532,7 @@ kvdec_status kvdec_topk_select_workspace(const kvdec_topk_desc* d, size_t* bytes
   if (!bytes) return fail(KVDEC_ERR_INVALID, "bytes is NULL");
   kvdec_status st = check_topk(d);
   if (st != KVDEC_OK) return st;
-  *bytes = (size_t)d->batch * d->num_kv_heads * ((d->max_seqlen + 3) & ~3) * sizeof(float);
+  *bytes = topk_workspace_bytes(d->batch * d->num_kv_heads, d->max_seqlen);
   return ok();
 }
 
@@ -543,7 +543,7 @@ kvdec_status kvdec_topk_select(const kvdec_topk_desc* d, const void* q, const vo
   if (st != KVDEC_OK) return st;
   if (d->batch == 0) return ok();
   if (!idx_len) return fail(KVDEC_ERR_INVALID, "idx_len must be non-NULL");
-  const size_t need = (size_t)d->batch * d->num_kv_heads * ((d->max_seqlen + 3) & ~3) * sizeof(float);
+  const size_t need = topk_workspace_bytes(d->batch * d->num_kv_heads, d->max_seqlen);
   if (d->max_seqlen > 0) {
     if (!q || !k) return fail(KVDEC_ERR_INVALID, "q and k must be non-NULL");
     if (d->top_k > 0 && !idx) return fail(KVDEC_ERR_INVALID, "idx must be non-NULL");
@@ -565,6 +565,10 @@ kvdec_status kvdec_topk_select(const kvdec_topk_desc* d, const void* q, const vo
   a.G = d->num_q_heads / d->num_kv_heads;
   a.S = d->max_seqlen;
   a.S4 = (d->max_seqlen + 3) & ~3;
+  a.C = topk_chunks(d->max_seqlen);
+  a.sel = ws ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) +
+                                           (size_t)a.B * a.Hkv * a.S4 * sizeof(float))
+             : nullptr;
   a.top_k = d->top_k;
   a.dtype = d->dtype;
   return hip_status(launch_topk(a, stream), "top-k selection launch");

@@ -89,9 +89,16 @@ struct TopkArgs {
   float* scores;           // [B * Hkv, S4] workspace, S4 = S rounded up to 4
   int32_t* idx;            // [B * Hkv, top_k]
   int32_t* idx_len;        // [B * Hkv]
+  uint32_t* sel;           // [B * Hkv, topk_sel_words(C)] workspace after the scores
   int B, Hq, Hkv, G, S, S4, top_k;
+  int C;                   // selection chunks per pair, topk_chunks(S)
   int dtype;
 };
+constexpr int kSelChunk = 16384;  // tokens per selection workgroup
+constexpr int kSelHist = 2048;    // bins of a radix digit's histogram
+inline int topk_chunks(int S) { return S > 0 ? (S + kSelChunk - 1) / kSelChunk : 1; }
+__host__ __device__ constexpr int topk_sel_words(int chunks) { return 2048 + 2048 + 1024 + 8 + chunks * 1028; }
+size_t topk_workspace_bytes(int pairs, int S);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -19,14 +19,18 @@
 //   topk_score_kernel  -- the same scores one KV head at a time (more heads):
 //     one wave per 16-token tile, lane l holds piece l % 16 (8 dims) of rows
 //     4 * (l / 16) .. +3, the query sum in fp32 for its piece.
-//   topk_select_kernel -- one 1024-thread workgroup per pair over the pair's
-//     scores (L2-resident): a radix select of the k-th largest key in three
-//     passes of 11, 11 and 10 bits (LDS histograms), then an ordered
-//     compaction: per 256-token segment (lane l: tokens 4l .. 4l+3), ballots
-//     count the keys above the threshold and those equal to it, a scan over
-//     the segments gives each its output offset and its ties before it, and
-//     a second sweep writes the selected indices in order.  Every sweep reads
-//     the scores with 16-byte loads, four in flight per thread.
+//   topk_radix_kernel<0..2> -- a radix select of the k-th largest orderable
+//     key in three digits of 11, 11 and 10 bits, one 1024-thread workgroup per
+//     16K-token chunk of a pair (LDS histogram of the chunk's keys that match
+//     the prefix so far); the chunk that finishes last adds the chunks'
+//     histograms and picks the digit.  The last digit's pass also leaves each
+//     chunk's count of keys above and equal to the threshold before it.
+//   topk_write_kernel -- the ordered compaction of each chunk: per 256-token
+//     segment (lane l: tokens 4l .. 4l+3) ballots count the keys above the
+//     threshold and those equal to it, a scan over the chunk's segments gives
+//     each its output offset and its ties before it, and the selected indices
+//     are written in order.  Every pass reads the chunk's scores with 16-byte
+//     loads, 16 keys per thread.
 #include "device_common.h"
 #include "internal.h"
 
@@ -34,11 +38,31 @@ namespace kvdec {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelBatch = 4;  // 16-byte loads each thread keeps in flight in a sweep
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kMaxSegments = kTopkMaxLen / 256;
+constexpr int kSelSegs = kSelChunk / 256;  // 256-token segments per chunk: one per lane of a wave
+static_assert(kSelSegs == 64 && kSelChunk == 4 * 4 * kSelThreads, "a thread holds 16 keys of its chunk");
+static_assert(kTopkMaxLen / kSelChunk <= kSelWaves, "one wave per chunk when the last pass splits counts");
 constexpr int kRowSteps = 16;     // 16-segment steps each wave of the whole-row score kernel takes
 constexpr int kRowMaxHkv = 64;    // KV heads whose query sums the whole-row kernel keeps in LDS
+
+// A pair's slice of the selection workspace (after the score rows).  The
+// merged histograms are atomic targets; each kernel reads what the previous
+// ones left (a kernel boundary between every write and read of another
+// workgroup's data).
+struct SelPair {
+  uint32_t* h0;      // [2048] keys per top digit (bits 21..31)
+  uint32_t* h1;      // [2048] per middle digit (bits 10..20), keys under the chosen top digit
+  uint32_t* h2;      // [1024] per low digit (bits 0..9), keys under the chosen 22-bit prefix
+  uint32_t* state;   // [8]: after the middle pass prefix, mask, remaining, -; after the low
+                     // pass prefix, mask, remaining, -
+  uint32_t* chunks;  // [chunks, 1028]: each chunk's low-digit histogram, then its keys above
+                     // the 22-bit prefix
+};
+
+__device__ __forceinline__ SelPair sel_pair(const TopkArgs& a, int pair) {
+  uint32_t* base = a.sel + (size_t)pair * topk_sel_words(a.C);
+  return {base, base + 2048, base + 4096, base + 5120, base + 5128};
+}
 
 // Orderable key of a float: larger float <=> larger unsigned key.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -53,6 +77,8 @@ __global__ __launch_bounds__(256) void topk_score_kernel(TopkArgs a) {
   const int pair = blockIdx.y, b = pair / a.Hkv, g = pair - b * a.Hkv;
   const int len = uniform_i32(min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S));
   const int t0 = (blockIdx.x * 4 + wave) * kTile;
+  // the selection's top-digit histogram of this pair starts at zero
+  for (int w = blockIdx.x * 256 + threadIdx.x; w < 2048; w += gridDim.x * 256) sel_pair(a, pair).h0[w] = 0;
   if (t0 >= len) return;
   // the group's query sum for this lane's 8 dims, fp32 in head order
   float qs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -111,6 +137,9 @@ __global__ __launch_bounds__(256) void topk_score_rows_kernel(TopkArgs a) {
   const int len = uniform_i32(min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S));
   const int nseg = len * Hkv;
   const int blk0 = blockIdx.x * kBlockSegs;
+  // the selection's top-digit histograms of this sequence's pairs start at zero
+  for (int w = blockIdx.x * 256 + tid; w < Hkv * 2048; w += gridDim.x * 256)
+    sel_pair(a, b * Hkv + (w >> 11)).h0[w & 2047] = 0;
   if (blk0 >= nseg) return;
   const uint16_t* kseq = a.k + (int64_t)b * a.S * Hkv * kHeadDim;
   // 16 segments from seg0 (those past the sequence read as zeros, unfetched)
@@ -184,32 +213,6 @@ __global__ __launch_bounds__(256) void topk_score_rows_kernel(TopkArgs a) {
   }
 }
 
-// Exclusive scan of one int per thread over the workgroup; *total gets the sum.
-__device__ int sel_scan(int x, int* s_wave, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int incl = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int t = s_wave[w];
-      s_wave[w] = run;
-      run += t;
-    }
-    *total = run;
-  }
-  __syncthreads();
-  const int r = s_wave[wave] + incl - x;
-  __syncthreads();  // s_wave is reused by the next scan
-  return r;
-}
-
 // Ranks of this lane's four tokens (4 * lane + c) among the flagged tokens of
 // a 256-token segment, in token order.
 __device__ __forceinline__ void seg_ranks(const bool (&f)[4], int lane, int (&rank)[4], int* total) {
@@ -229,156 +232,247 @@ __device__ __forceinline__ void seg_ranks(const bool (&f)[4], int lane, int (&ra
   *total = all;
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t s_hist[2048];
-  __shared__ int s_seg_gt[kMaxSegments], s_seg_eq[kMaxSegments];
-  __shared__ int s_wave[kSelWaves];
-  __shared__ int s_total;
-  __shared__ uint32_t s_sel[2];  // selected digit, remaining count
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pair = blockIdx.x, b = pair / a.Hkv;
-  const int len = min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S);
-  const int need = min(a.top_k, len);
-  int32_t* out = a.idx + (int64_t)pair * a.top_k;
-  if (tid == 0) a.idx_len[pair] = need;
-  if (need == 0) return;
-  if (need == len) {  // everything is kept
-    for (int t = tid; t < len; t += kSelThreads) out[t] = t;
-    return;
-  }
-  // the pair's scores (rows of S4 = S rounded up to 4 floats, so a 16-byte
-  // read never leaves the row); reads past the row's valid groups return zeros,
-  // and tokens at or past len are masked below
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+// This thread's 16 keys of chunk c: segment wave + 16 u (256 tokens each) of
+// the chunk, tokens 4 lane .. 4 lane + 3 of it.  Reads past the row's valid
+// 16-byte groups return zeros; tokens at or past len are masked by the caller.
+__device__ __forceinline__ void load_chunk(const TopkArgs& a, int pair, int len, int c, int wave, int lane,
+                                           f32x4 (&v)[4]) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform_ptr(a.scores + (int64_t)pair * a.S4),
                                               uniform_u32((uint32_t)((len + 3) & ~3) * 4u));
-  auto load4 = [&](int t) -> f32x4 {  // tokens t .. t+3
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * t, 0, 0));
-  };
-  // Radix select of the need-th largest key: digits of 11, 11, 10 bits.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = c * kSelChunk + 256 * (wave + kSelWaves * u) + 4 * lane;
+    v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * t, 0, 0));
+  }
+}
+
+// The digit of a merged histogram (nbins bins, h 16-byte aligned) that holds
+// the remaining-th largest key: *digit, and in *rem the rank of that key among
+// the keys of the digit.  Run by one whole wave; lane l reads the bins
+// [nbins - per (l + 1), nbins - per l), counted from the top.
+template <int NBINS>
+__device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t remaining, int lane, uint32_t* digit,
+                                           uint32_t* rem) {
+  constexpr int per = NBINS / 64;
+  const int first = NBINS - per * (lane + 1);
+  uint32_t cnt[per];
+#pragma unroll
+  for (int i = 0; i < per; i += 4) {
+    const u32x4 x = load_b128(h + first + i);
+    cnt[i] = x.x;
+    cnt[i + 1] = x.y;
+    cnt[i + 2] = x.z;
+    cnt[i + 3] = x.w;
+  }
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) total += cnt[i];
+  uint32_t incl = total;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const uint32_t before = incl - total;  // keys in higher bins
+  if (before < remaining && remaining <= incl) {
+    uint32_t run = before;
+    bool found = false;
+#pragma unroll
+    for (int i = per - 1; i >= 0; --i) {
+      if (!found && run + cnt[i] >= remaining) {
+        *digit = (uint32_t)(first + i);
+        *rem = remaining - run;
+        found = true;
+      }
+      run += cnt[i];
+    }
+  }
+}
+
+// One digit of the radix select of the need-th largest key (P = 0, 1, 2:
+// bits 21..31, 10..20, 0..9), one workgroup per chunk of a pair: the prefix
+// chosen so far comes from the previous passes (P = 1: the top digit from the
+// merged top histogram; P = 2: the stored prefix and the middle digit), then
+// the chunk's keys that match it are counted in an LDS histogram of the next
+// digit, whose bins are added to the pair's merged histogram.  The low pass
+// also keeps each chunk's own histogram and its count of keys above the
+// 22-bit prefix for the compaction's offsets.
+template <int P>
+__global__ __launch_bounds__(kSelThreads) void topk_radix_kernel(TopkArgs a) {
+  constexpr int shift = P == 0 ? 21 : P == 1 ? 10 : 0;
+  constexpr int nbins = P == 2 ? 1024 : 2048;
+  __shared__ uint32_t s_hist[kSelHist];
+  __shared__ uint32_t s_sel[2];  // digit, remaining
+  __shared__ uint32_t s_above;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, pair = blockIdx.y, b = pair / a.Hkv;
+  const int len = min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S);
+  const int need = min(a.top_k, len);
+  if (P == 0 && c == 0 && tid == 0) a.idx_len[pair] = need;
+  if (need == 0) return;
+  if (need == len) {  // everything is kept: each chunk writes its own tokens
+    if (P == 0) {
+      int32_t* out = a.idx + (int64_t)pair * a.top_k;
+      for (int t = c * kSelChunk + tid; t < min(len, (c + 1) * kSelChunk); t += kSelThreads) out[t] = t;
+    }
+    return;
+  }
+  const int nchunks = (len + kSelChunk - 1) / kSelChunk;
+  if (c >= nchunks) return;
+  const SelPair sp = sel_pair(a, pair);
+  f32x4 v[4];
+  load_chunk(a, pair, len, c, wave, lane, v);  // in flight while the prefix is found
   uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)need;
-  const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
-  for (int p = 0; p < 3; ++p) {
-    const int shift = shifts[p], nbins = 1 << widths[p];
-    for (int i = tid; i < nbins; i += kSelThreads) s_hist[i] = 0;
-    __syncthreads();
-    for (int t0 = 4 * tid; t0 < len; t0 += 4 * kSelBatch * kSelThreads) {
-      f32x4 v[kSelBatch];
-#pragma unroll
-      for (int u = 0; u < kSelBatch; ++u) v[u] = load4(t0 + 4 * u * kSelThreads);
-#pragma unroll
-      for (int u = 0; u < kSelBatch; ++u) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t k = order_key(v[u][c]);
-          if (t0 + 4 * u * kSelThreads + c < len && (k & mask) == prefix)
-            atomicAdd(&s_hist[(k >> shift) & (nbins - 1)], 1u);
-        }
-      }
-    }
-    __syncthreads();
+  if (P == 0) {
+    if (c == 0)  // the later passes' merged histograms start at zero
+      for (int i = tid; i < 2048 + 1024; i += kSelThreads) sp.h1[i] = 0;
+  } else {
     if (wave == 0) {
-      // lane l sums bins [nbins - per (l + 1), nbins - per l) (from the top)
-      const int per = nbins / 64;
-      uint32_t c = 0;
-      for (int i = 0; i < per; ++i) c += s_hist[nbins - per * (lane + 1) + i];
-      uint32_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      const uint32_t before = incl - c;  // keys in higher bins
-      if (before < remaining && remaining <= incl) {
-        uint32_t run = before;
-        for (int i = per - 1; i >= 0; --i) {
-          const int bin = nbins - per * (lane + 1) + i;
-          const uint32_t h = s_hist[bin];
-          if (run + h >= remaining) {
-            s_sel[0] = (uint32_t)bin;
-            s_sel[1] = remaining - run;
-            break;
-          }
-          run += h;
-        }
-      }
+      if (P == 1) find_digit<2048>(sp.h0, (uint32_t)need, lane, &s_sel[0], &s_sel[1]);
+      else find_digit<2048>(sp.h1, sp.state[2], lane, &s_sel[0], &s_sel[1]);
     }
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    mask |= (uint32_t)(nbins - 1) << shift;
-    remaining = s_sel[1];
-    __syncthreads();
+    if (P == 2) {
+      prefix = sp.state[0];
+      mask = sp.state[1];
+    }
   }
-  const uint32_t T = prefix;                 // the need-th largest key
-  const int take_eq = (int)remaining;        // keys equal to T to keep, lowest tokens first
-  // Ordered compaction over 256-token segments (lane l: tokens 4l .. 4l+3).
-  const int nseg = (len + 255) / 256;
-  auto flags = [&](const f32x4& v, int t, bool (&gt)[4], bool (&eq)[4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t k = order_key(v[c]);
-      gt[c] = t + c < len && k > T;
-      eq[c] = t + c < len && k == T;
+  for (int i = tid; i < nbins; i += kSelThreads) s_hist[i] = 0;
+  if (tid == 0) s_above = 0;
+  __syncthreads();
+  if (P > 0) {  // the digit just found extends the prefix
+    constexpr int pshift = P == 1 ? 21 : 10;
+    prefix |= s_sel[0] << pshift;
+    mask |= 2047u << pshift;
+    if (c == 0 && tid == 0) {
+      uint32_t* st = sp.state + 4 * (P - 1);
+      st[0] = prefix;
+      st[1] = mask;
+      st[2] = s_sel[1];
     }
-  };
-  for (int s0 = wave; s0 < nseg; s0 += kSelBatch * kSelWaves) {
-    f32x4 v[kSelBatch];
+  }
+  uint32_t above = 0;
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) v[u] = load4(256 * (s0 + u * kSelWaves) + 4 * lane);
+  for (int u = 0; u < 4; ++u) {
+    const int t = c * kSelChunk + 256 * (wave + kSelWaves * u) + 4 * lane;
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) {
-      const int s = s0 + u * kSelWaves;
-      if (s >= nseg) break;  // the same in every lane
-      bool gt[4], eq[4];
-      flags(v[u], 256 * s + 4 * lane, gt, eq);
-      int r[4], ngt, neq;
-      seg_ranks(gt, lane, r, &ngt);
-      seg_ranks(eq, lane, r, &neq);
-      if (lane == 0) {
-        s_seg_gt[s] = ngt;
-        s_seg_eq[s] = neq;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = order_key(v[u][e]);
+      if (t + e < len) {
+        if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & (nbins - 1)], 1u);
+        else if (P == 2 && (k & mask) > prefix) ++above;
       }
+    }
+  }
+  if (P == 2) {
+    above = wave_sum_u32(above);
+    if (lane == 0 && above) atomicAdd(&s_above, above);
+  }
+  __syncthreads();
+  uint32_t* merged = P == 0 ? sp.h0 : P == 1 ? sp.h1 : sp.h2;
+  for (int i = tid; i < nbins; i += kSelThreads) {
+    const uint32_t n = s_hist[i];
+    if (n) atomicAdd(&merged[i], n);
+    if (P == 2) sp.chunks[c * 1028 + i] = n;
+  }
+  if (P == 2 && tid == 0) sp.chunks[c * 1028 + 1024] = s_above;
+}
+
+// Ordered compaction of one chunk: the keys above T, and the first keys equal
+// to T in token order up to the count to keep, written in ascending token
+// order at the chunk's offset.  Per 256-token segment, ballots count both
+// kinds; a scan over the chunk's 64 segments (one per lane of wave 0) gives
+// each its output offset and its ties before it.
+__global__ __launch_bounds__(kSelThreads) void topk_write_kernel(TopkArgs a) {
+  __shared__ int s_seg_gt[kSelSegs], s_seg_eq[kSelSegs];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, pair = blockIdx.y, b = pair / a.Hkv;
+  const int len = min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S);
+  const int need = min(a.top_k, len);
+  if (need == 0 || need == len) return;  // written by the first pass
+  const int nchunks = (len + kSelChunk - 1) / kSelChunk;
+  if (c >= nchunks) return;
+  const SelPair sp = sel_pair(a, pair);
+  f32x4 v[4];
+  load_chunk(a, pair, len, c, wave, lane, v);  // in flight while the threshold is found
+  __shared__ uint32_t s_sel[2];
+  __shared__ int s_cnt[kSelWaves][2];
+  if (wave == 0) find_digit<1024>(sp.h2, sp.state[6], lane, &s_sel[0], &s_sel[1]);
+  __syncthreads();
+  const uint32_t d = s_sel[0];
+  const uint32_t T = sp.state[4] | d;  // the need-th largest key
+  const int take_eq = (int)s_sel[1];   // keys equal to T to keep, lowest tokens first
+  if (wave < c) {  // wave w: chunk w's keys above T and equal to T
+    const uint32_t* h = sp.chunks + wave * 1028;
+    uint32_t gt = 0;
+    for (int i = (int)d + 1 + lane; i < 1024; i += 64) gt += h[i];
+    gt = wave_sum_u32(gt);
+    if (lane == 0) {
+      s_cnt[wave][0] = (int)(gt + h[1024]);
+      s_cnt[wave][1] = (int)h[d];
     }
   }
   __syncthreads();
-  // scan the segments in order: each thread takes a contiguous run of them
-  const int per = (nseg + kSelThreads - 1) / kSelThreads;
-  const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
-  int my_gt = 0, my_eq = 0;
-  for (int s = s0; s < s1; ++s) {
-    my_gt += s_seg_gt[s];
-    my_eq += s_seg_eq[s];
+  int gt_before = 0, eq_before = 0;  // in the chunks before this one
+  for (int w = 0; w < c; ++w) {
+    gt_before += s_cnt[w][0];
+    eq_before += s_cnt[w][1];
   }
-  int gt_run = sel_scan(my_gt, s_wave, &s_total);
-  int eq_run = sel_scan(my_eq, s_wave, &s_total);
-  for (int s = s0; s < s1; ++s) {
-    const int g_ = s_seg_gt[s], e_ = s_seg_eq[s];
-    s_seg_gt[s] = gt_run + min(eq_run, take_eq);  // output offset of the segment
-    s_seg_eq[s] = eq_run;                          // ties before the segment
-    gt_run += g_;
-    eq_run += e_;
+  int32_t* out = a.idx + (int64_t)pair * a.top_k;
+  bool gt[4][4], eq[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = wave + kSelWaves * u;
+    const int t = c * kSelChunk + 256 * s + 4 * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = order_key(v[u][e]);
+      gt[u][e] = t + e < len && k > T;
+      eq[u][e] = t + e < len && k == T;
+    }
+    int r[4], ngt, neq;
+    seg_ranks(gt[u], lane, r, &ngt);
+    seg_ranks(eq[u], lane, r, &neq);
+    if (lane == 0) {
+      s_seg_gt[s] = ngt;
+      s_seg_eq[s] = neq;
+    }
   }
   __syncthreads();
-  for (int s0b = wave; s0b < nseg; s0b += kSelBatch * kSelWaves) {
-    f32x4 v[kSelBatch];
+  if (wave == 0) {  // lane l: segment l
+    const int g = s_seg_gt[lane], e = s_seg_eq[lane];
+    int ig = g, ie = e;
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) v[u] = load4(256 * (s0b + u * kSelWaves) + 4 * lane);
-#pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) {
-      const int s = s0b + u * kSelWaves;
-      if (s >= nseg) break;  // the same in every lane
-      const int t = 256 * s + 4 * lane;
-      bool gt[4], eq[4], sel[4];
-      flags(v[u], t, gt, eq);
-      int er[4], sr[4], dummy;
-      seg_ranks(eq, lane, er, &dummy);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sel[c] = gt[c] || (eq[c] && s_seg_eq[s] + er[c] < take_eq);
-      seg_ranks(sel, lane, sr, &dummy);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (sel[c]) out[s_seg_gt[s] + sr[c]] = t + c;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int yg = __shfl_up(ig, d, 64), ye = __shfl_up(ie, d, 64);
+      if (lane >= d) {
+        ig += yg;
+        ie += ye;
+      }
     }
+    const int eq_run = eq_before + ie - e;
+    s_seg_gt[lane] = gt_before + ig - g + min(eq_run, take_eq);  // output offset of the segment
+    s_seg_eq[lane] = eq_run;                                       // ties before the segment
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = wave + kSelWaves * u;
+    const int t = c * kSelChunk + 256 * s + 4 * lane;
+    int er[4], sr[4], dummy;
+    bool sel[4];
+    seg_ranks(eq[u], lane, er, &dummy);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sel[e] = gt[u][e] || (eq[u][e] && s_seg_eq[s] + er[e] < take_eq);
+    seg_ranks(sel, lane, sr, &dummy);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sel[e]) out[s_seg_gt[s] + sr[e]] = t + e;
   }
 }
 
@@ -401,8 +495,17 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  launch_timed(topk_select_kernel, dim3((unsigned)pairs), dim3(kSelThreads), 0u, stream, a);
+  const dim3 cgrid((unsigned)a.C, (unsigned)pairs);
+  launch_timed(topk_radix_kernel<0>, cgrid, dim3(kSelThreads), 0u, stream, a);
+  launch_timed(topk_radix_kernel<1>, cgrid, dim3(kSelThreads), 0u, stream, a);
+  launch_timed(topk_radix_kernel<2>, cgrid, dim3(kSelThreads), 0u, stream, a);
+  launch_timed(topk_write_kernel, cgrid, dim3(kSelThreads), 0u, stream, a);
   return hipGetLastError();
+}
+
+size_t topk_workspace_bytes(int pairs, int S) {
+  const size_t S4 = (size_t)((S + 3) & ~3);
+  return (size_t)pairs * (S4 * sizeof(float) + (size_t)topk_sel_words(topk_chunks(S)) * sizeof(uint32_t));
 }
 
 }  // namespace kvdec

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 7
+    assert _lib.lib.kvdec_abi_version() == 8
 
 
 def test_status_strings():
@@ -274,7 +274,14 @@ def test_gather_and_topk_validation():
     td = K.topk_desc(batch=2, num_q_heads=8, num_kv_heads=2, dtype=torch.float16, max_seqlen=100,
                      top_k=10)
     assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 0
-    assert n.value == 2 * 2 * 100 * 4  # S = 100 is a multiple of 4
+    # per pair: a score row of S rounded up to 4 floats, then three merged digit
+    # histograms (2048 + 2048 + 1024 words), 8 words of state, and per
+    # 16384-token chunk a 1024-bin histogram and 4 more words
+    assert n.value == 2 * 2 * (100 * 4 + (5120 + 8 + 1 * 1028) * 4)  # S = 100: one chunk
+    td.max_seqlen = 40001
+    assert _lib.lib.kvdec_topk_select_workspace(ctypes.byref(td), ctypes.byref(n)) == 0
+    assert n.value == 2 * 2 * (40004 * 4 + (5120 + 8 + 3 * 1028) * 4)  # three chunks
+    td.max_seqlen = 100
     T = _lib.lib.kvdec_topk_select
     assert T(ctypes.byref(td), FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 3  # workspace
     td.max_seqlen = 300000

@@ -171,6 +171,26 @@ def test_topk_ties_go_to_smaller_tokens():
     assert np.array_equal(gi[0, 3, :50], np.arange(50))
 
 
+def test_topk_chunks_and_ties_across_chunk_boundaries():
+    # 40000 rows: the selection splits each pair into 16384-token chunks.
+    # Sequence 0, head 3: every row equal, so all scores tie and the smallest
+    # tokens are kept, across the first chunk boundary.  Head 5: rows
+    # 16000..17999 equal and scoring above every other row (8 * the sign of the
+    # group's query sum), a tie band across the same boundary.
+    d = _model_small("llama3-8b", 72, S=40000, lens=(40000, 33000))
+    d["k"][0, :, 3] = d["k"][0, 77, 3]
+    qsum = np.asarray(d["q"][0, 20:24], np.float64).sum(axis=0)
+    d["k"][0, 16000:18000, 5] = 8.0 * np.where(qsum >= 0, 1.0, -1.0)
+    gi, gn = check_topk(d, 1500, "S=40000 tie band")
+    assert np.array_equal(gi[0, 5, :1500], np.arange(16000, 17500))
+    gi, gn = check_topk(d, 20000, "S=40000 all tie")
+    assert np.array_equal(gi[0, 3, :20000], np.arange(20000))
+    assert np.isin(np.arange(16000, 18000), gi[0, 5, :20000]).all()  # the band is inside
+    gi, gn = check_topk(d, 40000, "S=40000 keep all")
+    assert np.array_equal(gi[0, 0, :40000], np.arange(40000))
+    assert np.array_equal(gi[1, 7, :33000], np.arange(33000))
+
+
 def test_topk_then_gather_end_to_end():
     d = _model_small("llama3-8b", 69, S=5000, lens=(5000, 4000, 300, 0))
     top_k = 500
