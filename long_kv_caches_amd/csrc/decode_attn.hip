@@ -437,53 +437,62 @@ __device__ __forceinline__ void store_empty(const AttnArgs& a, int64_t head0) {
   }
 }
 
+constexpr int kMergeRows = 16;                 // partial rows a merge workgroup folds at once
+constexpr int kMergeThreads = 32 * kMergeRows;  // 32 lanes per row, 4 elements each
+
 // Merges n_p >= 1 partials of query head j of a group (slots slot0 +
 // i * slot_step, i < n_p) into the final output and lse of head head0 + j:
 // out = sum_i w_i o_i / sum_i w_i l_i with w_i = 2^(m_i - M), M = max_i m_i.
-// Thread (c, r) of the 256 takes elements 4c .. 4c+3 of the partials
-// i = r, r + 8, ... in order; the eight running sums are then added in the
-// order r = 0 .. 7, so the result does not depend on timing.
+// Thread (c, r) of the kMergeThreads takes elements 4c .. 4c+3 of the
+// partials i = r, r + kMergeRows, ... in order, with a running maximum, so
+// each partial is read once; the rows are then scaled to the common maximum
+// and added in the order r = 0, 1, ..., so the result does not depend on timing.
 template <int KIND, int G>
 __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot0, int slot_step,
                            int n_p) {
-  __shared__ float s_max[kWaves];
-  __shared__ f32x4 s_acc[8][32];
-  __shared__ float s_l[8];
+  __shared__ float s_m[kMergeRows];
+  __shared__ f32x4 s_acc[kMergeRows][32];
+  __shared__ float s_l[kMergeRows];
   const int tid = threadIdx.x, c = tid & 31, r = tid >> 5;
+  // row r folds partials r, r + kMergeRows, ... with a running maximum (one
+  // pass over the partials: their maxima and outputs are read together)
   float m = -INFINITY;
-  for (int i = tid; i < n_p; i += 256) m = fmaxf(m, a.ws_ml[((slot0 + (int64_t)i * slot_step) * G + j) * 2]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-  if ((tid & 63) == 0) s_max[tid >> 6] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, lsum = 0.f;
 #pragma unroll 4
-  for (int i = r; i < n_p; i += 8) {
+  for (int i = r; i < n_p; i += kMergeRows) {
     const int64_t sj = (slot0 + (int64_t)i * slot_step) * G + j;
     const float mi = a.ws_ml[sj * 2], li = a.ws_ml[sj * 2 + 1];
     const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + sj * kHeadDim + 4 * c);
-    const float w = fast_exp2(mi - M);
-    acc0 = __builtin_fmaf(w, o.x, acc0);
-    acc1 = __builtin_fmaf(w, o.y, acc1);
-    acc2 = __builtin_fmaf(w, o.z, acc2);
-    acc3 = __builtin_fmaf(w, o.w, acc3);
-    lsum = __builtin_fmaf(w, li, lsum);
+    const float mn = fmaxf(m, mi);
+    // m = -inf at first: sc = 0 (equal maxima need no scaling, -inf included)
+    const float sc = m == mn ? 1.f : fast_exp2(m - mn), w = mi == mn ? 1.f : fast_exp2(mi - mn);
+    acc0 = __builtin_fmaf(w, o.x, acc0 * sc);
+    acc1 = __builtin_fmaf(w, o.y, acc1 * sc);
+    acc2 = __builtin_fmaf(w, o.z, acc2 * sc);
+    acc3 = __builtin_fmaf(w, o.w, acc3 * sc);
+    lsum = __builtin_fmaf(w, li, lsum * sc);
+    m = mn;
   }
   s_acc[r][c] = f32x4{acc0, acc1, acc2, acc3};
-  if (c == 0) s_l[r] = lsum;
+  if (c == 0) {
+    s_m[r] = m;
+    s_l[r] = lsum;
+  }
   __syncthreads();
   if (r == 0) {
+    float M = s_m[0];
+#pragma unroll
+    for (int rr = 1; rr < kMergeRows; ++rr) M = fmaxf(M, s_m[rr]);
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, L = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
+    for (int rr = 0; rr < kMergeRows; ++rr) {
+      const float sr = fast_exp2(s_m[rr] - M);  // rows with no partial: -inf, weight 0
       const f32x4 v = s_acc[rr][c];
-      o0 += v.x;
-      o1 += v.y;
-      o2 += v.z;
-      o3 += v.w;
-      L += s_l[rr];
+      o0 = __builtin_fmaf(sr, v.x, o0);
+      o1 = __builtin_fmaf(sr, v.y, o1);
+      o2 = __builtin_fmaf(sr, v.z, o2);
+      o3 = __builtin_fmaf(sr, v.w, o3);
+      L = __builtin_fmaf(sr, s_l[rr], L);
     }
     constexpr int QK = kQKind<KIND>;
     const float inv = kKv8<KIND> ? a.out_scale / L : 1.f / L;
@@ -955,7 +964,7 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
 
 // One workgroup per (pair, query head of the group).
 template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(256) void decode_chunk_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void decode_chunk_merge_kernel(AttnArgs a) {
   const int j = blockIdx.x % G, p = blockIdx.x / G;
   const int g = p % a.Hkv, b = p / a.Hkv;
   const int len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
@@ -1249,7 +1258,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
 // line and units follow it, so no two runs share a slot, and the slots of
 // one pair are LH apart.
 template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(256) void decode_balanced_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void decode_balanced_merge_kernel(AttnArgs a) {
   const int j = blockIdx.x % G, p = blockIdx.x / G;
   const int b = p / a.Hkv, g = p % a.Hkv;
   const int LH = line_heads<SRC>(a);
@@ -1281,14 +1290,14 @@ hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
                  stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
+    decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), dim3(kMergeThreads), 0, stream>>>(a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv));
   launch_timed(decode_chunk_kernel<KIND, G, SRC>, grid, block, 0u, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
-  decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), block, 0, stream>>>(a);
+  decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), dim3(kMergeThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
