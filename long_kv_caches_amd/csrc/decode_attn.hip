@@ -437,29 +437,33 @@ __device__ __forceinline__ void store_empty(const AttnArgs& a, int64_t head0) {
   }
 }
 
-constexpr int kMergeRows = 16;                 // partial rows a merge workgroup folds at once
-constexpr int kMergeThreads = 32 * kMergeRows;  // 32 lanes per row, 4 elements each
+// Partial rows a merge workgroup folds at once (32 lanes per row, 4 elements
+// each): more rows shorten each row's chain of loads when a few heads have many
+// partials, fewer rows keep large grids of heads with few partials cheap to
+// dispatch (measured on MI355X: 32768 heads of a paged batch took 74 us with
+// 16 rows and 21 us with 4; 128 hybrid heads 6.9 us with 8 rows and 6.2 with 16).
+__host__ __device__ constexpr int merge_rows(int heads) { return heads <= 1024 ? 16 : heads <= 8192 ? 8 : 4; }
 
 // Merges n_p >= 1 partials of query head j of a group (slots slot0 +
 // i * slot_step, i < n_p) into the final output and lse of head head0 + j:
 // out = sum_i w_i o_i / sum_i w_i l_i with w_i = 2^(m_i - M), M = max_i m_i.
-// Thread (c, r) of the kMergeThreads takes elements 4c .. 4c+3 of the
-// partials i = r, r + kMergeRows, ... in order, with a running maximum, so
+// Thread (c, r) of the 32 * ROWS takes elements 4c .. 4c+3 of the partials
+// i = r, r + ROWS, ... in order, with a running maximum, so
 // each partial is read once; the rows are then scaled to the common maximum
 // and added in the order r = 0, 1, ..., so the result does not depend on timing.
-template <int KIND, int G>
+template <int KIND, int G, int ROWS>
 __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot0, int slot_step,
                            int n_p) {
-  __shared__ float s_m[kMergeRows];
-  __shared__ f32x4 s_acc[kMergeRows][32];
-  __shared__ float s_l[kMergeRows];
+  __shared__ float s_m[ROWS];
+  __shared__ f32x4 s_acc[ROWS][32];
+  __shared__ float s_l[ROWS];
   const int tid = threadIdx.x, c = tid & 31, r = tid >> 5;
-  // row r folds partials r, r + kMergeRows, ... with a running maximum (one
+  // row r folds partials r, r + ROWS, ... with a running maximum (one
   // pass over the partials: their maxima and outputs are read together)
   float m = -INFINITY;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, lsum = 0.f;
 #pragma unroll 4
-  for (int i = r; i < n_p; i += kMergeRows) {
+  for (int i = r; i < n_p; i += ROWS) {
     const int64_t sj = (slot0 + (int64_t)i * slot_step) * G + j;
     const float mi = a.ws_ml[sj * 2], li = a.ws_ml[sj * 2 + 1];
     const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + sj * kHeadDim + 4 * c);
@@ -482,10 +486,10 @@ __device__ void merge_head(const AttnArgs& a, int64_t head0, int j, int64_t slot
   if (r == 0) {
     float M = s_m[0];
 #pragma unroll
-    for (int rr = 1; rr < kMergeRows; ++rr) M = fmaxf(M, s_m[rr]);
+    for (int rr = 1; rr < ROWS; ++rr) M = fmaxf(M, s_m[rr]);
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, L = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < kMergeRows; ++rr) {
+    for (int rr = 0; rr < ROWS; ++rr) {
       const float sr = fast_exp2(s_m[rr] - M);  // rows with no partial: -inf, weight 0
       const f32x4 v = s_acc[rr][c];
       o0 = __builtin_fmaf(sr, v.x, o0);
@@ -963,14 +967,14 @@ __global__ __launch_bounds__(256) void decode_chunk_kernel(AttnArgs a) {
 }
 
 // One workgroup per (pair, query head of the group).
-template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(kMergeThreads) void decode_chunk_merge_kernel(AttnArgs a) {
+template <int KIND, int G, int SRC, int ROWS>
+__global__ __launch_bounds__(32 * ROWS) void decode_chunk_merge_kernel(AttnArgs a) {
   const int j = blockIdx.x % G, p = blockIdx.x / G;
   const int g = p % a.Hkv, b = p / a.Hkv;
   const int len = __builtin_amdgcn_readfirstlane(pair_len<SRC>(a, b, g));
   const int n_c = (len + a.chunk - 1) / a.chunk;
   if (n_c <= 1) return;  // written by the chunk kernel
-  merge_head<KIND, G>(a, (int64_t)b * a.Hq + (int64_t)g * G, j, (int64_t)p * a.n_chunks, 1, n_c);
+  merge_head<KIND, G, ROWS>(a, (int64_t)b * a.Hq + (int64_t)g * G, j, (int64_t)p * a.n_chunks, 1, n_c);
 }
 
 // ---------------------------------------------------------------------------
@@ -1257,8 +1261,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
 // and unit u for line head h is slot (k + u) * LH + h: items grow along the
 // line and units follow it, so no two runs share a slot, and the slots of
 // one pair are LH apart.
-template <int KIND, int G, int SRC>
-__global__ __launch_bounds__(kMergeThreads) void decode_balanced_merge_kernel(AttnArgs a) {
+template <int KIND, int G, int SRC, int ROWS>
+__global__ __launch_bounds__(32 * ROWS) void decode_balanced_merge_kernel(AttnArgs a) {
   const int j = blockIdx.x % G, p = blockIdx.x / G;
   const int b = p / a.Hkv, g = p % a.Hkv;
   const int LH = line_heads<SRC>(a);
@@ -1273,13 +1277,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_balanced_merge_kernel(At
   const ItemLine L = item_line(a, a.ws_pref[a.n_units], LH);
   const int k0 = L.of_tile(ubase), k1 = L.of_tile(uend - 1);  // columns, each non-empty
   if (k0 == k1) return;  // one item covered the pair and wrote the output
-  merge_head<KIND, G>(a, head0, j, (int64_t)(k0 + u) * LH + h, LH, k1 - k0 + 1);
+  merge_head<KIND, G, ROWS>(a, head0, j, (int64_t)(k0 + u) * LH + h, LH, k1 - k0 + 1);
 }
 
 
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
+
+// One merge workgroup per query head, with merge_rows(heads) rows.
+template <void (*K16)(AttnArgs), void (*K8)(AttnArgs), void (*K4)(AttnArgs)>
+hipError_t launch_merge(int heads, const AttnArgs& a, hipStream_t stream) {
+  const int rows = merge_rows(heads);
+  const dim3 grid((unsigned)heads), block((unsigned)(32 * rows));
+  if (rows == 16) K16<<<grid, block, 0, stream>>>(a);
+  else if (rows == 8) K8<<<grid, block, 0, stream>>>(a);
+  else K4<<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 template <int KIND, int G, int SRC>
 hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
@@ -1290,15 +1305,15 @@ hipError_t launch_src(const AttnArgs& a, hipStream_t stream) {
                  stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_balanced_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), dim3(kMergeThreads), 0, stream>>>(a);
-    return hipGetLastError();
+    return launch_merge<decode_balanced_merge_kernel<KIND, G, SRC, 16>, decode_balanced_merge_kernel<KIND, G, SRC, 8>,
+                        decode_balanced_merge_kernel<KIND, G, SRC, 4>>(a.B * a.Hkv * G, a, stream);
   }
   const dim3 grid((unsigned)((int64_t)a.B * a.n_chunks * a.Hkv));
   launch_timed(decode_chunk_kernel<KIND, G, SRC>, grid, block, 0u, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
-  decode_chunk_merge_kernel<KIND, G, SRC><<<dim3((unsigned)(a.B * a.Hkv * G)), dim3(kMergeThreads), 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_merge<decode_chunk_merge_kernel<KIND, G, SRC, 16>, decode_chunk_merge_kernel<KIND, G, SRC, 8>,
+                      decode_chunk_merge_kernel<KIND, G, SRC, 4>>(a.B * a.Hkv * G, a, stream);
 }
 
 template <int KIND, int G, int SRC>
