@@ -136,6 +136,14 @@ def test_paged_bitwise_equals_ragged():
 def test_paged_mha_reduced_batch():
     d = kvgen.paged_mha(seed=10, B=96)
     _parity(d, "paged Llama-2-7B MHA, B=96")
+    _parity(d, "paged Llama-2-7B MHA, B=96", split_tokens=256)  # 3072 heads: 8-row merge
+
+
+def test_merge_of_many_short_heads():
+    # 260 x 32 = 8320 query heads: the merge folds 4 rows of partials per head
+    d = kvgen.dense_small(seed=17, B=260, Hq=32, Hkv=16, S=256)
+    _parity(d, "dense 260x32/16x256", split_tokens=64)
+    _parity(d, "dense 260x32/16x256")
 
 
 def test_page_size_32():
