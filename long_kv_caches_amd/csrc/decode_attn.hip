@@ -1078,7 +1078,7 @@ __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) 
   ItemLine L;
   L.N = N;
   L.Wc = min(a.n_blocks * kWaves / LH, N);
-  L.C0 = min(L.Wc, (a.n_cu * kWaves + LH - 1) / LH);  // columns whose first wave is in round 0
+  L.C0 = min(L.Wc, (a.n_cu * kWaves + LH - 1) / LH);  // columns whose first wave is dispatched first
   const bool weighted = N >= 2 * L.Wc;
   L.w0 = weighted ? kFirstRoundWeight : 100;
   L.w1 = 100;

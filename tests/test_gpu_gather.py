@@ -93,22 +93,24 @@ def test_gather_e4m3(split):
     check_lse(gl, rl, "gather e4m3 lse")
 
 
-def topk_on_gpu(d, top_k):
+def topk_on_gpu(d, top_k, null_seqlens=False, dirty_workspace=False):
     B, Hq, Hkv, S = d["B"], d["Hq"], d["Hkv"], d["S"]
     desc = K.topk_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16, max_seqlen=S,
                        top_k=top_k)
     ws = K.alloc_workspace(K.kvdec_topk_select_workspace(desc))
+    if dirty_workspace:
+        ws.fill_(255)  # the selection must not depend on what the workspace held
     idx = torch.full((B, Hkv, max(top_k, 1)), -7, dtype=torch.int32, device="cuda")
     n = torch.full((B * Hkv,), -7, dtype=torch.int32, device="cuda")
-    sl = torch.from_numpy(np.asarray(d["seqlens"], np.int32)).cuda()
+    sl = None if null_seqlens else torch.from_numpy(np.asarray(d["seqlens"], np.int32)).cuda()
     K.kvdec_topk_select(desc, dev(d["q"]), dev(d["k"]), sl, idx, n, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), n.cpu().numpy()
 
 
-def check_topk(d, top_k, what, pairs=None):
+def check_topk(d, top_k, what, pairs=None, **gpu_kw):
     say(f"[topk] {what} top_k={top_k}")
-    gi, gn = topk_on_gpu(d, top_k)
+    gi, gn = topk_on_gpu(d, top_k, **gpu_kw)
     q, k = d["q"], d["k"]
     sl = np.asarray(d["seqlens"])
     if pairs is not None:  # check a sample of (b, g) pairs (the oracle on those sequences only)
@@ -189,6 +191,24 @@ def test_topk_chunks_and_ties_across_chunk_boundaries():
     gi, gn = check_topk(d, 40000, "S=40000 keep all")
     assert np.array_equal(gi[0, 0, :40000], np.arange(40000))
     assert np.array_equal(gi[1, 7, :33000], np.arange(33000))
+
+
+def test_topk_null_seqlens_and_dirty_workspace():
+    # seqlens NULL: every sequence has all S rows (two selection chunks); the
+    # workspace holds all-ones bytes before the call (it needs no initialisation)
+    d = _model_small("llama3-8b", 73, S=20000, lens=(20000, 20000))
+    for top_k in (1, 2500, 19999):
+        check_topk(d, top_k, "S=20000 seqlens NULL", null_seqlens=True, dirty_workspace=True)
+
+
+def test_topk_no_rows():
+    # max_seqlen 0: only the counts are written; q, k, idx and the workspace may be NULL
+    desc = K.topk_desc(batch=3, num_q_heads=8, num_kv_heads=2, dtype=torch.float16, max_seqlen=0,
+                       top_k=5)
+    n = torch.full((6,), -7, dtype=torch.int32, device="cuda")
+    K.kvdec_topk_select(desc, None, None, None, None, n, None)
+    torch.cuda.synchronize()
+    assert n.cpu().numpy().tolist() == [0] * 6
 
 
 def test_topk_then_gather_end_to_end():
