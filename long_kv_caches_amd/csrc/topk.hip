@@ -471,8 +471,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_write_kernel(TopkArgs a) {
     for (int e = 0; e < 4; ++e) sel[e] = gt[u][e] || (eq[u][e] && s_seg_eq[s] + er[e] < take_eq);
     seg_ranks(sel, lane, sr, &dummy);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (sel[e]) out[s_seg_gt[s] + sr[e]] = t + e;
+    for (int e = 0; e < 4; ++e) {
+      const int pos = s_seg_gt[s] + sr[e];  // < need by construction; checked so no write leaves the row
+      if (sel[e] && pos < need) out[pos] = t + e;
+    }
   }
 }
 
