@@ -20,7 +20,7 @@ import torch
 import kvgen
 import long_kv_caches_amd as K
 import oracle
-from gpu_util import check_close, check_lse, dev, host_f64, say
+from gpu_util import check_close, check_lse, dev, host_f64, say, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -93,32 +93,34 @@ def test_gather_e4m3(split):
     check_lse(gl, rl, "gather e4m3 lse")
 
 
-def topk_on_gpu(d, top_k, null_seqlens=False, dirty_workspace=False):
+def topk_on_gpu(d, top_k, null_seqlens=False, dirty_workspace=False, bf16=False):
     B, Hq, Hkv, S = d["B"], d["Hq"], d["Hkv"], d["S"]
-    desc = K.topk_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16, max_seqlen=S,
-                       top_k=top_k)
+    desc = K.topk_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv,
+                       dtype=torch.bfloat16 if bf16 else torch.float16, max_seqlen=S, top_k=top_k)
+    conv = to_bf16_bits if bf16 else (lambda x: x)
     ws = K.alloc_workspace(K.kvdec_topk_select_workspace(desc))
     if dirty_workspace:
         ws.fill_(255)  # the selection must not depend on what the workspace held
     idx = torch.full((B, Hkv, max(top_k, 1)), -7, dtype=torch.int32, device="cuda")
     n = torch.full((B * Hkv,), -7, dtype=torch.int32, device="cuda")
     sl = None if null_seqlens else torch.from_numpy(np.asarray(d["seqlens"], np.int32)).cuda()
-    K.kvdec_topk_select(desc, dev(d["q"]), dev(d["k"]), sl, idx, n, ws)
+    K.kvdec_topk_select(desc, dev(conv(d["q"]), bf16), dev(conv(d["k"]), bf16), sl, idx, n, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), n.cpu().numpy()
 
 
-def check_topk(d, top_k, what, pairs=None, **gpu_kw):
-    say(f"[topk] {what} top_k={top_k}")
-    gi, gn = topk_on_gpu(d, top_k, **gpu_kw)
-    q, k = d["q"], d["k"]
+def check_topk(d, top_k, what, pairs=None, bf16=False, **gpu_kw):
+    say(f"[topk] {what} top_k={top_k} bf16={bf16}")
+    gi, gn = topk_on_gpu(d, top_k, bf16=bf16, **gpu_kw)
+    q, k = (to_bf16_bits(d["q"]), to_bf16_bits(d["k"])) if bf16 else (d["q"], d["k"])
+    kind = oracle.BF16 if bf16 else oracle.F16
     sl = np.asarray(d["seqlens"])
     if pairs is not None:  # check a sample of (b, g) pairs (the oracle on those sequences only)
         bs = sorted({p // d["Hkv"] for p in pairs})
     else:
         bs = list(range(d["B"]))
-    s, m = oracle.topk_scores(q[bs], k[bs], num_kv_heads=d["Hkv"], seqlens=sl[bs])
-    oi, on = oracle.topk_select(q[bs], k[bs], top_k, num_kv_heads=d["Hkv"], seqlens=sl[bs])
+    s, m = oracle.topk_scores(q[bs], k[bs], num_kv_heads=d["Hkv"], seqlens=sl[bs], kind=kind)
+    oi, on = oracle.topk_select(q[bs], k[bs], top_k, num_kv_heads=d["Hkv"], seqlens=sl[bs], kind=kind)
     G = d["Hq"] // d["Hkv"]
     swaps = 0
     for bi, b in enumerate(bs):
@@ -164,6 +166,15 @@ def test_topk_head_layouts(Hq, Hkv):
     d = kvgen.dense_small(seed=71 + Hkv, B=3, Hq=Hq, Hkv=Hkv, S=777, seqlens=[777, 500, 3])
     for top_k in (1, 100, 600):
         check_topk(d, top_k, f"Hq={Hq} Hkv={Hkv} S=777")
+
+
+@pytest.mark.parametrize("Hq,Hkv,S,lens", [(32, 8, 17000, (17000, 12345)), (65, 65, 777, (777, 300))])
+def test_topk_bf16(Hq, Hkv, S, lens):
+    # bf16 K and q: the whole-row score pass over two selection chunks, and
+    # the one-head-at-a-time pass (more than 64 KV heads)
+    d = kvgen.dense_small(seed=74 + Hkv, B=2, Hq=Hq, Hkv=Hkv, S=S, seqlens=list(lens))
+    for top_k in (1, 250, 3000):
+        check_topk(d, top_k, f"bf16 Hq={Hq} Hkv={Hkv} S={S}", bf16=True)
 
 
 def test_topk_ties_go_to_smaller_tokens():
