@@ -25,16 +25,18 @@ from gpu_util import check_close, check_lse, dev, host_f64, say, to_bf16_bits
 pytestmark = pytest.mark.gpu
 
 
-def gather_on_gpu(d, idx, n, split=0, fp8=False):
+def gather_on_gpu(d, idx, n, split=0, fp8=False, bf16=False):
     B, Hq, Hkv, S = d["B"], d["Hq"], d["Hkv"], d["S"]
     fmt = dict(kv_format=K.KVDEC_KV_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if fp8 else {}
-    desc = K.gather_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16, max_seqlen=S,
+    dt = torch.bfloat16 if bf16 else torch.float16
+    c = (lambda x: dev(to_bf16_bits(x), True)) if bf16 else dev
+    desc = K.gather_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=dt, max_seqlen=S,
                          softmax_scale=d["scale"], split_tokens=split, max_k=idx.shape[2], **fmt)
     ws = K.alloc_workspace(K.kvdec_gather_attn_workspace(desc))
-    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=dt, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
-    K.kvdec_gather_attn(desc, dev(d["q"]), dev(d["k"]), dev(d["v"]), i32(idx), i32(n), out, lse, ws)
+    K.kvdec_gather_attn(desc, c(d["q"]), c(d["k"]), c(d["v"]), i32(idx), i32(n), out, lse, ws)
     torch.cuda.synchronize()
     return host_f64(out), lse.cpu().numpy()
 
@@ -53,6 +55,19 @@ def test_gather_random_indices(model, split):
     ro, rl = oracle.gather_attn(d["q"], d["k"], d["v"], idx, n, num_kv_heads=d["Hkv"], scale=d["scale"])
     check_close(go, ro, "gather")
     check_lse(gl, rl, "gather lse")
+
+
+def test_gather_bf16():
+    d = _model_small("llama3-8b", 75)
+    idx, n = kvgen.random_indices(76, d["B"], d["Hkv"], d["seqlens"], 300)
+    c = to_bf16_bits
+    ro, rl = oracle.gather_attn(c(d["q"]), c(d["k"]), c(d["v"]), idx, n, num_kv_heads=8, scale=d["scale"],
+                                kind=oracle.BF16)
+    for split in (0, 128):
+        say(f"[gather] bf16 split={split}")
+        go, gl = gather_on_gpu(d, idx, n, split=split, bf16=True)
+        check_close(go, ro, f"gather bf16 split={split}", bf16_out=True)
+        check_lse(gl, rl, "gather bf16 lse")
 
 
 def test_gather_unsorted_and_repeated_indices():

@@ -6,35 +6,39 @@ import torch
 import kvgen
 import long_kv_caches_amd as K
 import oracle
-from gpu_util import bits, check_close, check_lse, decode_on_gpu, dev, host_f64, say
+from gpu_util import bits, check_close, check_lse, decode_on_gpu, dev, host_f64, say, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
 
-def hybrid_on_gpu(d, split_tokens=0, head_map=None):
+def hybrid_on_gpu(d, split_tokens=0, head_map=None, bf16=False):
     hm = d["head_map"] if head_map is None else head_map
     B, Hq, Hkv = d["B"], d["Hq"], d["Hkv"]
     fp8 = d["pers_k"].dtype == np.uint8
     fmt = dict(kv_format=K.KVDEC_KV_E4M3, k_scale=d["k_scale"], v_scale=d["v_scale"]) if fp8 else {}
-    desc = K.hybrid_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=torch.float16,
+    dt = torch.bfloat16 if bf16 else torch.float16
+    c = (lambda x: dev(to_bf16_bits(x), True)) if bf16 else dev
+    desc = K.hybrid_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, dtype=dt,
                          softmax_scale=d["scale"], split_tokens=split_tokens,
                          num_pers_slots=d["pers_k"].shape[1], pers_cap=d["pers_k"].shape[2],
                          buf_cap=d["buf_k"].shape[2], **fmt)
     ws = K.alloc_workspace(K.kvdec_sparse_hybrid_attn_workspace(desc))
-    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=dt, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).cuda()
-    K.kvdec_sparse_hybrid_attn(desc, dev(d["q"]), dev(d["pers_k"]), dev(d["pers_v"]),
-                               i32(d["pers_len"]), dev(d["buf_k"]), dev(d["buf_v"]),
+    K.kvdec_sparse_hybrid_attn(desc, c(d["q"]), c(d["pers_k"]), c(d["pers_v"]),
+                               i32(d["pers_len"]), c(d["buf_k"]), c(d["buf_v"]),
                                i32(d["buf_len"]), i32(hm), out, lse, ws)
     torch.cuda.synchronize()
     return out, lse.cpu().numpy()
 
 
-def hybrid_oracle(d, head_map=None):
+def hybrid_oracle(d, head_map=None, bf16=False):
     hm = d["head_map"] if head_map is None else head_map
-    return oracle.hybrid_attn(d["q"], d["pers_k"], d["pers_v"], d["pers_len"], d["buf_k"],
-                              d["buf_v"], d["buf_len"], hm, scale=d["scale"],
+    c = to_bf16_bits if bf16 else (lambda x: x)
+    return oracle.hybrid_attn(c(d["q"]), c(d["pers_k"]), c(d["pers_v"]), d["pers_len"], c(d["buf_k"]),
+                              c(d["buf_v"]), d["buf_len"], hm, scale=d["scale"],
+                              kind=oracle.BF16 if bf16 else oracle.F16,
                               k_scale=d.get("k_scale"), v_scale=d.get("v_scale"))
 
 
@@ -47,6 +51,19 @@ def test_hybrid_reduced_context(model):
         ro, rl = hybrid_oracle(d)
         check_close(host_f64(out), ro, f"hybrid {model} split={split}")
         check_lse(lse, rl)
+
+
+def test_hybrid_bf16():
+    # bf16 q, K and V (the output is bf16), at G = 4 (Llama3-8B heads) and
+    # G = 5 (Qwen2.5-14B heads), both on the matrix-core tile path
+    for model in ("llama3-8b", "qwen2.5-14b"):
+        d = kvgen.clo_hybrid(seed=6, model=model, B=2, S=4096)
+        ro, rl = hybrid_oracle(d, bf16=True)
+        for split in (0, 128):
+            say(f"[hybrid] bf16 {model} split={split}")
+            out, lse = hybrid_on_gpu(d, split, bf16=True)
+            check_close(host_f64(out), ro, f"hybrid bf16 {model} split={split}", bf16_out=True)
+            check_lse(lse, rl)
 
 
 def _dense_view(kf, vf, d, rows=None):
