@@ -493,7 +493,7 @@ def bench_gather(args, K, np, torch, dev, stream):
     tokens = int(d["seqlens"].sum())
     score_bytes = tokens * Hkv * D * 2 + tokens * Hkv * 4
     r["topk_select"] = {"us_per_call": round(sms * 1e3, 2),
-                        "kernels": "topk_score_rows_kernel + topk_radix_kernel<0..2> + topk_write_kernel",
+                        "kernels": "topk_score_rows_kernel + topk_radix_kernel<0..2> + topk_final_kernel + topk_write_kernel",
                         "kernel_us_per_call": round(skern_us * slaunches / max(args.steps, 1), 2),
                         "score_pass_bytes": score_bytes,
                         "score_pass_gbs_over_call": round(score_bytes / (sms * 1e-3) / 1e9, 1)}

@@ -363,9 +363,9 @@ kvdec_status kvdec_kvpr_load_layer(int32_t b, int32_t l, int32_t s_prime, int32_
  * start and its end, with no extra packets on the stream.  Main kernels: the
  * split kernel of an attention call (not the merge kernel), the lookup kernel
  * of kvdec_headcache_lookup (not the compaction kernel), the projection of
- * kvdec_headcache_lookup_ahead, each of the five kernels of
- * kvdec_topk_select (the score pass, three radix-digit passes and the
- * compaction), the GEMM of kvdec_kv_recompute and of
+ * kvdec_headcache_lookup_ahead, each of the six kernels of
+ * kvdec_topk_select (the score pass, three radix-digit passes, the threshold
+ * and the compaction), the GEMM of kvdec_kv_recompute and of
  * kvdec_kvpr_load_layer.
  * kvdec_kernel_timing(1) starts a new measurement (the library keeps and
  * reuses its events); kvdec_kernel_timing(0) stops recording.

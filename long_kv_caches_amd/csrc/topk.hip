@@ -21,16 +21,20 @@
 //     4 * (l / 16) .. +3, the query sum in fp32 for its piece.
 //   topk_radix_kernel<0..2> -- a radix select of the k-th largest orderable
 //     key in three digits of 11, 11 and 10 bits, one 1024-thread workgroup per
-//     16K-token chunk of a pair (LDS histogram of the chunk's keys that match
-//     the prefix so far); the chunk that finishes last adds the chunks'
-//     histograms and picks the digit.  The last digit's pass also leaves each
-//     chunk's count of keys above and equal to the threshold before it.
+//     16K-token chunk of a pair: an LDS histogram of the chunk's keys that match
+//     the prefix so far, added to the pair's merged histogram with atomics; the
+//     next kernel's first wave picks the digit from it.  The low pass also keeps
+//     each chunk's own histogram and its keys above the 22-bit prefix.
+//   topk_final_kernel -- per pair: the threshold key T, the count of keys equal
+//     to it to keep, and each chunk's keys above and equal to T before it.
 //   topk_write_kernel -- the ordered compaction of each chunk: per 256-token
 //     segment (lane l: tokens 4l .. 4l+3) ballots count the keys above the
 //     threshold and those equal to it, a scan over the chunk's segments gives
 //     each its output offset and its ties before it, and the selected indices
 //     are written in order.  Every pass reads the chunk's scores with 16-byte
 //     loads, 16 keys per thread.
+// No workgroup waits for another: each read of other workgroups' counts is in
+// a later kernel.
 #include "device_common.h"
 #include "internal.h"
 
@@ -53,10 +57,10 @@ struct SelPair {
   uint32_t* h0;      // [2048] keys per top digit (bits 21..31)
   uint32_t* h1;      // [2048] per middle digit (bits 10..20), keys under the chosen top digit
   uint32_t* h2;      // [1024] per low digit (bits 0..9), keys under the chosen 22-bit prefix
-  uint32_t* state;   // [8]: after the middle pass prefix, mask, remaining, -; after the low
-                     // pass prefix, mask, remaining, -
-  uint32_t* chunks;  // [chunks, 1028]: each chunk's low-digit histogram, then its keys above
-                     // the 22-bit prefix
+  uint32_t* state;   // [8]: after the middle pass prefix, mask, remaining, then T; after the
+                     // low pass prefix, mask, remaining, then the keys equal to T to keep
+  uint32_t* chunks;  // [chunks, 1028]: each chunk's low-digit histogram, its keys above the
+                     // 22-bit prefix, then the keys above T and equal to T before the chunk
 };
 
 __device__ __forceinline__ SelPair sel_pair(const TopkArgs& a, int pair) {
@@ -383,6 +387,48 @@ __global__ __launch_bounds__(kSelThreads) void topk_radix_kernel(TopkArgs a) {
   if (P == 2 && tid == 0) sp.chunks[c * 1028 + 1024] = s_above;
 }
 
+// The threshold of a pair, after the three digit passes: its low digit from
+// the merged low histogram gives T, the need-th largest key, and the count of
+// keys equal to T to keep; the chunks' own low histograms give each chunk's
+// keys above T and equal to T, whose exclusive sums over the chunks before it
+// the compaction needs.  One workgroup per pair.
+__global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkArgs a) {
+  __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_cnt[kSelWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pair = blockIdx.x, b = pair / a.Hkv;
+  const int len = min(max(a.seqlens ? a.seqlens[b] : a.S, 0), a.S);
+  const int need = min(a.top_k, len);
+  if (need == 0 || need == len) return;  // written by the first pass
+  const int nchunks = (len + kSelChunk - 1) / kSelChunk;
+  const SelPair sp = sel_pair(a, pair);
+  if (wave == 0) find_digit<1024>(sp.h2, sp.state[6], lane, &s_sel[0], &s_sel[1]);
+  __syncthreads();
+  const uint32_t d = s_sel[0];
+  if (wave < nchunks) {  // wave w: chunk w's keys above T and equal to T
+    const uint32_t* h = sp.chunks + wave * 1028;
+    uint32_t gt = 0;
+    for (int i = (int)d + 1 + lane; i < 1024; i += 64) gt += h[i];
+    gt = wave_sum_u32(gt);
+    if (lane == 0) {
+      s_cnt[wave][0] = gt + h[1024];
+      s_cnt[wave][1] = h[d];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t gt_run = 0, eq_run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      sp.chunks[c * 1028 + 1025] = gt_run;
+      sp.chunks[c * 1028 + 1026] = eq_run;
+      gt_run += s_cnt[c][0];
+      eq_run += s_cnt[c][1];
+    }
+    sp.state[3] = sp.state[4] | d;  // T
+    sp.state[7] = s_sel[1];         // keys equal to T to keep
+  }
+}
+
 // Ordered compaction of one chunk: the keys above T, and the first keys equal
 // to T in token order up to the count to keep, written in ascending token
 // order at the chunk's offset.  Per 256-token segment, ballots count both
@@ -399,30 +445,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_write_kernel(TopkArgs a) {
   if (c >= nchunks) return;
   const SelPair sp = sel_pair(a, pair);
   f32x4 v[4];
-  load_chunk(a, pair, len, c, wave, lane, v);  // in flight while the threshold is found
-  __shared__ uint32_t s_sel[2];
-  __shared__ int s_cnt[kSelWaves][2];
-  if (wave == 0) find_digit<1024>(sp.h2, sp.state[6], lane, &s_sel[0], &s_sel[1]);
-  __syncthreads();
-  const uint32_t d = s_sel[0];
-  const uint32_t T = sp.state[4] | d;  // the need-th largest key
-  const int take_eq = (int)s_sel[1];   // keys equal to T to keep, lowest tokens first
-  if (wave < c) {  // wave w: chunk w's keys above T and equal to T
-    const uint32_t* h = sp.chunks + wave * 1028;
-    uint32_t gt = 0;
-    for (int i = (int)d + 1 + lane; i < 1024; i += 64) gt += h[i];
-    gt = wave_sum_u32(gt);
-    if (lane == 0) {
-      s_cnt[wave][0] = (int)(gt + h[1024]);
-      s_cnt[wave][1] = (int)h[d];
-    }
-  }
-  __syncthreads();
-  int gt_before = 0, eq_before = 0;  // in the chunks before this one
-  for (int w = 0; w < c; ++w) {
-    gt_before += s_cnt[w][0];
-    eq_before += s_cnt[w][1];
-  }
+  load_chunk(a, pair, len, c, wave, lane, v);  // in flight while the threshold is read
+  const uint32_t T = sp.state[3];          // the need-th largest key
+  const int take_eq = (int)sp.state[7];     // keys equal to T to keep, lowest tokens first
+  const int gt_before = (int)sp.chunks[c * 1028 + 1025];  // keys above T in the chunks before
+  const int eq_before = (int)sp.chunks[c * 1028 + 1026];  // keys equal to T in the chunks before
   int32_t* out = a.idx + (int64_t)pair * a.top_k;
   bool gt[4][4], eq[4][4];
 #pragma unroll
@@ -501,6 +528,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   launch_timed(topk_radix_kernel<0>, cgrid, dim3(kSelThreads), 0u, stream, a);
   launch_timed(topk_radix_kernel<1>, cgrid, dim3(kSelThreads), 0u, stream, a);
   launch_timed(topk_radix_kernel<2>, cgrid, dim3(kSelThreads), 0u, stream, a);
+  launch_timed(topk_final_kernel, dim3((unsigned)pairs), dim3(kSelThreads), 0u, stream, a);
   launch_timed(topk_write_kernel, cgrid, dim3(kSelThreads), 0u, stream, a);
   return hipGetLastError();
 }
