@@ -152,6 +152,12 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* desc, const void* q, const
  *   head_map [Hkv] int32: slot >= 0 reads persistent slot `slot` (rows
  *   0..pers_len[b]-1), -1 reads the cache buffer of that KV head (rows
  *   0..buf_len[b*Hkv+g]-1, the selected tokens compacted in any order).
+ *   The metadata lives on the device, so the host cannot check it before the
+ *   launch.  The kernels clamp instead of faulting: a slot >= num_pers_slots
+ *   makes that head empty (out = 0, lse = -inf), and lengths are clamped into
+ *   [0, pers_cap] and [0, buf_cap].  With KVDEC_CHECK=1 in the environment the
+ *   call copies the metadata to the host first and rejects such values with
+ *   KVDEC_ERR_INVALID, launching nothing (see kvdec_check_enabled).
  * The result for each KV head equals kvdec_decode_attn over the rows it reads.
  */
 typedef struct {

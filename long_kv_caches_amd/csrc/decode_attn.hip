@@ -565,7 +565,8 @@ struct VecPath {
   }
 };
 
-// Matrix-core path, for e4m3 K/V (3 <= G <= 8 query heads, padded to 16).
+// Matrix-core path, for every K/V format (fp16, bf16, e4m3) at 3 <= G <= 8
+// query heads, padded to 16.
 //   Scores: S[token][head] by four v_mfma_f32_16x16x32 (f16 or bf16, the
 //   query's type): A = K (lane l: token l%16, dims 32*(l/16) .. +31 of the
 //   row, widened from its 32 codes), B = q (lane l: head l%16, the same

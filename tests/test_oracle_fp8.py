@@ -104,3 +104,24 @@ def test_generator_codes_round_to_nearest():
     nearest = np.abs(t[:, None].astype(np.float64) - grid[None, :]).min(axis=1)
     assert np.all(np.abs(t - vals) <= nearest + 1e-12)
     assert np.abs(vals).max() == 448.0
+
+
+def test_fp8_hybrid_mixed_head_map_equals_16bit_hybrid():
+    # Both branches with e4m3 codes: the 16-bit hybrid (pinned on its own) over
+    # the same values, bit for bit.  Slots differ from head indices and every
+    # (b, g) buffer has its own length.
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, D, P, pcap, bcap = 2, 8, 4, 128, 2, 30, 12
+    pk8, pv8 = _random_codes(rng, (B, P, pcap, D)), _random_codes(rng, (B, P, pcap, D))
+    bk8, bv8 = _random_codes(rng, (B, Hkv, bcap, D)), _random_codes(rng, (B, Hkv, bcap, D))
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    head_map = np.array([-1, 1, -1, 0], np.int32)
+    pers_len = np.array([30, 7], np.int32)
+    buf_len = np.array([0, 3, 12, 5, 9, 1, 11, 2], np.int32)
+    ks, vs = 0.25, 2.0
+    w16 = lambda c, s: (oracle.widen_e4m3(c) * s).astype(np.float16)
+    o8, l8 = oracle.hybrid_attn(q, pk8, pv8, pers_len, bk8, bv8, buf_len, head_map, scale=0.07,
+                                k_scale=ks, v_scale=vs)
+    o16, l16 = oracle.hybrid_attn(q, w16(pk8, ks), w16(pv8, vs), pers_len, w16(bk8, ks),
+                                  w16(bv8, vs), buf_len, head_map, scale=0.07)
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)

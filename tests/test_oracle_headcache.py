@@ -5,6 +5,7 @@ import math
 import os
 
 import numpy as np
+import pytest
 from scipy.spatial.distance import cosine as scipy_cosine_distance
 
 import kvgen
@@ -235,3 +236,54 @@ def test_clo_ahead_drift_sets_cosines():
     cos = (qa * ql).sum(1) / np.linalg.norm(qa, axis=1) / np.linalg.norm(ql, axis=1)
     expect = 1.0 / np.sqrt(1.0 + d["drift"].astype(np.float64) ** 2)
     assert np.all(np.abs(cos - expect) < 0.06), (cos, expect)
+
+
+def _bits(values, kind):
+    """16-bit patterns of values exactly representable in fp16 and bf16."""
+    v = np.asarray(values, np.float64)
+    if kind == oracle.F16:
+        out = v.astype(np.float16)
+        assert np.array_equal(out.astype(np.float64), v)
+        return out.view(np.uint16)
+    f = v.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), v)
+    u = f.view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", [oracle.F16, oracle.BF16])
+@pytest.mark.parametrize("case", ["cos_one", "cos_half", "eq10_mix"])
+def test_aggregate_equal_to_tau_is_a_hit(kind, case):
+    # CLO page, section 2: a head hits when its cosine reaches tau (>=).  The
+    # inputs make the fp64 aggregate exactly a float32 value:
+    #   cos_one : q = label = 2 e0 -> c = 4 / (2 * 2) = 1
+    #   cos_half: q = e0, label = e0 + e1 + e2 + e3 -> c = 1 / (1 * 2) = 1/2
+    #   eq10_mix: heads with c = 1/2 and c = 1, weights 1/4 and 3/4 ->
+    #             a = (1/8 + 3/4) / 1 = 7/8 (Eq. 10)
+    # tau = a must hit, the next float32 above a must miss, the one below hit.
+    D = 128
+    e = np.eye(D)
+    half_q, half_l = e[0], e[0] + e[1] + e[2] + e[3]
+    if case == "cos_one":
+        qv, lv, w, a = [2 * e[0]], [2 * e[0]], [1.0], 1.0
+    elif case == "cos_half":
+        qv, lv, w, a = [half_q], [half_l], [0.5], 0.5
+    else:
+        qv, lv, w, a = [half_q, 2 * e[0]], [half_l, 2 * e[0]], [0.25, 0.75], 0.875
+    G = len(qv)
+    q = _bits(np.array(qv)[None], kind)
+    lab = _bits(np.array(lv)[None], kind)
+    w = np.array(w, np.float32)
+    a32 = np.float32(a)
+    assert float(a32) == a
+    for tau, want in ((a32, 1), (np.nextafter(a32, np.float32(2)), 0),
+                      (np.nextafter(a32, np.float32(-2)), 1)):
+        r = oracle.headcache_lookup(q, lab, w, np.array([tau], np.float32), num_kv_heads=1,
+                                    kind=kind)
+        assert r["agg"][0, 0] == a
+        assert r["hit"][0, 0] == want, (case, float(tau))
+        assert r["miss_count"] == 1 - want
+        # a miss replaces every label of the group with q; a hit keeps them
+        assert np.array_equal(r["labels"], q if want == 0 else lab)
+        assert G == r["cos"].shape[1]
