@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 8
+#define KVDEC_ABI_VERSION 9
 
 typedef enum {
   KVDEC_OK = 0,
@@ -137,6 +137,25 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* desc, const void* q, const
                                const void* v, const int32_t* seqlens, const int32_t* cu_seqlens,
                                const int32_t* block_table, void* out, float* lse,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kvdec_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same operation, kernels and results
+ * (bit for bit) as kvdec_decode_attn; the partials live in a library-owned
+ * device array of KVDEC_NOALLOC_SCRATCH_BYTES per GPU, set up on the call's
+ * first use on a device and held until the process ends.  The call allocates
+ * nothing.  A descriptor whose workspace (kvdec_decode_attn_workspace) exceeds
+ * that size returns KVDEC_ERR_WORKSPACE with nothing launched.  Every call on
+ * one GPU shares its array: calls that may overlap on one GPU (two streams,
+ * two threads) race on it and give wrong results; serialise them, or use
+ * kvdec_decode_attn with a workspace each.
+ */
+#define KVDEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvdec_status kvdec_decode_attn_noalloc(const kvdec_attn_desc* desc, const void* q, const void* k,
+                                       const void* v, const int32_t* seqlens,
+                                       const int32_t* cu_seqlens, const int32_t* block_table,
+                                       void* out, float* lse, hipStream_t stream);
 
 /*
  * CLO cache buffer + persistent cache attention (CLO page, section 7: the

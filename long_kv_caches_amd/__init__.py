@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     KVDEC_W_IN_OUT, KVDEC_W_OUT_IN,
     AttnDesc, HybridDesc,
     KvdecError, alloc_workspace, attn_desc, hybrid_desc, kvdec_decode_attn,
+    kvdec_decode_attn_noalloc, NOALLOC_SCRATCH_BYTES,
     kvdec_decode_attn_workspace, kvdec_headcache_lookup, kvdec_headcache_lookup_ahead,
     kvdec_headcache_thresholds,
     kvdec_kernel_timing, kvdec_kernel_timing_read, kvdec_kv_recompute, kvdec_kvpr_load_layer,

@@ -66,6 +66,7 @@ def _load():
     sig = {
         "kvdec_decode_attn_workspace": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)], st),
         "kvdec_decode_attn": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, sz, P], st),
+        "kvdec_decode_attn_noalloc": ([ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P], st),
         "kvdec_sparse_hybrid_attn_workspace": ([ctypes.POINTER(HybridDesc), ctypes.POINTER(sz)], st),
         "kvdec_sparse_hybrid_attn": ([ctypes.POINTER(HybridDesc), P, P, P, P, P, P, P, P, P, P, P,
                                       sz, P], st),
@@ -96,7 +97,9 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_sparse_hybrid_attn_workspace",
+NOALLOC_SCRATCH_BYTES = 32 << 20
+EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_decode_attn_noalloc",
+            "kvdec_sparse_hybrid_attn_workspace",
             "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_lookup_ahead",
             "kvdec_gather_attn_workspace", "kvdec_gather_attn", "kvdec_topk_select_workspace",
             "kvdec_topk_select",
@@ -268,6 +271,15 @@ def kvdec_decode_attn(desc, q, k, v, seqlens, cu_seqlens, block_table, out, lse,
     _check(lib.kvdec_decode_attn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(seqlens),
                                  _ptr(cu_seqlens), _ptr(block_table), _ptr(out), _ptr(lse),
                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kvdec_decode_attn_noalloc(desc, q, k, v, seqlens, cu_seqlens, block_table, out, lse,
+                              stream=None):
+    """kvdec_decode_attn with the library's own scratch in place of a workspace."""
+    _check(lib.kvdec_decode_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(seqlens), _ptr(cu_seqlens), _ptr(block_table),
+                                         _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

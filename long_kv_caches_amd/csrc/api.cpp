@@ -6,8 +6,9 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
-
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -295,6 +296,38 @@ static kvdec_status recompute_args(int32_t b, int32_t l, int32_t h, int32_t num_
   return ok();
 }
 
+// Library-owned scratch of kvdec_decode_attn_noalloc: the attention kernels'
+// per-call partials, for callers that cannot allocate.  The array's name is a
+// host-side stand-in in host code; kernels get the device address that
+// hipGetSymbolAddress returns, fetched once per device with that device
+// current.  Nothing in it needs to start at zero (the kernels write every
+// partial before they read it).
+static __device__ __align__(256) unsigned char scratch[KVDEC_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static kvdec_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KVDEC_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ok();
+}
+
 }  // namespace kvdec
 
 using namespace kvdec;
@@ -348,6 +381,27 @@ const char* kvdec_status_string(kvdec_status s) {
     case KVDEC_ERR_HIP: return "KVDEC_ERR_HIP";
   }
   return "unknown kvdec_status";
+}
+
+kvdec_status kvdec_decode_attn_noalloc(const kvdec_attn_desc* d, const void* q, const void* k,
+                                       const void* v, const int32_t* seqlens,
+                                       const int32_t* cu_seqlens, const int32_t* block_table,
+                                       void* out, float* lse, hipStream_t stream) {
+  kvdec_status st = check_common(d, true);
+  if (st != KVDEC_OK) return st;
+  if (d->batch == 0) return ok();
+  const size_t need = attn_ws(d, plan_decode(d));
+  if (need > KVDEC_NOALLOC_SCRATCH_BYTES)
+    return fail(KVDEC_ERR_WORKSPACE,
+                "this call needs %zu bytes of partials, the library's scratch holds %zu",
+                need, (size_t)KVDEC_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != KVDEC_OK) return st;
+  }
+  return kvdec_decode_attn(d, q, k, v, seqlens, cu_seqlens, block_table, out, lse, ws,
+                           need > 0 ? (size_t)KVDEC_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* d, size_t* bytes) {

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 8
+    assert _lib.lib.kvdec_abi_version() == 9
 
 
 def test_status_strings():
@@ -301,3 +301,26 @@ def test_stream_read_validation(src, nbytes, sink, needle):
     st = _lib.lib.kvdec_stream_read(src, nbytes, sink, None)
     assert st == K._lib.KVDEC_ERR_INVALID
     assert needle in K.last_error()
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # Fixed 64-token chunks of a 2^20-token bound: 8 pairs x 16384 chunks x
+    # 8 heads of partials, far above the library's scratch.  The call must say
+    # so before any HIP call (the fake pointers are never touched).
+    d = _desc(batch=1, num_q_heads=64, num_kv_heads=8, max_seqlen=1 << 20, kv_rows=16,
+              split_tokens=64)
+    need = K.kvdec_decode_attn_workspace(d)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    st = _lib.lib.kvdec_decode_attn_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None,
+                                            FAKE, None, None)
+    assert st == _lib.KVDEC_ERR_WORKSPACE
+    assert "scratch" in K.last_error() and str(need) in K.last_error()
+    # descriptor errors come first, as in kvdec_decode_attn
+    bad = _desc(head_dim=64)
+    st = _lib.lib.kvdec_decode_attn_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, None,
+                                            FAKE, None, None)
+    assert st == _lib.KVDEC_ERR_UNSUPPORTED
+    # an empty batch is a no-op
+    empty = _desc(batch=0)
+    assert _lib.lib.kvdec_decode_attn_noalloc(ctypes.byref(empty), None, None, None, None, None,
+                                              None, None, None, None) == _lib.KVDEC_OK
