@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 9
+#define KVDEC_ABI_VERSION 10
 
 typedef enum {
   KVDEC_OK = 0,
@@ -297,6 +297,97 @@ kvdec_status kvdec_headcache_lookup_ahead(int32_t B, int32_t Hq, int32_t Hkv, in
                                           const float* weights, const float* tau, uint8_t* hit,
                                           float* agg, float* cos, int32_t* miss_list,
                                           int32_t* miss_count, hipStream_t stream);
+
+/*
+ * Miss-driven prefetch into the cache buffer (CLO page, section 3, decoding
+ * flow, Figure 9: the heads the lookup misses are fetched while the previous
+ * layer computes; Figure 7: an update writes the new KV rows straight to
+ * their final place in the cache buffer, with no staging copy).  The GPU
+ * reads the selected rows from the offloaded KV pool in pinned host memory
+ * itself, over PCIe: there is no host-side gather.
+ *
+ * For each of the first *miss_count entries p = b * Hkv + g of miss_list (as
+ * kvdec_headcache_lookup writes them), skipping entries outside [0, B*Hkv)
+ * and KV heads with head_map[g] >= 0 (persistent heads, always resident):
+ *   n = clamp(idx_len[p], 0, min(max_k, buf_cap))
+ *   buf[b, g, i, :] = pool[b, clamp(idx[p * max_k + i], 0, S-1), g, :]  for i < n
+ *   buf_len[p] = n
+ * for K and V alike.  Rows i >= n of the buffer, and pairs not in the list,
+ * are left untouched.  The result does not depend on the order of the list.
+ *
+ *   desc           sizes (below)
+ *   miss_list, miss_count  [B * Hkv], [1] int32 (device)
+ *   head_map       [Hkv] int32 or NULL (every head is a buffer head)
+ *   idx, idx_len   [B * Hkv, max_k], [B * Hkv] int32: the selected token rows
+ *                  of each pair (any order; kvdec_topk_select writes them)
+ *   pool_k, pool_v (host) the full KV in pinned host memory (hipHostMalloc or
+ *                  a pinned torch tensor; pageable memory is refused, since
+ *                  the GPU cannot read it), 16-byte aligned: token t of
+ *                  sequence b, head g starts at element
+ *                  b * pool_stride_b + t * pool_stride_s + g * pool_stride_h
+ *                  ([B, S, Hkv, 128]: S*Hkv*128, Hkv*128, 128)
+ *   buf_k, buf_v   [B, Hkv, buf_cap, 128] (device), 16-byte aligned
+ *   buf_len        [B * Hkv] int32 (device), written for the listed pairs
+ *   ready_flag     NULL, or a 32-bit sequence number in host-mapped memory
+ *                  (kvdec_host_flag_alloc) that the host raises once the pool
+ *                  rows are in place.  The copy then waits on the GPU until
+ *                  (int32)(*ready_flag - ready_value) >= 0, for at most
+ *                  timeout_us microseconds (<= 1000000): the host enqueues the
+ *                  whole step without blocking on the transfer (CLO page,
+ *                  section 2: GPU-centric synchronisation through an
+ *                  identifier variable in shared memory).
+ *   status         with ready_flag: [1] int32 (device or host-mapped), set to
+ *                  0 when the flag was reached, 1 when the wait gave up; after
+ *                  a give-up nothing is copied and buf_len is unchanged.
+ *                  Ignored without ready_flag.
+ * elem_bytes is 2 for fp16 / bf16 K/V and 1 for e4m3 codes.  All the checks
+ * (including that the whole pool range lies in one pinned allocation) run
+ * before anything is enqueued.
+ */
+typedef struct {
+  int32_t batch, num_kv_heads, head_dim;  /* head_dim == 128 */
+  int32_t elem_bytes;                     /* 2 or 1 */
+  int32_t max_seqlen;                     /* S: token rows per (b, g) in the pool, >= 1 */
+  int64_t pool_stride_b, pool_stride_s, pool_stride_h;  /* elements, >= 0, 16-byte multiples */
+  int32_t max_k;                          /* row stride of idx */
+  int32_t buf_cap;                        /* rows per (b, g) in the cache buffer */
+} kvdec_prefetch_desc;
+
+kvdec_status kvdec_headcache_prefetch(const kvdec_prefetch_desc* desc, const int32_t* miss_list,
+                                      const int32_t* miss_count, const int32_t* head_map,
+                                      const int32_t* idx, const int32_t* idx_len,
+                                      const void* pool_k, const void* pool_v, void* buf_k,
+                                      void* buf_v, int32_t* buf_len, const uint32_t* ready_flag,
+                                      uint32_t ready_value, uint32_t timeout_us, int32_t* status,
+                                      hipStream_t stream);
+
+/*
+ * GPU-centric synchronisation (CLO page, section 2, and its argument chain,
+ * row 8: the GPU polls an identifier variable in host-shared memory instead
+ * of the host blocking on the stream, so kernel launches and data transfer
+ * run on separate host threads).
+ *
+ * kvdec_host_flag_alloc: a 32-bit flag (initially 0) in fine-grained pinned
+ * host memory that the GPU reads and writes coherently while kernels run;
+ * free it with kvdec_host_flag_free.  These two allocate and free; they are
+ * set-up calls, never made inside a step.
+ *
+ * kvdec_flag_wait: enqueues a one-wave kernel that waits until
+ * (int32)(*flag - value) >= 0 or timeout_us microseconds (<= 1000000) have
+ * passed, then writes *status = 0 (reached) or 1 (gave up).  Work queued
+ * after it on `stream` starts only then, and sees host writes made before
+ * the flag was raised.  The wait always ends: the GPU never spins unbounded.
+ * flag and status: host-mapped or device memory HIP knows, 4-byte aligned.
+ *
+ * kvdec_flag_signal: enqueues a kernel that sets *flag = value after the work
+ * queued before it on `stream` has finished (a system-scope release), so a
+ * host thread can poll the flag instead of synchronising the stream.
+ */
+kvdec_status kvdec_host_flag_alloc(uint32_t** flag /*(host) out*/);
+kvdec_status kvdec_host_flag_free(uint32_t* flag);
+kvdec_status kvdec_flag_wait(const uint32_t* flag, uint32_t value, uint32_t timeout_us,
+                             int32_t* status, hipStream_t stream);
+kvdec_status kvdec_flag_signal(uint32_t* flag, uint32_t value, hipStream_t stream);
 
 /*
  * CLO threshold chain, Eqs. 7-9 (host only, fp64, rounded to fp32 once):

@@ -452,6 +452,31 @@ def random_indices(seed, B, Hkv, lens, top_k):
     return idx, n
 
 
+def clo_prefetch(seed=0, model="llama3-8b", B=4, S=131072, frac=0.1, n_pers=2, D=D_HEAD,
+                 elem="f16"):
+    """Inputs of the miss-driven prefetch: the ``clo_queries`` draws; then,
+    from ``Draws(seed + 4000037)``, the offloaded full KV in the dense layout
+    [B, S, Hkv, D] ~ N(0,1) (K then V; fp16, or e4m3-like random byte codes
+    with no NaN pattern when elem="u8"); the selections come from
+    ``random_indices(seed + 5000011, ...)``: round(frac * S) sorted token rows
+    per (b, g).  The head map puts the n_pers KV heads of largest importance
+    on persistent slots."""
+    base = clo_queries(seed, model, B, D)
+    Hq, Hkv = base["Hq"], base["Hkv"]
+    dr = Draws(seed + 4_000_037)
+    if elem == "u8":
+        codes = lambda: dr.ctl.integers(0, 0x7E, size=(B, S, Hkv, D), dtype=np.uint8) | (
+            dr.ctl.integers(0, 2, size=(B, S, Hkv, D), dtype=np.uint8) << 7)
+        pool_k, pool_v = codes(), codes()
+    else:
+        pool_k = dr.normal((B, S, Hkv, D))
+        pool_v = dr.normal((B, S, Hkv, D))
+    top_k = int(round(frac * S))
+    idx, idx_len = random_indices(seed + 5_000_011, B, Hkv, np.full(B, S), top_k)
+    return dict(base, S=S, pool_k=pool_k, pool_v=pool_v, idx=idx, idx_len=idx_len, top_k=top_k,
+                head_map=persistent_heads(base["s"], Hkv, n_pers), scale=1.0 / math.sqrt(D))
+
+
 # ---------------------------------------------------------------------------
 # KVPR partial-recompute workload
 # ---------------------------------------------------------------------------

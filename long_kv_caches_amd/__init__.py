@@ -16,4 +16,6 @@ from ._lib import (  # noqa: F401
     kvdec_sparse_hybrid_attn_workspace, last_error, status_string,
     GatherDesc, TopkDesc, gather_desc, topk_desc, kvdec_gather_attn, kvdec_gather_attn_workspace,
     kvdec_topk_select, kvdec_topk_select_workspace, kvdec_stream_read,
+    PrefetchDesc, prefetch_desc, HostFlag, kvdec_headcache_prefetch, kvdec_flag_wait,
+    kvdec_flag_signal,
 )

@@ -52,6 +52,14 @@ class TopkDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
 
+class PrefetchDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("pool_stride_b", ctypes.c_int64),
+                ("pool_stride_s", ctypes.c_int64), ("pool_stride_h", ctypes.c_int64),
+                ("max_k", ctypes.c_int32), ("buf_cap", ctypes.c_int32)]
+
+
 class HybridDesc(ctypes.Structure):
     _fields_ = [("base", AttnDesc), ("num_pers_slots", ctypes.c_int32),
                 ("pers_cap", ctypes.c_int32), ("buf_cap", ctypes.c_int32)]
@@ -76,6 +84,12 @@ def _load():
         "kvdec_gather_attn": ([P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], st),
         "kvdec_topk_select_workspace": ([P, ctypes.POINTER(ctypes.c_size_t)], st),
         "kvdec_topk_select": ([P, P, P, P, P, P, P, ctypes.c_size_t, P], st),
+        "kvdec_headcache_prefetch": ([ctypes.POINTER(PrefetchDesc)] + [P] * 11
+                                     + [ctypes.c_uint32, ctypes.c_uint32, P, P], st),
+        "kvdec_host_flag_alloc": ([ctypes.POINTER(P)], st),
+        "kvdec_host_flag_free": ([P], st),
+        "kvdec_flag_wait": ([P, ctypes.c_uint32, ctypes.c_uint32, P, P], st),
+        "kvdec_flag_signal": ([P, ctypes.c_uint32, P], st),
         "kvdec_headcache_thresholds": ([i32, P, ctypes.c_double, ctypes.c_double, P], st),
         "kvdec_kv_recompute": ([i32, i32, i32, i32, i32, P, i64, P, P, i32, P, P, i64, P], st),
         "kvdec_kvpr_split": ([i64, i64, i64, i64, i32, ctypes.c_double, ctypes.c_double,
@@ -103,7 +117,8 @@ EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_decode_at
             "kvdec_sparse_hybrid_attn", "kvdec_headcache_lookup", "kvdec_headcache_lookup_ahead",
             "kvdec_gather_attn_workspace", "kvdec_gather_attn", "kvdec_topk_select_workspace",
             "kvdec_topk_select",
-            "kvdec_headcache_thresholds",
+            "kvdec_headcache_thresholds", "kvdec_headcache_prefetch", "kvdec_host_flag_alloc",
+            "kvdec_host_flag_free", "kvdec_flag_wait", "kvdec_flag_signal",
             "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
             "kvdec_kernel_timing_read", "kvdec_stream_read", "kvdec_status_string",
             "kvdec_last_error", "kvdec_abi_version")
@@ -237,6 +252,81 @@ def kvdec_kvpr_load_layer(x_host, x_dev, k_host, v_host, w_k, w_v, k_cache, v_ca
                                      k_host.shape[1] * H * hd, _ptr(w_k), _ptr(w_v), int(w_layout),
                                      _ptr(k_cache), _ptr(v_cache), k_cache.shape[1] * H * hd,
                                      _stream(compute_stream), _stream(copy_stream)))
+
+
+def prefetch_desc(*, batch, num_kv_heads, elem_bytes, max_seqlen, pool_strides, max_k, buf_cap,
+                  head_dim=128):
+    """pool_strides: (b, s, h) element strides of the host pool."""
+    sb, ss, sh = (int(x) for x in pool_strides)
+    return PrefetchDesc(batch, num_kv_heads, head_dim, elem_bytes, max_seqlen, sb, ss, sh, max_k,
+                        buf_cap)
+
+
+class HostFlag:
+    """A 32-bit flag in fine-grained pinned host memory (kvdec_host_flag_alloc).
+    `value` reads and writes it from the host; `ptr` is its address."""
+
+    def __init__(self):
+        p = ctypes.c_void_p()
+        _check(lib.kvdec_host_flag_alloc(ctypes.byref(p)))
+        self.ptr = p.value
+        self._word = ctypes.c_uint32.from_address(self.ptr)
+
+    @property
+    def value(self) -> int:
+        return self._word.value
+
+    @value.setter
+    def value(self, v: int) -> None:
+        self._word.value = int(v) & 0xFFFFFFFF
+
+    def close(self) -> None:
+        if self.ptr:
+            _check(lib.kvdec_host_flag_free(ctypes.c_void_p(self.ptr)))
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _flag_ptr(f):
+    if isinstance(f, HostFlag):
+        return ctypes.c_void_p(f.ptr)
+    return _ptr(f)
+
+
+def _any_ptr(t):
+    """Address of a contiguous tensor on the host or the device."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvdec_headcache_prefetch(desc, miss_list, miss_count, head_map, idx, idx_len, pool_k, pool_v,
+                             buf_k, buf_v, buf_len, ready_flag=None, ready_value=0, timeout_us=0,
+                             status=None, stream=None):
+    """pool_k, pool_v: pinned host tensors; the rest on the device (status may also be a
+    HostFlag-like host-mapped word); ready_flag: HostFlag or None."""
+    _check(lib.kvdec_headcache_prefetch(
+        ctypes.byref(desc), _ptr(miss_list), _ptr(miss_count), _ptr(head_map), _ptr(idx),
+        _ptr(idx_len), _any_ptr(pool_k), _any_ptr(pool_v), _ptr(buf_k), _ptr(buf_v), _ptr(buf_len),
+        None if ready_flag is None else _flag_ptr(ready_flag), int(ready_value) & 0xFFFFFFFF,
+        int(timeout_us), None if status is None else _flag_ptr(status), _stream(stream)))
+
+
+def kvdec_flag_wait(flag, value, timeout_us, status, stream=None):
+    """flag: HostFlag or device int32 tensor; status: device int32 tensor or HostFlag."""
+    _check(lib.kvdec_flag_wait(_flag_ptr(flag), int(value) & 0xFFFFFFFF, int(timeout_us),
+                               _flag_ptr(status), _stream(stream)))
+
+
+def kvdec_flag_signal(flag, value, stream=None):
+    _check(lib.kvdec_flag_signal(_flag_ptr(flag), int(value) & 0xFFFFFFFF, _stream(stream)))
 
 
 def kvdec_kernel_timing(enable: bool) -> None:

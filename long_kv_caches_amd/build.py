@@ -17,7 +17,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvdec.so")
 
 SOURCES = ["api.cpp", "decode_attn.hip", "headcache.hip", "kv_recompute.hip", "topk.hip",
-           "stream_read.hip"]
+           "stream_read.hip", "prefetch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -328,6 +328,95 @@ static kvdec_status scratch_address(void** out) {
   return ok();
 }
 
+
+// Memory the GPU reads or writes outside the caller's device buffers must be
+// memory HIP knows: pinned host memory (hipHostMalloc, or torch's pinned
+// tensors) or device memory.  A GPU access to pageable host memory faults,
+// so it is refused here.  Checks that [p, p + bytes) lies in one such
+// allocation and returns the address kernels use for p.
+static kvdec_status mapped_range(const void* p, size_t bytes, bool host_only, const char* what,
+                                 void** dev) {
+  hipPointerAttribute_t at = {};
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the runtime's last error: this failure is reported here
+    return fail(KVDEC_ERR_INVALID,
+                "%s is not memory HIP knows (host memory must be pinned, e.g. hipHostMalloc)", what);
+  }
+  const bool host = at.type == hipMemoryTypeHost;
+  if (!host && (host_only || at.type != hipMemoryTypeDevice))
+    return fail(KVDEC_ERR_INVALID, "%s must be pinned host memory%s (memory type %d)", what,
+                host_only ? "" : " or device memory", (int)at.type);
+  if (!at.devicePointer) return fail(KVDEC_ERR_INVALID, "%s has no device mapping", what);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e == hipSuccess) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base), at_p = reinterpret_cast<uintptr_t>(p);
+    if (at_p < lo || at_p - lo + bytes > size)
+      return fail(KVDEC_ERR_INVALID, "%s: %zu bytes from it run past its allocation (%zu bytes)",
+                  what, bytes, size - (at_p - lo));
+  } else {
+    // no range query for this memory: the last byte must be mapped the same way
+    (void)hipGetLastError();
+    hipPointerAttribute_t end = {};
+    if (bytes > 1) {
+      e = hipPointerGetAttributes(&end, static_cast<const char*>(p) + bytes - 1);
+      if (e != hipSuccess || end.type != at.type) {
+        (void)hipGetLastError();
+        return fail(KVDEC_ERR_INVALID, "%s: %zu bytes from it are not all in known memory", what,
+                    bytes);
+      }
+    }
+  }
+  *dev = at.devicePointer;
+  return ok();
+}
+
+// Ticks per microsecond of the constant-rate clock kernels read (wall_clock64).
+static uint64_t wall_ticks_per_us() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 100;
+  }
+  int khz = cached[dev].load(std::memory_order_relaxed);
+  if (khz <= 0) {
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0) {
+      (void)hipGetLastError();
+      khz = 100000;
+    }
+    cached[dev].store(khz, std::memory_order_relaxed);
+  }
+  return (uint64_t)std::max(khz / 1000, 1);
+}
+
+static constexpr uint32_t kMaxTimeoutUs = 1000000;
+
+// Checks a flag wait's arguments and returns the device addresses of flag
+// and status (each any HIP-known memory, 4-byte aligned).
+static kvdec_status flag_wait_args(const uint32_t* flag, uint32_t timeout_us, int32_t* status,
+                                   void** fdev, void** sdev) {
+  if (!flag || !status) return fail(KVDEC_ERR_INVALID, "flag and status must be non-NULL");
+  if (timeout_us > kMaxTimeoutUs)
+    return fail(KVDEC_ERR_INVALID, "timeout_us must be <= %u", kMaxTimeoutUs);
+  if (reinterpret_cast<uintptr_t>(flag) % 4 || reinterpret_cast<uintptr_t>(status) % 4)
+    return fail(KVDEC_ERR_INVALID, "flag and status must be 4-byte aligned");
+  kvdec_status st = mapped_range(flag, 4, false, "flag", fdev);
+  if (st != KVDEC_OK) return st;
+  return mapped_range(status, 4, false, "status", sdev);
+}
+
+static kvdec_status enqueue_flag_wait(void* fdev, uint32_t value, uint32_t timeout_us, void* sdev,
+                                      hipStream_t stream) {
+  const uint64_t ticks = (uint64_t)timeout_us * wall_ticks_per_us();
+  return hip_status(launch_flag_wait(static_cast<const uint32_t*>(fdev), value, ticks,
+                                     timeout_us + 1, static_cast<int32_t*>(sdev), stream),
+                    "flag wait launch");
+}
+
 }  // namespace kvdec
 
 using namespace kvdec;
@@ -637,6 +726,118 @@ kvdec_status kvdec_headcache_lookup(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
                                 miss_list, miss_count, &a);
   if (st != KVDEC_OK || B == 0) return st;
   return hip_status(launch_headcache_lookup(a, stream), "head-cache lookup launch");
+}
+
+kvdec_status kvdec_host_flag_alloc(uint32_t** flag) {
+  if (!flag) return fail(KVDEC_ERR_INVALID, "flag is NULL");
+  *flag = nullptr;
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, 64, hipHostMallocCoherent | hipHostMallocMapped);
+  if (e != hipSuccess) return hip_status(e, "hipHostMalloc (flag)");
+  static_cast<volatile uint32_t*>(p)[0] = 0;
+  *flag = static_cast<uint32_t*>(p);
+  return ok();
+}
+
+kvdec_status kvdec_host_flag_free(uint32_t* flag) {
+  if (!flag) return ok();
+  return hip_status(hipHostFree(flag), "hipHostFree (flag)");
+}
+
+kvdec_status kvdec_flag_wait(const uint32_t* flag, uint32_t value, uint32_t timeout_us,
+                             int32_t* status, hipStream_t stream) {
+  void *fdev = nullptr, *sdev = nullptr;
+  kvdec_status st = flag_wait_args(flag, timeout_us, status, &fdev, &sdev);
+  if (st != KVDEC_OK) return st;
+  return enqueue_flag_wait(fdev, value, timeout_us, sdev, stream);
+}
+
+kvdec_status kvdec_flag_signal(uint32_t* flag, uint32_t value, hipStream_t stream) {
+  if (!flag) return fail(KVDEC_ERR_INVALID, "flag must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(flag) % 4) return fail(KVDEC_ERR_INVALID, "flag must be 4-byte aligned");
+  void* fdev = nullptr;
+  kvdec_status st = mapped_range(flag, 4, false, "flag", &fdev);
+  if (st != KVDEC_OK) return st;
+  return hip_status(launch_flag_signal(static_cast<uint32_t*>(fdev), value, stream),
+                    "flag signal launch");
+}
+
+kvdec_status kvdec_headcache_prefetch(const kvdec_prefetch_desc* d, const int32_t* miss_list,
+                                      const int32_t* miss_count, const int32_t* head_map,
+                                      const int32_t* idx, const int32_t* idx_len,
+                                      const void* pool_k, const void* pool_v, void* buf_k,
+                                      void* buf_v, int32_t* buf_len, const uint32_t* ready_flag,
+                                      uint32_t ready_value, uint32_t timeout_us, int32_t* status,
+                                      hipStream_t stream) {
+  if (!d) return fail(KVDEC_ERR_INVALID, "desc is NULL");
+  if (d->batch < 0 || d->num_kv_heads < 1) return fail(KVDEC_ERR_INVALID, "bad batch / num_kv_heads");
+  if (d->head_dim != kHeadDim) return fail(KVDEC_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->elem_bytes != 1 && d->elem_bytes != 2)
+    return fail(KVDEC_ERR_UNSUPPORTED, "elem_bytes must be 2 (fp16, bf16) or 1 (e4m3)");
+  if (d->max_seqlen < 1 || d->max_k < 0 || d->buf_cap < 0)
+    return fail(KVDEC_ERR_INVALID, "max_seqlen must be >= 1, max_k and buf_cap >= 0");
+  if (d->pool_stride_b < 0 || d->pool_stride_s < 0 || d->pool_stride_h < 0)
+    return fail(KVDEC_ERR_INVALID, "pool strides must be >= 0");
+  const int64_t eb = d->elem_bytes;
+  if ((d->pool_stride_b * eb) % 16 || (d->pool_stride_s * eb) % 16 || (d->pool_stride_h * eb) % 16)
+    return fail(KVDEC_ERR_INVALID, "pool strides must be multiples of 16 bytes");
+  if ((int64_t)d->batch * d->num_kv_heads > INT32_MAX / 2 ||
+      (int64_t)d->batch * d->num_kv_heads * std::max(d->max_k, 1) > INT32_MAX)
+    return fail(KVDEC_ERR_UNSUPPORTED, "batch * num_kv_heads * max_k too large");
+  const int pairs = d->batch * d->num_kv_heads;
+  const bool nothing = pairs == 0;
+  if (nothing && !ready_flag) return ok();
+  void *fdev = nullptr, *sdev = nullptr, *kdev = nullptr, *vdev = nullptr;
+  kvdec_status st;
+  if (ready_flag) {
+    st = flag_wait_args(ready_flag, timeout_us, status, &fdev, &sdev);
+    if (st != KVDEC_OK) return st;
+  }
+  if (!nothing) {
+    if (!miss_list || !miss_count || !idx || !idx_len || !pool_k || !pool_v || !buf_k || !buf_v ||
+        !buf_len)
+      return fail(KVDEC_ERR_INVALID, "miss_list, miss_count, idx, idx_len, the pools, the "
+                                     "buffers and buf_len must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(pool_k) % 16 || reinterpret_cast<uintptr_t>(pool_v) % 16 ||
+        reinterpret_cast<uintptr_t>(buf_k) % 16 || reinterpret_cast<uintptr_t>(buf_v) % 16)
+      return fail(KVDEC_ERR_INVALID, "pools and buffers must be 16-byte aligned");
+    // every row the kernel can address: b < B, t < S, g < Hkv (indices are clamped)
+    const int64_t last = (int64_t)(d->batch - 1) * d->pool_stride_b +
+                         (int64_t)(d->max_seqlen - 1) * d->pool_stride_s +
+                         (int64_t)(d->num_kv_heads - 1) * d->pool_stride_h + kHeadDim;
+    st = mapped_range(pool_k, (size_t)(last * eb), true, "pool_k", &kdev);
+    if (st != KVDEC_OK) return st;
+    st = mapped_range(pool_v, (size_t)(last * eb), true, "pool_v", &vdev);
+    if (st != KVDEC_OK) return st;
+  }
+  if (ready_flag) {
+    st = enqueue_flag_wait(fdev, ready_value, timeout_us, sdev, stream);
+    if (st != KVDEC_OK) return st;
+  }
+  if (nothing) return ok();
+  PrefetchArgs a = {};
+  a.miss_list = miss_list;
+  a.miss_count = miss_count;
+  a.head_map = head_map;
+  a.idx = idx;
+  a.idx_len = idx_len;
+  a.pool_k = kdev;
+  a.pool_v = vdev;
+  a.buf_k = buf_k;
+  a.buf_v = buf_v;
+  a.buf_len = buf_len;
+  a.status = static_cast<int32_t*>(sdev);
+  a.stride_b = d->pool_stride_b;
+  a.stride_s = d->pool_stride_s;
+  a.stride_h = d->pool_stride_h;
+  a.B = d->batch;
+  a.Hkv = d->num_kv_heads;
+  a.S = d->max_seqlen;
+  a.max_k = d->max_k;
+  a.buf_cap = d->buf_cap;
+  a.max_rows = std::min(d->max_k, d->buf_cap);
+  a.elem_bytes = d->elem_bytes;
+  return hip_status(launch_prefetch(a, stream), "prefetch launch");
 }
 
 kvdec_status kvdec_headcache_lookup_ahead(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,

@@ -144,6 +144,29 @@ struct QProjArgs {
 };
 hipError_t launch_qproj(const QProjArgs& a, hipStream_t stream);
 
+// Miss-driven prefetch into the cache buffer (prefetch.hip).
+struct PrefetchArgs {
+  const int32_t* miss_list;   // [B * Hkv] pairs b * Hkv + g, the first *miss_count valid
+  const int32_t* miss_count;  // [1]
+  const int32_t* head_map;    // [Hkv] or NULL: heads with a slot >= 0 are persistent, skipped
+  const int32_t* idx;         // [B * Hkv, max_k] selected token rows of each pair
+  const int32_t* idx_len;     // [B * Hkv]
+  const void* pool_k;         // device address of the pinned host pool (K)
+  const void* pool_v;
+  void* buf_k;                // [B, Hkv, buf_cap, 128] cache buffer
+  void* buf_v;
+  int32_t* buf_len;           // [B * Hkv], set for every missed pair
+  int32_t* status;            // NULL, or the flag wait's result: nonzero = copy nothing
+  int64_t stride_b, stride_s, stride_h;  // pool strides in elements
+  int B, Hkv, S, max_k, buf_cap;
+  int max_rows;               // min(max_k, buf_cap)
+  int elem_bytes;             // 2 (fp16, bf16) or 1 (e4m3 codes)
+};
+hipError_t launch_prefetch(const PrefetchArgs& a, hipStream_t stream);
+hipError_t launch_flag_wait(const uint32_t* flag, uint32_t target, uint64_t ticks,
+                            uint32_t max_polls, int32_t* status, hipStream_t stream);
+hipError_t launch_flag_signal(uint32_t* flag, uint32_t value, hipStream_t stream);
+
 struct RecomputeArgs {
   const uint16_t* x;
   const uint16_t* wk;

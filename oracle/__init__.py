@@ -358,3 +358,45 @@ def kvpr_best_split(b, s_prime, l_max, h, p, v_com, v_gpu):
     l = _load().orc_kvpr_best_split(float(b), int(s_prime), int(l_max), float(h), float(p),
                                     float(v_com), float(v_gpu), ctypes.byref(t))
     return l, t.value
+
+
+def prefetch_missed(pool_k, pool_v, idx, idx_len, miss_list, buf_k, buf_v, buf_len,
+                    head_map=None):
+    """CLO miss-driven prefetch (CLO page, section 3: the heads the lookup of
+    layer l misses are fetched during layer l-1, Figure 9; Figure 7: an update
+    writes the new KV rows straight to their final place in the cache buffer).
+
+    pool_k, pool_v [B, S, Hkv, D] (the offloaded full KV); idx [B, Hkv, max_k]
+    and idx_len [B*Hkv] (each pair's selected token rows); miss_list: pairs
+    b*Hkv + g; buf_k, buf_v [B, Hkv, buf_cap, D] and buf_len [B*Hkv] (the cache
+    buffer before the update); head_map [Hkv] or None (slot >= 0: persistent
+    head, never fetched).  For every listed buffer head:
+        n = min(idx_len, max_k, buf_cap);  buf[b, g, i] = pool[b, idx[b, g, i], g]  (i < n);
+        buf_len[b*Hkv + g] = n.
+    Returns updated copies (buf_k, buf_v, buf_len); everything else is left as
+    it was.  A listed pair outside the batch, or an index outside [0, S),
+    raises ValueError.  Pinned by: a selection of every token reproduces the
+    whole head; attention over the updated buffer equals the pinned gather
+    attention over the same indices; the result ignores the list's order.
+    """
+    pool_k = np.asarray(pool_k); pool_v = np.asarray(pool_v)
+    B, S, Hkv, D = pool_k.shape
+    idx = np.asarray(idx, np.int32)
+    idx_len = np.asarray(idx_len, np.int32).reshape(-1)
+    max_k, buf_cap = idx.shape[2], np.asarray(buf_k).shape[2]
+    bk = np.array(buf_k, copy=True); bv = np.array(buf_v, copy=True)
+    bl = np.array(buf_len, np.int32, copy=True).reshape(-1)
+    for p in np.asarray(miss_list, np.int64).reshape(-1):
+        if p < 0 or p >= B * Hkv:
+            raise ValueError(f"prefetch_missed: pair {p} outside the batch")
+        b, g = divmod(int(p), Hkv)
+        if head_map is not None and head_map[g] >= 0:
+            continue
+        n = max(0, min(int(idx_len[p]), max_k, buf_cap))
+        rows = idx[b, g, :n]
+        if np.any((rows < 0) | (rows >= S)):
+            raise ValueError(f"prefetch_missed: index outside [0, {S}) for pair {p}")
+        bk[b, g, :n] = pool_k[b, rows, g]
+        bv[b, g, :n] = pool_v[b, rows, g]
+        bl[p] = n
+    return bk, bv, bl

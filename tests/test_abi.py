@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 9
+    assert _lib.lib.kvdec_abi_version() == 10
 
 
 def test_status_strings():
