@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_ABI_VERSION 10
+#define KVDEC_ABI_VERSION 11
 
 typedef enum {
   KVDEC_OK = 0,
@@ -502,6 +502,29 @@ kvdec_status kvdec_kernel_timing_read(double* total_ms, int64_t* launches);
  * pointers non-NULL.  Asynchronous on `stream`; it is a main kernel for
  * kvdec_kernel_timing.  KVDEC_ERR_INVALID on bad arguments (nothing launched). */
 kvdec_status kvdec_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Debug validation of metadata that lives on the device.  The kernels never
+ * fault on malformed metadata: they clamp it (see the kv_rows, head_map, idx
+ * and miss_list notes above), which reads wrong rows or drops work without a
+ * status.  With KVDEC_CHECK=1 in the environment (read at every call), each
+ * call first copies its metadata to the host, after the work already queued
+ * on its stream, synchronising that stream, and returns KVDEC_ERR_INVALID,
+ * with nothing launched and a message naming the entry, for:
+ *   kvdec_decode_attn (and _noalloc): cu_seqlens[0] != 0, cu_seqlens
+ *     decreasing, a length above max_seqlen, cu_seqlens[B] > kv_rows,
+ *     seqlens outside [0, max_seqlen], a used block-table entry outside
+ *     [0, kv_rows);
+ *   kvdec_sparse_hybrid_attn: a head_map entry that is neither -1 nor a slot
+ *     in [0, num_pers_slots), pers_len outside [0, pers_cap], a buffer head's
+ *     buf_len outside [0, buf_cap];
+ *   kvdec_gather_attn: idx_len outside [0, max_k], a listed row outside [0, S);
+ *   kvdec_topk_select: seqlens outside [0, max_seqlen];
+ *   kvdec_headcache_prefetch: miss_count outside [0, B*Hkv], a listed pair
+ *     outside [0, B*Hkv), and for listed buffer heads idx_len outside
+ *     [0, min(max_k, buf_cap)] or a listed row outside [0, S).
+ * Returns 1 when the mode is on for the next call, else 0.  For debugging
+ * only: the copies and the synchronisation cost far more than the kernels. */
+int kvdec_check_enabled(void);
 
 const char* kvdec_status_string(kvdec_status status);
 const char* kvdec_last_error(void);

@@ -17,5 +17,5 @@ from ._lib import (  # noqa: F401
     GatherDesc, TopkDesc, gather_desc, topk_desc, kvdec_gather_attn, kvdec_gather_attn_workspace,
     kvdec_topk_select, kvdec_topk_select_workspace, kvdec_stream_read,
     PrefetchDesc, prefetch_desc, HostFlag, kvdec_headcache_prefetch, kvdec_flag_wait,
-    kvdec_flag_signal,
+    kvdec_flag_signal, check_enabled,
 )

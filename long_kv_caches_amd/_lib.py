@@ -102,6 +102,7 @@ def _load():
         "kvdec_status_string": ([st], ctypes.c_char_p),
         "kvdec_last_error": ([], ctypes.c_char_p),
         "kvdec_abi_version": ([], ctypes.c_int),
+        "kvdec_check_enabled": ([], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -121,7 +122,12 @@ EXPORTED = ("kvdec_decode_attn_workspace", "kvdec_decode_attn", "kvdec_decode_at
             "kvdec_host_flag_free", "kvdec_flag_wait", "kvdec_flag_signal",
             "kvdec_kv_recompute", "kvdec_kvpr_split", "kvdec_kvpr_load_layer", "kvdec_kernel_timing",
             "kvdec_kernel_timing_read", "kvdec_stream_read", "kvdec_status_string",
-            "kvdec_last_error", "kvdec_abi_version")
+            "kvdec_last_error", "kvdec_abi_version", "kvdec_check_enabled")
+
+
+def check_enabled() -> bool:
+    """Whether KVDEC_CHECK=1 (debug validation of device metadata) is on."""
+    return bool(lib.kvdec_check_enabled())
 
 
 def status_string(status: int) -> str:

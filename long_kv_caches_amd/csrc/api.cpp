@@ -417,6 +417,142 @@ static kvdec_status enqueue_flag_wait(void* fdev, uint32_t value, uint32_t timeo
                     "flag wait launch");
 }
 
+
+// ---------------------------------------------------------------------------
+// Debug validation of device-resident metadata, on when the environment holds
+// KVDEC_CHECK=1.  The kernels clamp malformed metadata so that it cannot make
+// them fault; this mode copies the metadata to the host instead (after the
+// work already queued on the stream, which may be what writes it), and
+// rejects what the kernels would clamp, before anything is launched.
+// ---------------------------------------------------------------------------
+static bool check_mode() {
+  const char* e = getenv("KVDEC_CHECK");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+template <typename T>
+static kvdec_status fetch(std::vector<T>* h, const T* d, size_t n, hipStream_t stream,
+                          const char* what) {
+  h->assign(n, T());
+  if (n == 0) return ok();
+  if (!d) return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: %s is NULL", what);
+  hipError_t e = hipMemcpyAsync(h->data(), d, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, what);
+  return ok();
+}
+
+static kvdec_status check_decode_meta(const kvdec_attn_desc* d, const int32_t* seqlens,
+                                      const int32_t* cu, const int32_t* bt, hipStream_t stream) {
+  const int B = d->batch;
+  std::vector<int32_t> h;
+  kvdec_status st;
+  if (d->layout == KVDEC_RAGGED) {
+    if ((st = fetch(&h, cu, (size_t)B + 1, stream, "cu_seqlens")) != KVDEC_OK) return st;
+    if (h[0] != 0) return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: cu_seqlens[0] = %d, not 0", h[0]);
+    for (int b = 0; b < B; ++b) {
+      if (h[b + 1] < h[b])
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: cu_seqlens decreases at %d (%d after %d)",
+                    b + 1, h[b + 1], h[b]);
+      if (h[b + 1] - h[b] > d->max_seqlen)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: sequence %d has %d tokens > max_seqlen %d",
+                    b, h[b + 1] - h[b], d->max_seqlen);
+    }
+    if (h[B] > d->kv_rows)
+      return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: cu_seqlens[%d] = %d > kv_rows %lld", B, h[B],
+                  (long long)d->kv_rows);
+    return ok();
+  }
+  if (!seqlens) return ok();  // dense: every length is max_seqlen
+  if ((st = fetch(&h, seqlens, (size_t)B, stream, "seqlens")) != KVDEC_OK) return st;
+  for (int b = 0; b < B; ++b)
+    if (h[b] < 0 || h[b] > d->max_seqlen)
+      return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: seqlens[%d] = %d outside [0, max_seqlen %d]",
+                  b, h[b], d->max_seqlen);
+  if (d->layout != KVDEC_PAGED) return ok();
+  std::vector<int32_t> t;
+  const int mp = d->max_pages_per_seq;
+  if ((st = fetch(&t, bt, (size_t)B * mp, stream, "block_table")) != KVDEC_OK) return st;
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < (h[b] + d->page_size - 1) / d->page_size; ++p) {
+      const int id = t[(size_t)b * mp + p];
+      if (id < 0 || id >= d->kv_rows)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: block_table[%d][%d] = %d outside [0, %lld)",
+                    b, p, id, (long long)d->kv_rows);
+    }
+  return ok();
+}
+
+static kvdec_status check_hybrid_meta(const kvdec_hybrid_desc* hd, const int32_t* pers_len,
+                                      const int32_t* buf_len, const int32_t* head_map,
+                                      hipStream_t stream) {
+  const int B = hd->base.batch, Hkv = hd->base.num_kv_heads;
+  std::vector<int32_t> hm, pl, bl;
+  kvdec_status st;
+  if ((st = fetch(&hm, head_map, (size_t)Hkv, stream, "head_map")) != KVDEC_OK) return st;
+  bool pers = false;
+  for (int g = 0; g < Hkv; ++g) {
+    if (hm[g] < -1 || hm[g] >= hd->num_pers_slots)
+      return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: head_map[%d] = %d is neither -1 nor a slot "
+                  "in [0, %d)", g, hm[g], hd->num_pers_slots);
+    pers |= hm[g] >= 0;
+  }
+  if (pers) {
+    if ((st = fetch(&pl, pers_len, (size_t)B, stream, "pers_len")) != KVDEC_OK) return st;
+    for (int b = 0; b < B; ++b)
+      if (pl[b] < 0 || pl[b] > hd->pers_cap)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: pers_len[%d] = %d outside [0, pers_cap %d]",
+                    b, pl[b], hd->pers_cap);
+  }
+  if ((st = fetch(&bl, buf_len, (size_t)B * Hkv, stream, "buf_len")) != KVDEC_OK) return st;
+  for (int b = 0; b < B; ++b)
+    for (int g = 0; g < Hkv; ++g) {
+      const int n = bl[(size_t)b * Hkv + g];
+      if (hm[g] < 0 && (n < 0 || n > hd->buf_cap))
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: buf_len[%d] = %d outside [0, buf_cap %d]",
+                    b * Hkv + g, n, hd->buf_cap);
+    }
+  return ok();
+}
+
+// Index lists of (sequence, KV head) pairs (row stride max_k): lengths in
+// [0, len_cap], the listed rows in [0, S).  Only the pairs in `pairs` (all,
+// when empty) are checked.
+static kvdec_status check_index_lists(const int32_t* idx, const int32_t* idx_len, int n_pairs,
+                                      int max_k, int len_cap, int S,
+                                      const std::vector<int>& pairs, hipStream_t stream) {
+  std::vector<int32_t> len, ix;
+  kvdec_status st;
+  if ((st = fetch(&len, idx_len, (size_t)n_pairs, stream, "idx_len")) != KVDEC_OK) return st;
+  bool any = false;
+  auto each = [&](auto&& fn) -> kvdec_status {
+    if (pairs.empty()) {
+      for (int p = 0; p < n_pairs; ++p)
+        if ((st = fn(p)) != KVDEC_OK) return st;
+    } else {
+      for (int p : pairs)
+        if ((st = fn(p)) != KVDEC_OK) return st;
+    }
+    return ok();
+  };
+  st = each([&](int p) -> kvdec_status {
+    if (len[p] < 0 || len[p] > len_cap)
+      return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: idx_len[%d] = %d outside [0, %d]", p, len[p],
+                  len_cap);
+    any |= len[p] > 0;
+    return ok();
+  });
+  if (st != KVDEC_OK || !any) return st;
+  if ((st = fetch(&ix, idx, (size_t)n_pairs * max_k, stream, "idx")) != KVDEC_OK) return st;
+  return each([&](int p) -> kvdec_status {
+    for (int i = 0; i < len[p]; ++i) {
+      const int t = ix[(size_t)p * max_k + i];
+      if (t < 0 || t >= S)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: idx[%d][%d] = %d outside [0, %d)", p, i, t, S);
+    }
+    return ok();
+  });
+}
 }  // namespace kvdec
 
 using namespace kvdec;
@@ -424,6 +560,8 @@ using namespace kvdec;
 extern "C" {
 
 int kvdec_abi_version(void) { return KVDEC_ABI_VERSION; }
+
+int kvdec_check_enabled(void) { return check_mode() ? 1 : 0; }
 
 kvdec_status kvdec_kernel_timing(int enable) {
   TimingState& t = g_timing;
@@ -541,6 +679,8 @@ kvdec_status kvdec_decode_attn(const kvdec_attn_desc* d, const void* q, const vo
     a.page = d->page_size;
     a.max_pages = d->max_pages_per_seq;
   }
+  if (check_mode() && (st = check_decode_meta(d, seqlens, cu_seqlens, block_table, stream)) != KVDEC_OK)
+    return st;
   return run_attn(d, p, a, ws, ws_bytes, stream);
 }
 
@@ -593,6 +733,8 @@ kvdec_status kvdec_sparse_hybrid_attn(const kvdec_hybrid_desc* h, const void* q,
   a.buf_cap = h->buf_cap;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  if (check_mode() && (st = check_hybrid_meta(h, pers_len, buf_len, head_map, stream)) != KVDEC_OK)
+    return st;
   return run_attn(d, p, a, ws, ws_bytes, stream);
 }
 
@@ -651,6 +793,10 @@ kvdec_status kvdec_gather_attn(const kvdec_gather_desc* gd, const void* q, const
   // with no cache rows or no index slots every pair is empty: the kernels
   // then read neither k, v nor idx
   if (d->max_seqlen == 0 || gd->max_k == 0) a.max_k = 0;
+  if (check_mode() &&
+      (st = check_index_lists(idx, idx_len, d->batch * d->num_kv_heads, gd->max_k, gd->max_k,
+                              std::max(d->max_seqlen, 1), {}, stream)) != KVDEC_OK)
+    return st;
   return run_attn(d, p, a, ws, ws_bytes, stream);
 }
 
@@ -714,6 +860,14 @@ kvdec_status kvdec_topk_select(const kvdec_topk_desc* d, const void* q, const vo
              : nullptr;
   a.top_k = d->top_k;
   a.dtype = d->dtype;
+  if (check_mode() && a.seqlens) {
+    std::vector<int32_t> h;
+    if ((st = fetch(&h, seqlens, (size_t)d->batch, stream, "seqlens")) != KVDEC_OK) return st;
+    for (int b = 0; b < d->batch; ++b)
+      if (h[b] < 0 || h[b] > d->max_seqlen)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: seqlens[%d] = %d outside [0, max_seqlen %d]",
+                    b, h[b], d->max_seqlen);
+  }
   return hip_status(launch_topk(a, stream), "top-k selection launch");
 }
 
@@ -809,6 +963,27 @@ kvdec_status kvdec_headcache_prefetch(const kvdec_prefetch_desc* d, const int32_
     if (st != KVDEC_OK) return st;
     st = mapped_range(pool_v, (size_t)(last * eb), true, "pool_v", &vdev);
     if (st != KVDEC_OK) return st;
+  }
+  if (!nothing && check_mode()) {
+    // before the flag wait is queued: a rejected call launches nothing
+    std::vector<int32_t> mc, ml, hm;
+    if ((st = fetch(&mc, miss_count, 1, stream, "miss_count")) != KVDEC_OK) return st;
+    if (mc[0] < 0 || mc[0] > pairs)
+      return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: miss_count = %d outside [0, %d]", mc[0], pairs);
+    if ((st = fetch(&ml, miss_list, (size_t)mc[0], stream, "miss_list")) != KVDEC_OK) return st;
+    if (head_map && (st = fetch(&hm, head_map, (size_t)d->num_kv_heads, stream, "head_map")) != KVDEC_OK)
+      return st;
+    std::vector<int> listed;
+    for (int i = 0; i < mc[0]; ++i) {
+      if (ml[i] < 0 || ml[i] >= pairs)
+        return fail(KVDEC_ERR_INVALID, "KVDEC_CHECK: miss_list[%d] = %d outside [0, %d)", i,
+                    ml[i], pairs);
+      if (!head_map || hm[ml[i] % d->num_kv_heads] < 0) listed.push_back(ml[i]);
+    }
+    if (!listed.empty() &&
+        (st = check_index_lists(idx, idx_len, pairs, d->max_k, std::min(d->max_k, d->buf_cap),
+                                d->max_seqlen, listed, stream)) != KVDEC_OK)
+      return st;
   }
   if (ready_flag) {
     st = enqueue_flag_wait(fdev, ready_value, timeout_us, sdev, stream);

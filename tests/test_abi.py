@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.EXPORTED)
-    assert _lib.lib.kvdec_abi_version() == 10
+    assert _lib.lib.kvdec_abi_version() == 11
 
 
 def test_status_strings():
@@ -324,3 +324,12 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     empty = _desc(batch=0)
     assert _lib.lib.kvdec_decode_attn_noalloc(ctypes.byref(empty), None, None, None, None, None,
                                               None, None, None, None) == _lib.KVDEC_OK
+
+
+def test_check_mode_follows_the_environment(monkeypatch):
+    monkeypatch.delenv("KVDEC_CHECK", raising=False)
+    assert not K.check_enabled()
+    monkeypatch.setenv("KVDEC_CHECK", "1")
+    assert K.check_enabled()
+    monkeypatch.setenv("KVDEC_CHECK", "0")
+    assert not K.check_enabled()
