@@ -38,31 +38,270 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_32k_traffic.json")
-TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_32k_e4m3_traffic.json")
-KERNEL_SOURCES = ["long_kv_caches_amd/csrc/decode_attn.hip", "long_kv_caches_amd/csrc/device_common.h",
-                  "long_kv_caches_amd/csrc/internal.h", "long_kv_caches_amd/csrc/api.cpp"]
+_CSRC = "long_kv_caches_amd/csrc/"
+DECODE_SOURCES = [_CSRC + f for f in ("decode_attn.hip", "device_common.h", "internal.h", "api.cpp")]
+RECOMPUTE_SOURCES = [_CSRC + f for f in ("kv_recompute.hip", "device_common.h", "internal.h", "api.cpp")]
+
+# Counter summaries in profiles/, per workload: the file, the main kernel it
+# covers (a substring of the kernel's name in rocprofv3's output) and the
+# sources that kernel is built from.  `bench.py --summarize-pmc DIR` writes
+# them from rocprofv3 counter runs of this script (the commands are in each
+# file); a summary counts only while those sources hash to what it records.
+COUNTERS = {
+    "llama3-8b-32k": ("decode_attn_llama3_8b_32k_traffic.json", "decode_balanced_kernel<", DECODE_SOURCES),
+    "llama3-8b-32k-fp8": ("decode_attn_llama3_8b_32k_e4m3_traffic.json", "decode_balanced_kernel<",
+                          DECODE_SOURCES),
+    "llama2-7b-paged": ("decode_attn_llama2_7b_paged_b1024_traffic.json", "decode_balanced_kernel<",
+                        DECODE_SOURCES),
+    "clo-llama3-8b-128k": ("clo_hybrid_attn_llama3_8b_128k_traffic.json", "decode_balanced_kernel<",
+                           DECODE_SOURCES),
+    "clo-qwen2.5-14b-128k": ("clo_hybrid_attn_qwen2_5_14b_128k_traffic.json", "decode_balanced_kernel<",
+                             DECODE_SOURCES),
+    "clo-gather-llama3-8b-128k": ("gather_attn_llama3_8b_128k_traffic.json", "decode_balanced_kernel<",
+                                  DECODE_SOURCES),
+    "kvpr-opt13b": ("kv_recompute_opt13b_counters.json", "kv_recompute_kernel_wide<1>", RECOMPUTE_SOURCES),
+    "kvpr-opt13b-attention": ("decode_attn_opt13b_merged_cache_traffic.json", "decode_balanced_kernel<",
+                              DECODE_SOURCES),
+}
+# Kernel-trace summaries in profiles/, per workload (`--summarize-trace DIR`).
+TRACES = {
+    "llama3-8b-32k": ("decode_attn_llama3_8b_32k_kernel_trace.txt",
+                      "Llama3-8B 32K ragged decode attention (16 sequences, 32 query / 8 KV heads, fp16)"),
+    "llama3-8b-32k-fp8": ("decode_attn_llama3_8b_32k_e4m3_kernel_trace.txt",
+                          "Llama3-8B 32K ragged decode attention over e4m3 K/V"),
+    "llama2-7b-paged": ("decode_attn_llama2_7b_paged_b1024_kernel_trace.txt",
+                        "Llama-2-7B paged decode attention, batch 1024, 16-token pages"),
+    "clo-llama3-8b-128k": ("clo_hybrid_attn_and_lookup_llama3_8b_128k_kernel_trace.txt",
+                           "CLO hybrid attention, head-cache lookup (and one layer ahead) and the "
+                           "miss-driven prefetch, Llama3-8B 128K batch 4"),
+    "clo-qwen2.5-14b-128k": ("clo_hybrid_attn_and_lookup_qwen2_5_14b_128k_kernel_trace.txt",
+                             "CLO hybrid attention, head-cache lookup (and one layer ahead) and the "
+                             "miss-driven prefetch, Qwen2.5-14B 128K batch 4"),
+    "clo-gather-llama3-8b-128k": ("gather_attn_and_topk_llama3_8b_128k_kernel_trace.txt",
+                                  "index-gather attention over the exact top-10% rows and the top-k "
+                                  "selection, Llama3-8B heads, 128K cache, batch 8"),
+    "kvpr-opt13b": ("kv_recompute_and_attn_opt13b_kernel_trace.txt",
+                    "KVPR partial K/V recompute GEMM (b=32, l=256, h=5120 -> 0.859 TFLOP) and attention "
+                    "over the merged 1024-token cache, OPT-13B layer"),
+    "kvpr-overlap": ("kvpr_overlapped_layer_load_opt13b_kernel_trace.txt",
+                     "KVPR layer load: X[0:l] and K/V[l:s') over PCIe overlapped with the recompute, "
+                     "OPT-13B layer"),
+}
 
 
-def kernel_source_hash() -> str:
+def trace_command(workload):
+    return (f"rocprofv3 --kernel-trace --stats -f csv -d <out>/TRACE -o run -- python3 <repo>/bench.py "
+            f"--workload {workload} --no-cpu-baseline > <out>/TRACE/bench.json")
+
+
+def summarize_trace(workload, out_dir):
+    """Writes profiles/<trace file> from the rocprofv3 kernel-trace run in
+    out_dir/TRACE (trace_command): the kernels by total time, and the bench
+    line of the same run."""
+    import csv
+    import glob
+    d = os.path.join(out_dir, "TRACE")
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"summarize-trace: no kernel_stats.csv under {d}")
+    with open(stats[0]) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    name, what = TRACES[workload]
+    lines = [f"rocprofv3 kernel-trace summary: {what}.", "",
+             "Command (repository root on the GPU box; cd /tmp && export TMPDIR=/tmp first):",
+             "  " + trace_command(workload),
+             "  (bench.py: 200 ms device-copy prewarm, then per timed call: warmup steps, 50 timed steps, "
+             "50 more with per-launch kernel events)", "",
+             f"{'kernel':<66}{'calls':>7}{'avg us':>10}{'min us':>10}{'max us':>10}{'% time':>8}"]
+    for r in rows[:14]:
+        k = r["Name"].replace("void kvdec::(anonymous namespace)::", "").replace("void kvdec::", "")
+        k = k.replace("kvdec::(anonymous namespace)::", "").replace("kvdec::", "")
+        k = k.split("(")[0] if not k.startswith("void at::") else k[:64]
+        lines.append(f"{k[:64]:<66}{int(r['Calls']):>7}{float(r['AverageNs']) / 1e3:>10.2f}"
+                     f"{float(r['MinNs']) / 1e3:>10.2f}{float(r['MaxNs']) / 1e3:>10.2f}"
+                     f"{float(r['Percentage']):>8.2f}")
+    try:
+        with open(os.path.join(d, "bench.json")) as f:
+            b = json.loads(f.read().strip().splitlines()[-1])
+        lines += ["", "The bench line of the same run (under the profiler):",
+                  f"  value {b['value']} {b['unit']}, ms_per_step {b['ms_per_step']}",
+                  "  roofline: " + json.dumps(b["roofline"])]
+        for extra in ("attention", "lookup", "lookup_ahead", "prefetch", "topk_select", "by_split_point"):
+            if extra in b:
+                lines.append(f"  {extra}: " + json.dumps(b[extra]))
+    except (OSError, ValueError, IndexError, KeyError):
+        pass
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"summaries": [name]}))
+
+
+PMC_GROUPS = {"FETCH_SIZE": ["FETCH_SIZE"], "WRITE_SIZE": ["WRITE_SIZE"],
+              "MFMA": ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                       "SQ_BUSY_CYCLES"],
+              "LDS": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]}
+
+
+def pmc_command(workload, group):
+    """The rocprofv3 counter run of one group (each group a run of its own,
+    the program straight after --), from the repository root on the GPU machine."""
+    return (f"rocprofv3 --pmc {' '.join(PMC_GROUPS[group])} -f csv -d <out>/{group} -o run -- "
+            f"python3 <repo>/bench.py --workload {workload} --no-cpu-baseline --no-stream-read "
+            f"--steps 10 --warmup 3 --prewarm-ms 0 --calibrate-copy > <out>/{group}/bench.json")
+
+
+def summarize_pmc(workload, out_dir):
+    """Writes the counter summaries of `workload` into profiles/ from the
+    rocprofv3 runs in out_dir/<group>/ (pmc_command).  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are scaled by what the same counters read
+    for the calibration run's 1 GiB device copies (__amd_rocclr_copyBuffer),
+    and compared with the algorithmic bytes the bench line reports."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def group(name):
+        files = glob.glob(os.path.join(out_dir, name, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            return None, None
+        per = defaultdict(lambda: defaultdict(list))  # kernel -> counter -> [(value, grid, ns)]
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                per[r["Kernel_Name"]][r["Counter_Name"]].append(
+                    (float(r["Counter_Value"]), int(r["Grid_Size"]),
+                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        bench_line = None
+        try:
+            with open(os.path.join(out_dir, name, "bench.json")) as f:
+                bench_line = json.loads(f.read().strip().splitlines()[-1])
+        except (OSError, ValueError, IndexError):
+            pass
+        agents = glob.glob(os.path.join(out_dir, name, "**", "*agent_info.csv"), recursive=True)
+        gpu = {}
+        if agents:
+            with open(agents[0]) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Agent_Type") == "GPU":
+                        gpu = r
+        return per, (bench_line, gpu)
+
+    def mean_of(per, match, counter, exclude=()):
+        vals = [v for k, cs in per.items() if match in k and not any(e in k for e in exclude)
+                for v in cs.get(counter, [])]
+        return (sum(v[0] for v in vals) / len(vals), len(vals), sum(v[2] for v in vals) / len(vals)) if vals else None
+
+    def calibration(per, counter, nbytes):
+        # the calibration copies (nbytes each) read the most: other copies
+        # through the same copy kernel (a prewarm) are 4 times smaller
+        vals = [v[0] for k, cs in per.items() if "copyBuffer" in k for v in cs.get(counter, [])]
+        top = max(vals)
+        sel = [v for v in vals if v >= 0.75 * top]
+        return nbytes / (sum(sel) / len(sel) * 1024.0)
+
+    fetch, fmeta = group("FETCH_SIZE")
+    write, _ = group("WRITE_SIZE")
+    targets = [workload] + (["kvpr-opt13b-attention"] if workload == "kvpr-opt13b" else [])
+    written = []
+    for tw in targets:
+        name, match, sources = COUNTERS[tw]
+        bench_line = fmeta[0] if fmeta else None
+        out = {"kernel": match.rstrip("<"), "workload": tw, "kernel_source_hash": source_hash(sources),
+               "commands": [pmc_command(workload, g) for g in PMC_GROUPS
+                            if os.path.isdir(os.path.join(out_dir, g))]}
+        if fetch is not None and write is not None:
+            if not bench_line or "calibration_copy_bytes" not in bench_line:
+                raise SystemExit("summarize-pmc: the counter runs need --calibrate-copy")
+            cb = int(bench_line["calibration_copy_bytes"])
+            ff, fw = calibration(fetch, "FETCH_SIZE", cb), calibration(write, "WRITE_SIZE", cb)
+            fk, nf, _ = mean_of(fetch, match, "FETCH_SIZE")
+            wk, nw, _ = mean_of(write, match, "WRITE_SIZE")
+            hbm = int(round((fk * ff + wk * fw) * 1024))
+            out.update({"fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                        "dispatches": nf,
+                        "copy_calibration": {"fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
+                                             "copy_bytes": cb,
+                                             "note": "device-to-device copies of copy_bytes "
+                                                     "(__amd_rocclr_copyBuffer) read by the same counters "
+                                                     "in the same process"},
+                        "hbm_bytes_per_launch": hbm})
+            algo = None
+            if bench_line:
+                if tw == "kvpr-opt13b":
+                    algo = bench_line["roofline"].get("bytes_per_launch")
+                elif tw == "kvpr-opt13b-attention":
+                    algo = bench_line.get("attention", {}).get("bytes")
+                else:
+                    algo = bench_line["roofline"].get("bytes_per_launch")
+            if algo:
+                out["algorithmic_bytes_per_launch"] = int(algo)
+                out["traffic_over_algorithmic"] = round(hbm / algo, 4)
+            if "decode_balanced_kernel" in match:
+                mf = mean_of(fetch, "decode_balanced_merge_kernel<", "FETCH_SIZE")
+                mw = mean_of(write, "decode_balanced_merge_kernel<", "WRITE_SIZE")
+                if mf and mw:
+                    out["merge_kernel_fetch_kib"] = round(mf[0], 1)
+                    out["merge_kernel_write_kib"] = round(mw[0], 1)
+        if tw == "kvpr-opt13b":
+            mfma, mmeta = group("MFMA")
+            if mfma is not None:
+                gpu = mmeta[1]
+                xcc = int(gpu.get("Num_Xcc", 8) or 8)
+                simds = int(gpu.get("Simd_Count", 0) or 0) or 4 * int(gpu.get("Cu_Count", 256))
+                busy, n, ns = mean_of(mfma, match, "SQ_VALU_MFMA_BUSY_CYCLES")
+                grbm, _, _ = mean_of(mfma, match, "GRBM_GUI_ACTIVE")
+                mops, _, _ = mean_of(mfma, match, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+                sqb, _, _ = mean_of(mfma, match, "SQ_BUSY_CYCLES")
+                active = grbm / xcc  # GRBM_GUI_ACTIVE is summed over the XCDs
+                out["mfma"] = {"sq_valu_mfma_busy_cycles": busy, "grbm_gui_active": grbm,
+                               "sq_insts_valu_mfma_mops_bf16": mops, "sq_busy_cycles": sqb,
+                               "xcds": xcc, "simds": simds, "dispatches": n,
+                               "kernel_ns_under_counters": round(ns, 1),
+                               "bf16_flop_per_launch": mops * 512,
+                               "busy_frac": round(busy / simds / active, 4),
+                               "implied_clock_ghz": round(active / ns, 3),
+                               "note": "busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per "
+                                       "XCD); the clock is GRBM_GUI_ACTIVE per XCD over the dispatch's time"}
+            lds, _ = group("LDS")
+            if lds is not None:
+                for variant in ("kv_recompute_kernel_wide<1>", "kv_recompute_kernel_wide<0>"):
+                    conf = mean_of(lds, variant, "SQ_LDS_BANK_CONFLICT")
+                    act = mean_of(lds, variant, "SQ_LDS_IDX_ACTIVE")
+                    if conf and act:
+                        out.setdefault("lds", {})[variant] = {
+                            "sq_lds_bank_conflict": conf[0], "sq_lds_idx_active": act[0],
+                            "conflict_frac_of_active": round(conf[0] / act[0], 4)}
+        with open(os.path.join(ROOT, "profiles", name), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        written.append(name)
+    print(json.dumps({"summaries": written}))
+
+
+def source_hash(sources) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_algorithmic, path=None):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+def counter_summary(workload):
+    """The workload's counter summary from profiles/, if it was taken on the
+    current sources of its kernel; else None."""
+    name, _, sources = COUNTERS[workload]
     try:
-        with open(path or TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("kernel_source_hash") == source_hash(sources) else None
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's main kernel, from its counter summary."""
+    t = counter_summary(workload)
+    return None if t is None else t.get("hbm_bytes_per_launch")
 
 
 WORKLOADS = ("llama3-8b-32k", "llama2-7b-paged", "clo-llama3-8b-128k", "clo-qwen2.5-14b-128k",
@@ -161,6 +400,18 @@ def stream_read_reference(K, torch, dev, stream, nbytes=2 << 30, reps=20):
             "tbs": round(nbytes / (ms / max(n, 1) * 1e-3) / 1e12, 4)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def oracle_seconds(fn, reps=3):
     times = []
     for _ in range(reps):
@@ -174,7 +425,7 @@ def hbm_roofline(kernel, nbytes, kern_us, traffic=None):
     gbs = nbytes / (kern_us * 1e-6) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel_us": round(kern_us, 2)}
+            "kernel_us": round(kern_us, 2), "bytes_per_launch": int(nbytes)}
 
 
 def common(args, workload, metric, unit, value, ms, dtype, data, config, higher=True):
@@ -235,8 +486,6 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
         K.kvdec_decode_attn(desc, q, k, v, None, cu, None, out, lse, ws, stream=stream)
 
     ms, kern_us, launches = time_steps(step, args.steps, args.warmup, stream, K, torch, args.prewarm_ms)
-    if args.calibrate_copy:
-        calibrate_copy(torch, dev)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     config = {"batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
               "context_lengths": "uniform [16384, 32768]", "total_tokens": T, "layout": "ragged",
@@ -258,7 +507,7 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
     r["kv_token_heads_per_s"] = round(T * Hkv / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
                                  step_bytes, kern_us,
-                                 measured_traffic(step_bytes, TRAFFIC_FILE_FP8 if fp8 else TRAFFIC_FILE))
+                                 measured_traffic("llama3-8b-32k-fp8" if fp8 else "llama3-8b-32k"))
     r["roofline"]["launches_timed"] = launches
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
     if not args.no_cpu_baseline:
@@ -278,7 +527,7 @@ def bench_llama3(args, K, np, torch, dev, stream, fp8=False):
                                                            cu_seqlens=d["cu_seqlens"]))
             sample = f"the full workload (all {B} sequences, {T} tokens), median of 3 runs, {cs:.2f} s each"
         r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
-                             "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
+                             "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle", "sample": sample}
         r["cpu_baseline"]["gpu_speedup"] = round(r["value"] / r["cpu_baseline"]["value"], 1)
         if not fp8:
             r["cpu_baseline"]["single_thread"] = single_thread_oracle(d, np, oracle, args.seed)
@@ -322,7 +571,7 @@ def bench_paged(args, K, np, torch, dev, stream):
     r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
     r["kv_token_heads_per_s"] = round(T * H / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-                                 step_bytes, kern_us)
+                                 step_bytes, kern_us, measured_traffic("llama2-7b-paged"))
     r["roofline"]["launches_timed"] = launches
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes", reps=20)
     if not args.no_cpu_baseline:
@@ -334,7 +583,7 @@ def bench_paged(args, K, np, torch, dev, stream):
                                                        seqlens=d["seqlens"][:n],
                                                        block_table=d["block_table"][:n], page_size=page))
         r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
-                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                              "sample": f"the first {n} of {B} sequences ({int(lens[:n].sum())} tokens), "
                                        f"median of 3 runs, {cs:.2f} s each"}
     return r
@@ -376,7 +625,7 @@ def bench_clo(args, K, np, torch, dev, stream, model):
     r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
     r["kv_token_heads_per_s"] = round(rows / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-                                 step_bytes, kern_us)
+                                 step_bytes, kern_us, measured_traffic(args.workload))
     r["roofline"]["launches_timed"] = launches
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
 
@@ -437,7 +686,7 @@ def bench_clo(args, K, np, torch, dev, stream, model):
                                                        d["pers_len"][:1], d["buf_k"][:1], d["buf_v"][:1],
                                                        d["buf_len"][:Hkv], hmn, scale=d["scale"]))
         r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
-                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                              "sample": f"batch element 0 of {B} ({sub_rows} KV rows), median of 3 runs, "
                                        f"{cs:.2f} s each"}
     return r
@@ -560,7 +809,7 @@ def bench_gather(args, K, np, torch, dev, stream):
     r["pct_of_hbm_peak"] = round(100.0 * gbs / HBM_PEAK_GBS, 2)
     r["kv_token_heads_per_s"] = round(rows / (ms * 1e-3), 1)
     r["roofline"] = hbm_roofline("decode_balanced_kernel" if args.split_tokens == 0 else "decode_chunk_kernel",
-                                 step_bytes, kern_us)
+                                 step_bytes, kern_us, measured_traffic("clo-gather-llama3-8b-128k"))
     r["roofline"]["launches_timed"] = launches
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, step_bytes, "bytes")
 
@@ -584,7 +833,7 @@ def bench_gather(args, K, np, torch, dev, stream):
         cs = oracle_seconds(lambda: oracle.gather_attn(d["q"][:1], d["k"][:1], d["v"][:1], oi, on,
                                                        num_kv_heads=Hkv, scale=d["scale"]))
         r["cpu_baseline"] = {"value": round(sub_bytes / cs / 1e12, 6), "unit": "TB/s",
-                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                              "sample": f"sequence 0 of {B} ({sub_rows} selected rows), median of 3 runs, {cs:.2f} s each"}
     return r
 
@@ -619,9 +868,23 @@ def bench_kvpr(args, K, np, torch, dev, stream):
                "synthetic (seeded; X ~ N(0,1), W ~ N(0, 1/h), bf16)",
                {"batch": b, "hidden": h, "num_heads": H, "head_dim": D, "split_point": l,
                 "context": s, "flops_per_step": flops, "w_layout": "out_in (nn.Linear)"})
+    # algorithmic bytes of one call: X, W_K and W_V read, the K/V rows written
+    rbytes = b * l * h * 2 + 2 * h * h * 2 + 2 * b * l * h * 2
+    c = counter_summary("kvpr-opt13b")
     r["roofline"] = {"bound": "mfma", "kernel": "kv_recompute_kernel_wide", "achieved": round(kern_tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(kern_tflops / 2500.0, 4),
-                     "traffic": None, "kernel_us": round(kern_us, 2), "launches_timed": launches}
+                     "traffic": c.get("hbm_bytes_per_launch") if c else None, "bytes_per_launch": rbytes,
+                     "kernel_us": round(kern_us, 2), "launches_timed": launches}
+    if c and "mfma" in c:
+        m = c["mfma"]
+        peak_at_clock = m["simds"] * 1024 * m["implied_clock_ghz"] * 1e9 / 1e12  # bf16: 1024 flop/clk/SIMD
+        r["roofline"]["counters"] = {
+            "mfma_busy_frac": m["busy_frac"], "implied_clock_ghz": m["implied_clock_ghz"],
+            "mfma_peak_at_that_clock_tflops": round(peak_at_clock, 1),
+            "source": "profiles/" + COUNTERS["kvpr-opt13b"][0]}
+        if "lds" in c:
+            r["roofline"]["counters"]["lds_bank_conflict_frac"] = {
+                k: v["conflict_frac_of_active"] for k, v in c["lds"].items()}
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, flops, "flops", reps=20)
     io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)
     r["w_in_out"] = {"ms_per_step": round(io_ms, 4), "tflops": round(flops / (io_ms * 1e-3) / 1e12, 2),
@@ -641,13 +904,14 @@ def bench_kvpr(args, K, np, torch, dev, stream):
     abytes = b * s * H * D * 4 + b * H * D * 4 + b * H * 4
     r["attention"] = {"us_per_call": round(ams * 1e3, 2), "kernel_us": round(akern_us, 2),
                       "bytes": abytes, "tbs": round(abytes / (ams * 1e-3) / 1e12, 4),
-                      "kernel_frac_of_hbm_peak": round(abytes / (akern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                      "kernel_frac_of_hbm_peak": round(abytes / (akern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic("kvpr-opt13b-attention")}
     if not args.no_cpu_baseline:
         import oracle
         rows = np.arange(0, b * l, (b * l) // 16, dtype=np.int32)  # 16 of the b*l rows
         cs = oracle_seconds(lambda: oracle.kv_recompute(d["x"], d["w_k"], d["w_v"], l=l, rows=rows))
         r["cpu_baseline"] = {"value": round(4.0 * rows.size * h * h / cs / 1e12, 6), "unit": "TFLOP/s",
-                             "cores": oracle.max_threads(), "kind": "oracle",
+                             "cores": oracle.max_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                              "sample": f"{rows.size} of the {b * l} recomputed rows (both K and V), "
                                        f"median of 3 runs, {cs:.2f} s each"}
     return r
@@ -744,11 +1008,14 @@ def bench_kvpr_overlap(args, K, np, torch, dev, stream):
 
 
 def calibrate_copy(torch, dev):
+    """Three 1 GiB device-to-device copies: what HBM counters read for a
+    copy of known size, in the same process as the kernels they scale."""
     src = torch.ones(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+    return src.numel() * src.element_size()
 
 
 def main():
@@ -766,7 +1033,19 @@ def main():
                     help="skip the streaming-read reference (HBM read rate of one kernel on this box)")
     ap.add_argument("--prewarm-ms", type=float, default=200.0,
                     help="device copies before the warmup steps, to bring the unlocked clocks up")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="write the workload's counter summaries into profiles/ from the rocprofv3 "
+                         "counter runs in DIR/<group>/ (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the workload's kernel-trace summary into profiles/ from the rocprofv3 "
+                         "run in DIR/TRACE (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_pmc or args.summarize_trace:
+        if args.summarize_pmc:
+            summarize_pmc(args.workload, args.summarize_pmc)
+        if args.summarize_trace:
+            summarize_trace(args.workload, args.summarize_trace)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
@@ -794,6 +1073,8 @@ def main():
         r = bench_kvpr_overlap(args, K, np, torch, dev, stream)
     else:
         r = bench_kvpr(args, K, np, torch, dev, stream)
+    if args.calibrate_copy:
+        r["calibration_copy_bytes"] = calibrate_copy(torch, dev)
     if r["roofline"]["bound"] == "hbm" and not args.no_stream_read:
         ref = stream_read_reference(K, torch, dev, stream)
         r["stream_read"] = ref

@@ -1070,9 +1070,10 @@ struct ItemLine {
   }
 };
 
-// Waves of a first-round workgroup stream about 13% faster than the others
-// (measured on MI355X with the priority steps below: 0.435 vs 0.385 tiles/us
-// per wave on the 16 x 16K-32K ragged batch), so their columns get that much
+// Waves of a first-round workgroup stream faster than the others (measured on
+// MI355X with the priority steps below, per-wave wall-clock stamps on the
+// 16 x 16K-32K ragged batch and the CLO hybrid: 1.086 times the rate of the
+// later waves, the same on three boxes), so their columns get that much
 // more.  At most N columns, and equal weights below 2 tiles per column, so
 // that no column is empty.
 __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) {

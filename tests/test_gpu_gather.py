@@ -267,3 +267,21 @@ def test_clo_full_size_sampled():
                                 scale=d["scale"])
     check_close(go[1:2], ro, "gather 128K (sequence 1)")
     check_lse(gl[1:2], rl, "gather 128K lse (sequence 1)")
+
+
+def test_topk_maximum_length_all_sixteen_chunks():
+    # S = 262144, the longest sequence the selection takes: 16 chunks of 16384
+    # tokens, every count row of the threshold scan in use.  Head 0: rows
+    # 245000..246999 equal and scoring above every other row, a tie band
+    # across the chunk 14 / 15 boundary (token 245760), so the smallest 1500
+    # of them are kept.  Then every row (keep-all) and every row but one.
+    S = 262144
+    d = kvgen.dense_small(seed=78, B=1, Hq=4, Hkv=2, S=S, seqlens=[S])
+    qsum = np.asarray(d["q"][0, 0:2], np.float64).sum(axis=0)
+    d["k"][0, 245000:247000, 0] = 8.0 * np.where(qsum >= 0, 1.0, -1.0)
+    gi, gn = check_topk(d, 1500, "S=262144 tie band across chunks 14/15")
+    assert np.array_equal(gi[0, 0, :1500], np.arange(245000, 246500))
+    gi, gn = check_topk(d, S, "S=262144 keep all")
+    assert np.array_equal(gi[0, 0, :S], np.arange(S)) and np.array_equal(gi[0, 1, :S], np.arange(S))
+    gi, gn = check_topk(d, S - 1, "S=262144 all but one")
+    assert gn.tolist() == [S - 1, S - 1]
