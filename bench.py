@@ -262,6 +262,15 @@ def summarize_pmc(workload, out_dir):
                                "implied_clock_ghz": round(active / ns, 3),
                                "note": "busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per "
                                        "XCD); the clock is GRBM_GUI_ACTIVE per XCD over the dispatch's time"}
+                vend = [k for k in mfma if k.startswith("Cijk_")]
+                if vend:
+                    vb, vn, vns = mean_of(mfma, vend[0], "SQ_VALU_MFMA_BUSY_CYCLES")
+                    vg, _, _ = mean_of(mfma, vend[0], "GRBM_GUI_ACTIVE")
+                    out["vendor_gemm_mfma"] = {
+                        "kernel": vend[0][:120], "dispatches": vn,
+                        "busy_frac": round(vb / simds / (vg / xcc), 4),
+                        "implied_clock_ghz": round(vg / xcc / vns, 3),
+                        "kernel_ns_under_counters": round(vns, 1)}
             lds, _ = group("LDS")
             if lds is not None:
                 for variant in ("kv_recompute_kernel_wide<1>", "kv_recompute_kernel_wide<0>"):
@@ -882,10 +891,32 @@ def bench_kvpr(args, K, np, torch, dev, stream):
             "mfma_busy_frac": m["busy_frac"], "implied_clock_ghz": m["implied_clock_ghz"],
             "mfma_peak_at_that_clock_tflops": round(peak_at_clock, 1),
             "source": "profiles/" + COUNTERS["kvpr-opt13b"][0]}
+        if "vendor_gemm_mfma" in c:
+            r["roofline"]["counters"]["vendor_gemm_mfma_busy_frac"] = c["vendor_gemm_mfma"]["busy_frac"]
+            r["roofline"]["counters"]["vendor_gemm_implied_clock_ghz"] = c["vendor_gemm_mfma"]["implied_clock_ghz"]
         if "lds" in c:
             r["roofline"]["counters"]["lds_bank_conflict_frac"] = {
                 k: v["conflict_frac_of_active"] for k, v in c["lds"].items()}
     r["isolated_call"] = isolated_calls(step, stream, torch, dev, flops, "flops", reps=20)
+    # the vendor GEMM on the same product, in the same run: hipBLASLt through
+    # torch.matmul, X [b*l, h] times [W_K | W_V] [h, 2h], contiguous, bf16 out
+    xm = x.reshape(b * l, h)
+    wcat = torch.cat([wk_io, wv_io], dim=1).contiguous()
+    vout = torch.empty((b * l, 2 * h), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        torch.matmul(xm, wcat, out=vout)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        torch.matmul(xm, wcat, out=vout)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    vms = e0.elapsed_time(e1) / args.steps
+    r["vendor_gemm"] = {"library": "hipBLASLt (torch.matmul), bf16 output, same inputs",
+                        "us_per_call": round(vms * 1e3, 2),
+                        "tflops": round(flops / (vms * 1e-3) / 1e12, 2)}
+    del vout, wcat
     io_ms, io_kern_us, _ = time_steps(step_io, args.steps, args.warmup, stream, K, torch)
     r["w_in_out"] = {"ms_per_step": round(io_ms, 4), "tflops": round(flops / (io_ms * 1e-3) / 1e12, 2),
                      "kernel_us": round(io_kern_us, 2),
