@@ -1071,11 +1071,13 @@ struct ItemLine {
 };
 
 // Waves of a first-round workgroup stream faster than the others (measured on
-// MI355X with the priority steps below, per-wave wall-clock stamps on the
-// 16 x 16K-32K ragged batch and the CLO hybrid: 1.086 times the rate of the
-// later waves, the same on three boxes), so their columns get that much
-// more.  At most N columns, and equal weights below 2 tiles per column, so
-// that no column is empty.
+// MI355X with the priority steps below: 1.086 times the rate of the later
+// waves on the 16 x 16K-32K ragged batch and the CLO hybrid, on three boxes),
+// so their columns get more: 1.13 times as much, which also lightens the
+// later waves, among them the slowest (a later-round wave on a slow XCD ends
+// the kernel; weighting by the rate ratio alone left it 1-3 us later in a
+// simulation on the measured per-wave rates).  At most N columns, and equal
+// weights below 2 tiles per column, so that no column is empty.
 __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) {
   ItemLine L;
   L.N = N;

@@ -19,7 +19,7 @@ constexpr int kWaves = 4;         // waves per attention workgroup
 constexpr int kMaxGroup = 8;      // query heads per KV head handled by one workgroup
 constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
 constexpr int kMinTilesPerWave = 8;
-constexpr int kFirstRoundWeight = 109;  // balanced: per 100, share of a first-round column
+constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-round column
 
 // Tile schedules of the attention kernels.
 enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };

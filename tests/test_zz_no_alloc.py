@@ -95,3 +95,34 @@ def test_noalloc_rejects_beyond_the_scratch_and_launches_nothing():
     assert e.value.status == _lib.KVDEC_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+def test_noalloc_replays_under_graph_capture():
+    # The call this entry point is for: captured once in a graph, replayed
+    # with new queries written between replays by ordinary eager work; every
+    # replay must equal the workspace call on the same inputs, bit for bit.
+    d = kvgen.ragged_llama(seed=26, B=8, lo=1000, hi=3000)
+    desc, (q, k, v, _, cu) = _desc_and_args(d)
+    B, Hq = d["B"], d["Hq"]
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    say("[noalloc] graph capture, 3 replays")
+    K.kvdec_decode_attn_noalloc(desc, q, k, v, None, cu, None, out, lse)  # first use: set-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.kvdec_decode_attn_noalloc(desc, q, k, v, None, cu, None, out, lse)
+    torch.cuda.synchronize()
+    ws = K.alloc_workspace(K.kvdec_decode_attn_workspace(desc))
+    ref = torch.empty_like(out)
+    ref_lse = torch.empty_like(lse)
+    gen = torch.Generator(device="cuda").manual_seed(27)
+    for rep in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(torch.float16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        K.kvdec_decode_attn(desc, q, k, v, None, cu, None, ref, ref_lse, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(ref)), rep
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref_lse.cpu().numpy().view(np.uint32))
