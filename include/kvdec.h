@@ -113,7 +113,8 @@ typedef struct {
 /* Workspace bytes kvdec_decode_attn needs for this descriptor on the current
  * device (0 only with split_tokens > 0 when every sequence fits one work
  * item).  The workspace holds the per-call partial results; its contents need
- * no initialisation and are dead after the call's kernels finish.  The size
+ * no initialisation and are dead after the call's kernels finish.  It must be
+ * 16-byte aligned (KVDEC_ERR_WORKSPACE otherwise).  The size
  * depends on the device's compute-unit count: query it on the device that
  * will run the call. */
 kvdec_status kvdec_decode_attn_workspace(const kvdec_attn_desc* desc, size_t* bytes /*(host)*/);

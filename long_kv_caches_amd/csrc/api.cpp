@@ -197,6 +197,8 @@ static kvdec_status run_attn(const kvdec_attn_desc* d, const Plan& p, AttnArgs& 
     if (!attn_workspace_carve(ws, ws_bytes, slots, a.G, n_pref, &a))
       return fail(KVDEC_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", attn_ws(d, p),
                   ws_bytes, ws ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+      return fail(KVDEC_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   }
   if (p.mode == MODE_CHUNKS && (int64_t)d->batch * p.n_chunks * d->num_kv_heads > INT32_MAX)
     return fail(KVDEC_ERR_UNSUPPORTED, "grid too large");

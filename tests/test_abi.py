@@ -91,6 +91,8 @@ def test_decode_pointer_and_workspace_validation():
     assert _decode(big, ws=None, ws_bytes=0) == K._lib.KVDEC_ERR_WORKSPACE
     assert _decode(big, ws=FAKE, ws_bytes=need - 1) == K._lib.KVDEC_ERR_WORKSPACE
     assert str(need) in K.last_error()
+    assert _decode(big, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == K._lib.KVDEC_ERR_WORKSPACE
+    assert "16-byte aligned" in K.last_error()
     # empty batch is a no-op success
     assert _decode(_desc(batch=0)) == K._lib.KVDEC_OK
 
