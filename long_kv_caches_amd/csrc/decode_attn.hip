@@ -221,6 +221,27 @@ __device__ __forceinline__ uint32_t gather_offset(const AttnArgs& a, uint32_t to
   return valid ? (uint32_t)t * row_bytes + piece : kOutsideRows;
 }
 
+// Page of the tile whose first row is t0 of sequence b (0 when !active),
+// clamped into the pool.  A scalar load: the entry is the same for the whole
+// wave, and waiting for a scalar load does not wait for the K/V loads the
+// wave has in flight, which waiting for a vector load would (vector loads
+// complete in issue order).
+__device__ __forceinline__ int tile_page(const AttnArgs& a, int b, int t0, bool active) {
+  using ConstI32 = const __attribute__((address_space(4))) int32_t*;
+  int pg = 0;
+  if (active) pg = ((ConstI32)a.block_table)[(int64_t)b * a.max_pages + t0 / a.page];
+  return uniform_i32(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
+}
+
+// Bytes of the valid rows of the tile whose first row is t0 (0 when !active
+// or past the end), from wave-uniform values: scalar arithmetic, with no
+// vector register taken for it while the wave's loads are in flight.
+__device__ __forceinline__ uint32_t tile_bytes(int len, int t0, bool active, uint32_t row_bytes) {
+  const int rem = uniform_i32(len - t0);
+  if (!active || rem <= 0) return 0u;
+  return (uint32_t)(rem < kTile ? rem : kTile) * row_bytes;
+}
+
 // Loads K and V of the tile whose first row is t0 of pair (b, g) into kf, vf.
 // The rows come through buffer resources whose base is the tile's first row
 // (scalar registers) and whose size covers only rows below len, so rows past
@@ -260,14 +281,13 @@ __device__ __forceinline__ void load_kv_tile(const AttnArgs& a, int b, int g, co
   }
   int64_t row0;  // byte offset of the tile's first row
   if constexpr (SRC == SRC_PAGED) {
-    int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
-    pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));  // a.S: pages in the pool
+    const int pg = tile_page(a, b, t0, active);
     // never straddles pages
     row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim * kKvBytes<KIND>;
   } else {
     row0 = (int64_t)t0 * row_bytes;
   }
-  const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+  const uint32_t nbytes = tile_bytes(len, t0, active, row_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
   if constexpr (kKv8<KIND>) {
@@ -681,13 +701,12 @@ struct MfmaPath {
     }
     int64_t row0;  // byte offset of the tile's first row
     if constexpr (SRC == SRC_PAGED) {
-      int pg = active ? a.block_table[(int64_t)b * a.max_pages + t0 / a.page] : 0;
-      pg = __builtin_amdgcn_readfirstlane(min(max(pg, 0), a.S - 1));
+      const int pg = tile_page(a, b, t0, active);
       row0 = (((int64_t)pg * a.Hkv + g) * a.page + t0 % a.page) * kHeadDim * kKvBytes<KIND>;
     } else {
       row0 = (int64_t)t0 * row_bytes;
     }
-    const uint32_t nbytes = uniform_u32(rows > 0 ? (uint32_t)rows * row_bytes : 0u);
+    const uint32_t nbytes = tile_bytes(len, t0, active, row_bytes);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kb + row0), nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vb + row0), nbytes);
 #pragma unroll
