@@ -1432,6 +1432,16 @@ int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles) {
     case KIND_F16 | KIND_KV8: occ = dispatch_g<KIND_F16 | KIND_KV8, OccF>(G, src); break;
     default: occ = dispatch_g<KIND_BF16 | KIND_KV8, OccF>(G, src); break;
   }
+  // fp16 K/V read from runs (not gathered rows): one workgroup per CU.  Its
+  // four waves, one per SIMD, read faster than two or three workgroups' worth
+  // (measured on MI355X, one process, interleaved: the 16 x 16K-32K ragged
+  // batch 237.1 -> 236.1 us, the CLO hybrid 111.1 -> 107.0, the 1024-sequence
+  // MHA batch 3377 -> 3348; a read probe with the same tiles: 6.9 TB/s at
+  // two workgroups per CU, 7.1 at one), and every column then starts in the
+  // first dispatch round.  bf16 (P.V in two halves), e4m3 (decoding) and
+  // gathered rows (index loads) have more to do per byte and lose with one
+  // (+1, +17 and +8 us), so they keep the resident maximum.
+  if (dtype == KIND_F16 && !kv8 && src != SRC_GATHER) occ = 1;
   const int64_t cap = (int64_t)device_cu_count() * occ;
   // at least kMinTilesPerWave tiles per wave when the work is small
   const int64_t need = (est_tiles + (int64_t)kWaves * kMinTilesPerWave - 1) / ((int64_t)kWaves * kMinTilesPerWave);
