@@ -1067,27 +1067,67 @@ __device__ void build_units(const AttnArgs& a, const UnitTable& ut) {
 }
 
 // Items of the line: columns k < Wc <= (persistent waves) / LH; item
-// k * LH + h (column k, line head h) belongs to persistent wave k * LH + h.
-// Column k holds line tiles [first(k), first(k + 1)), first(k) =
-// N * cum(k) / total: columns run by workgroups of the first dispatch round
-// (one per CU: blocks below the CU count) weigh w0, the others w1.  The main
-// and the merge kernel cut the line the same way from its length N.
+// k * LH + h (column k, line head h) belongs to the wave that runs column k
+// for line head h.  Column k holds line tiles [first(k), first(k + 1)),
+// first(k) = N * cum(k) / total, cum(k) the sum of the weights of columns
+// below k: a column run by workgroups of the first dispatch round (one per
+// CU: blocks below the CU count) weighs w0, the others w1, and where the
+// columns alternate between even and odd XCDs (xcd_cols), an odd column that
+// times wo / 100.  The main and the merge kernel cut the line the same way
+// from its length N.
 struct ItemLine {
   int N, Wc, C0;          // C0: columns of the first round
-  int w0, w1;
+  int w0, w1, wo;
+  bool xcd_cols;
   int64_t total;          // cum(Wc)
+  // sum over columns c < n of 100, or wo for the odd ones
+  __device__ int64_t xsum(int n) const { return 100 * (int64_t)n - (int64_t)(100 - wo) * (n >> 1); }
   __device__ int64_t cum(int k) const {
-    return k <= C0 ? (int64_t)w0 * k : (int64_t)w0 * C0 + (int64_t)w1 * (k - C0);
+    if (!xcd_cols)  // (all columns of one XCD weight; the common case, kept short)
+      return k <= C0 ? (int64_t)w0 * k : (int64_t)w0 * C0 + (int64_t)w1 * (k - C0);
+    return k <= C0 ? (int64_t)w0 * xsum(k)
+                   : (int64_t)w0 * xsum(C0) + (int64_t)w1 * (xsum(k) - xsum(C0));
   }
   __device__ int first(int k) const { return (int)((int64_t)N * cum(k) / total); }
-  // the column that holds tile x (x < N): the largest k with first(k) <= x
+  // the column that holds tile x (x < N): the largest k < Wc with first(k) <= x
   __device__ int of_tile(int x) const {
-    const int64_t lim = (int64_t)(x + 1) * total;  // first(k) <= x  <=>  N * cum(k) < lim
-    if (C0 >= Wc || (int64_t)N * w0 * C0 >= lim)
-      return (int)((lim - 1) / ((int64_t)N * w0));
-    return C0 + (int)((lim - 1 - (int64_t)N * w0 * C0) / ((int64_t)N * w1));
+    int lo = 0, hi = Wc;  // first(lo) <= x < first(hi) = N
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (first(mid) <= x) lo = mid;
+      else hi = mid;
+    }
+    return lo;
   }
 };
+
+// Which column and line head a wave runs.  With a.xcd_cols set (the host sets
+// it when a column's LH waves fill m >= 4 whole workgroups, LH = 4m as with
+// 32 KV heads, and the grid is one dispatch round, at most one workgroup per
+// CU, of whole groups of 8m workgroups) the m workgroups of a column are on
+// one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs column
+// 8 (t / m) + x for heads 4 (t % m) ...  Otherwise wave w = 4b + i runs
+// column w / LH for head w % LH.  (Measured on MI355X: on the paged 1024 x
+// 32-head batch, one XCD per column 3376 -> 3361 us, and with odd XCDs
+// weighted 0.90, 3312 us; the 8-head headline gained nothing from either,
+// and e4m3, at three workgroups per CU, lost 1-2 us.)
+struct ColumnOf {
+  int col, head;
+};
+__device__ __forceinline__ ColumnOf column_of(const AttnArgs& a, int LH) {
+  ColumnOf c;
+  const int b = (int)blockIdx.x, wave = (int)(threadIdx.x >> 6);
+  if (a.xcd_cols) {
+    const int m = LH / kWaves, x = b % 8, t = b / 8;
+    c.col = (t / m) * 8 + x;
+    c.head = (t % m) * kWaves + wave;
+  } else {
+    const int w = b * kWaves + wave;
+    c.col = w / LH;
+    c.head = w - c.col * LH;
+  }
+  return c;
+}
 
 // Waves of a first-round workgroup stream faster than the others (measured on
 // MI355X with the priority steps below: 1.086 times the rate of the later
@@ -1095,8 +1135,13 @@ struct ItemLine {
 // so their columns get more: 1.13 times as much, which also lightens the
 // later waves, among them the slowest (a later-round wave on a slow XCD ends
 // the kernel; weighting by the rate ratio alone left it 1-3 us later in a
-// simulation on the measured per-wave rates).  At most N columns, and equal
-// weights below 2 tiles per column, so that no column is empty.
+// simulation on the measured per-wave rates).  Waves on odd-numbered XCDs
+// stream slower than those on even ones (measured on MI355X with one
+// workgroup per CU: 0.94-0.98 against 1.00-1.06 of the mean on the CLO
+// hybrid), so where a column's waves share one XCD (a.xcd_cols, column_of),
+// columns on odd XCDs get kOddXcdWeight / 100 as much.  At
+// most N columns, and equal weights below 2 tiles per column, so that no
+// column is empty.
 __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) {
   ItemLine L;
   L.N = N;
@@ -1105,6 +1150,10 @@ __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) 
   const bool weighted = N >= 2 * L.Wc;
   L.w0 = weighted ? kFirstRoundWeight : 100;
   L.w1 = 100;
+  // the XCD weight where a column's waves share one XCD and every column
+  // runs in the first dispatch round
+  L.xcd_cols = a.xcd_cols != 0;  // column c on XCD c % 8
+  L.wo = weighted && L.xcd_cols ? kOddXcdWeight : 100;
   L.total = L.cum(L.Wc);
   return L;
 }
@@ -1201,9 +1250,9 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int LH = line_heads<SRC>(a);
+  const ColumnOf co = column_of(a, LH);
   const ItemLine L = item_line(a, uniform_i32(ut.pref[a.n_units]), LH);
-  const int gw = uniform_i32((int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6));
-  const int lk = gw / LH, lh = gw - (gw / LH) * LH;
+  const int lk = uniform_i32(co.col), lh = uniform_i32(co.head);
   if (lk >= L.Wc) return;
   const int x_end = uniform_i32(L.first(lk + 1));
   const int share = x_end - uniform_i32(L.first(lk));

@@ -20,6 +20,7 @@ constexpr int kMaxGroup = 8;      // query heads per KV head handled by one work
 constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
 constexpr int kMinTilesPerWave = 8;
 constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-round column
+constexpr int kOddXcdWeight = 90;       // balanced: per 100, share of a column on an odd XCD
 
 // Tile schedules of the attention kernels.
 enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };
@@ -59,6 +60,7 @@ struct AttnArgs {
   int n_blocks;                 // balanced: persistent workgroups
   int n_cu;                     // balanced: CUs of the device (workgroups of the first round)
   int n_units;                  // balanced: units of the tile line
+  int xcd_cols;                 // balanced: each column's workgroups on one XCD (column c on XCD c % 8)
   float scale_log2;             // softmax_scale * log2(e) (* k_scale for e4m3 K)
   float out_scale;              // e4m3 V: v_scale, applied with the final normalisation
   int src;
@@ -72,6 +74,12 @@ size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_pref);
 // returns false if ws_bytes is too small.
 bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_pref,
                           AttnArgs* a);
+// Whether the balanced schedule puts each column's workgroups on one XCD:
+// line_heads = 4m with m >= 4, n_blocks <= n_cu and a multiple of 8m.
+inline bool balanced_xcd_cols(int line_heads, int n_blocks, int n_cu) {
+  const int m = line_heads / kWaves;
+  return line_heads % kWaves == 0 && m >= 4 && n_blocks % (8 * m) == 0 && n_blocks <= n_cu;
+}
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
 int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);

@@ -139,6 +139,13 @@ def test_paged_mha_reduced_batch():
     _parity(d, "paged Llama-2-7B MHA, B=96", split_tokens=256)  # 3072 heads: 8-row merge
 
 
+def test_ragged_mha_columns_on_one_xcd():
+    # 32 KV heads with enough tiles for a full one-workgroup-per-CU grid: each
+    # column's eight workgroups run on one XCD, with odd XCDs' columns weighted
+    d = kvgen.ragged_llama(seed=18, lens=[1000, 1777, 64, 2049, 900, 1, 1500, 1311], Hq=32, Hkv=32)
+    _parity(d, "ragged MHA 8 sequences x 32 heads")
+
+
 def test_merge_of_many_short_heads():
     # 260 x 32 = 8320 query heads: the merge folds 4 rows of partials per head
     d = kvgen.dense_small(seed=17, B=260, Hq=32, Hkv=16, S=256)
