@@ -152,9 +152,10 @@ static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
 static void ws_shape(const kvdec_attn_desc* d, const Plan& p, int64_t* slots, int64_t* n_pref) {
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
   if (p.mode == MODE_BALANCED) {
-    // slot (item + unit) * LH + h
+    // slot (item + unit) * LH + h; the line prefix [n_units + 1] and each
+    // unit's first and last column [n_units][2]
     *slots = (p.max_items + p.n_units) * p.line_heads;
-    *n_pref = (int64_t)p.n_units + 1;
+    *n_pref = 3 * (int64_t)p.n_units + 1;
   } else {
     *slots = p.n_chunks > 1 ? pairs * p.n_chunks : 0;
     *n_pref = 0;

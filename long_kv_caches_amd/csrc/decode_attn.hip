@@ -1089,15 +1089,23 @@ struct ItemLine {
                    : (int64_t)w0 * xsum(C0) + (int64_t)w1 * (xsum(k) - xsum(C0));
   }
   __device__ int first(int k) const { return (int)((int64_t)N * cum(k) / total); }
-  // the column that holds tile x (x < N): the largest k < Wc with first(k) <= x
+  // the largest n with xsum(n) <= u (xsum grows by 100 + wo every two columns)
+  __device__ int xsum_inv(int64_t u) const {
+    const int64_t pair = 100 + wo, p = u / pair;
+    return (int)(2 * p + (u - p * pair >= 100 ? 1 : 0));
+  }
+  // the column that holds tile x (x < N): the largest k with first(k) <= x
   __device__ int of_tile(int x) const {
-    int lo = 0, hi = Wc;  // first(lo) <= x < first(hi) = N
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (first(mid) <= x) lo = mid;
-      else hi = mid;
+    const int64_t lim = (int64_t)(x + 1) * total;  // first(k) <= x  <=>  N * cum(k) < lim
+    if (!xcd_cols) {
+      if (C0 >= Wc || (int64_t)N * w0 * C0 >= lim)
+        return (int)((lim - 1) / ((int64_t)N * w0));
+      return C0 + (int)((lim - 1 - (int64_t)N * w0 * C0) / ((int64_t)N * w1));
     }
-    return lo;
+    const int64_t t = (lim - 1) / N;  // the largest cum(k) allowed
+    const int64_t c0 = (int64_t)w0 * xsum(C0);
+    const int k = C0 >= Wc || c0 > t ? xsum_inv(t / w0) : xsum_inv(xsum(C0) + (t - c0) / w1);
+    return min(k, Wc - 1);
   }
 };
 
@@ -1253,6 +1261,18 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   const ColumnOf co = column_of(a, LH);
   const ItemLine L = item_line(a, uniform_i32(ut.pref[a.n_units]), LH);
   const int lk = uniform_i32(co.col), lh = uniform_i32(co.head);
+  // Each unit's first and last column, for the merge kernel (which would
+  // otherwise recompute them with 64-bit divisions in each of its many
+  // workgroups); unit u goes to lane u / n_blocks of block u % n_blocks,
+  // before any wave leaves.
+  for (int u = (int)threadIdx.x * a.n_blocks + (int)blockIdx.x; u < a.n_units;
+       u += 256 * a.n_blocks) {
+    const int ub = ut.pref[u], ue = ut.pref[u + 1];
+    if (ue > ub) {
+      a.ws_cols[2 * u] = L.of_tile(ub);
+      a.ws_cols[2 * u + 1] = L.of_tile(ue - 1);
+    }
+  }
   if (lk >= L.Wc) return;
   const int x_end = uniform_i32(L.first(lk + 1));
   const int share = x_end - uniform_i32(L.first(lk));
@@ -1346,8 +1366,7 @@ __global__ __launch_bounds__(32 * ROWS) void decode_balanced_merge_kernel(AttnAr
     if (threadIdx.x == 0 && a.lse) a.lse[head0 + j] = -INFINITY;
     return;
   }
-  const ItemLine L = item_line(a, a.ws_pref[a.n_units], LH);
-  const int k0 = L.of_tile(ubase), k1 = L.of_tile(uend - 1);  // columns, each non-empty
+  const int k0 = a.ws_cols[2 * u], k1 = a.ws_cols[2 * u + 1];  // columns, each non-empty
   if (k0 == k1) return;  // one item covered the pair and wrote the output
   merge_head<KIND, G, ROWS>(a, head0, j, (int64_t)(k0 + u) * LH + h, LH, k1 - k0 + 1);
 }
@@ -1512,6 +1531,8 @@ bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64
   a->ws_ml = reinterpret_cast<float*>(p);
   p += up((size_t)slots * G * 2 * 4);
   a->ws_pref = n_pref > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;
+  // balanced: the units' column ranges follow the prefix (n_pref = 3 n_units + 1)
+  a->ws_cols = n_pref > 0 ? a->ws_pref + (n_pref - 1) / 3 + 1 : nullptr;
   return true;
 }
 

@@ -47,6 +47,7 @@ struct AttnArgs {
   float* ws_o;                  // [slots, G, 128] unnormalised partial outputs
   float* ws_ml;                 // [slots, G, 2] partial (max, sum) in log2 units
   int32_t* ws_pref;             // balanced: [n_units + 1] first tile of each unit
+  int32_t* ws_cols;             // balanced: [n_units][2] first and last column of each unit
   int B, Hq, Hkv, G;
   int S;                        // dense: rows per sequence; ragged: token rows T;
                                 // paged: pages P in the pool
