@@ -73,8 +73,6 @@ class Draws:
         if scale is not None:
             sc = np.asarray(scale, np.float32)
             sc_row = np.broadcast_to(sc, shape[len(shape) - sc.ndim:]).reshape(-1)
-            if BLOCK % sc_row.size:
-                raise ValueError("scale period must divide the block size")
         base = self._next_bitgen()
 
         def fill(i):
@@ -83,8 +81,10 @@ class Draws:
             blk = g.standard_normal(hi - lo, dtype=np.float32)
             if std != 1.0:
                 blk *= np.float32(std)
-            if sc_row is not None:
+            if sc_row is not None and BLOCK % sc_row.size == 0:
                 blk = (blk.reshape(-1, sc_row.size) * sc_row[None, :]).reshape(-1)
+            elif sc_row is not None:  # a period that straddles blocks (e.g. 40 x 128)
+                blk = blk * sc_row[np.arange(lo, hi) % sc_row.size]
             out[lo:hi] = blk.astype(np.float16) if out_dtype == np.float16 else f32_to_bf16_bits(blk)
 
         nblk = (n + BLOCK - 1) // BLOCK

@@ -146,6 +146,31 @@ def test_ragged_mha_columns_on_one_xcd():
     _parity(d, "ragged MHA 8 sequences x 32 heads")
 
 
+@pytest.mark.parametrize("hq,hkv,layout,bf16", [
+    (40, 40, "dense", False),   # OPT-13B's 40 heads: 25 columns of 40 on 1024 waves
+    (40, 40, "paged", False),
+    (40, 40, "ragged", True),
+    (24, 12, "ragged", False),
+    (10, 5, "dense", False),
+    (9, 3, "paged", False),     # G = 3, matrix-core tiles
+])
+def test_kv_heads_not_dividing_the_waves(hq, hkv, layout, bf16):
+    # Hkv does not divide the persistent waves: W % Hkv of them run no column
+    d = kvgen.ragged_llama(seed=22, lens=[700, 1, 0, 1333, 65, 2100], Hq=hq, Hkv=hkv)
+    if layout == "dense":
+        d = kvgen.ragged_to_dense(d)
+    elif layout == "paged":
+        d = kvgen.ragged_to_paged(d, seed=23)
+    _parity(d, f"{layout} {hq}/{hkv} heads, 6 sequences", bf16=bf16)
+
+
+def test_many_short_sequences_of_40_heads():
+    rng = np.random.default_rng(24)
+    lens = rng.integers(0, 40, size=1000).tolist()
+    d = kvgen.ragged_llama(seed=24, lens=lens, Hq=40, Hkv=40)
+    _parity(d, "ragged B=1000 x 40 heads, short sequences")
+
+
 def test_merge_of_many_short_heads():
     # 260 x 32 = 8320 query heads: the merge folds 4 rows of partials per head
     d = kvgen.dense_small(seed=17, B=260, Hq=32, Hkv=16, S=256)
