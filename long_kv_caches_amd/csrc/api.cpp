@@ -148,26 +148,26 @@ static Plan plan_hybrid(const kvdec_hybrid_desc* h) {
                    d->split_tokens);
 }
 
-// Partial slots and prefix entries the plan needs in the workspace.
-static void ws_shape(const kvdec_attn_desc* d, const Plan& p, int64_t* slots, int64_t* n_pref) {
+// Partial slots and column-table entries the plan needs in the workspace.
+static void ws_shape(const kvdec_attn_desc* d, const Plan& p, int64_t* slots, int64_t* n_cols) {
   const int64_t pairs = (int64_t)d->batch * d->num_kv_heads;
   if (p.mode == MODE_BALANCED) {
-    // slot (item + unit) * LH + h; the line prefix [n_units + 1] and each
-    // unit's first and last column [n_units][2]
+    // slot (item + unit) * LH + h; each unit's first and last column
+    // [n_units][2]
     *slots = (p.max_items + p.n_units) * p.line_heads;
-    *n_pref = 3 * (int64_t)p.n_units + 1;
+    *n_cols = 2 * (int64_t)p.n_units;
   } else {
     *slots = p.n_chunks > 1 ? pairs * p.n_chunks : 0;
-    *n_pref = 0;
+    *n_cols = 0;
   }
 }
 
 static size_t attn_ws(const kvdec_attn_desc* d, const Plan& p) {
   if (d->batch == 0) return 0;
-  int64_t slots, n_pref;
-  ws_shape(d, p, &slots, &n_pref);
-  if (slots == 0 && n_pref == 0) return 0;
-  return attn_workspace_bytes(slots, d->num_q_heads / d->num_kv_heads, n_pref);
+  int64_t slots, n_cols;
+  ws_shape(d, p, &slots, &n_cols);
+  if (slots == 0 && n_cols == 0) return 0;
+  return attn_workspace_bytes(slots, d->num_q_heads / d->num_kv_heads, n_cols);
 }
 
 static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
@@ -193,10 +193,10 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
 
 static kvdec_status run_attn(const kvdec_attn_desc* d, const Plan& p, AttnArgs& a, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-  int64_t slots, n_pref;
-  ws_shape(d, p, &slots, &n_pref);
-  if (slots > 0 || n_pref > 0) {
-    if (!attn_workspace_carve(ws, ws_bytes, slots, a.G, n_pref, &a))
+  int64_t slots, n_cols;
+  ws_shape(d, p, &slots, &n_cols);
+  if (slots > 0 || n_cols > 0) {
+    if (!attn_workspace_carve(ws, ws_bytes, slots, a.G, n_cols, &a))
       return fail(KVDEC_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", attn_ws(d, p),
                   ws_bytes, ws ? "" : " (NULL)");
     if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)

@@ -1253,25 +1253,21 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(AttnArgs a) {
   extern __shared__ int s_units[];
   const UnitTable ut{s_units, s_units + a.n_units + 1, s_units + 2 * a.n_units + 1};
   build_units<SRC>(a, ut);
-  if (blockIdx.x == 0)
-    for (int u = threadIdx.x; u <= a.n_units; u += 256) a.ws_pref[u] = ut.pref[u];
 
   const int lane = threadIdx.x & 63;
   const int LH = line_heads<SRC>(a);
   const ColumnOf co = column_of(a, LH);
   const ItemLine L = item_line(a, uniform_i32(ut.pref[a.n_units]), LH);
   const int lk = uniform_i32(co.col), lh = uniform_i32(co.head);
-  // Each unit's first and last column, for the merge kernel (which would
-  // otherwise recompute them with 64-bit divisions in each of its many
-  // workgroups); unit u goes to lane u / n_blocks of block u % n_blocks,
-  // before any wave leaves.
+  // Each unit's first and last column, (1, 0) for an empty unit, for the
+  // merge kernel (which would otherwise need the unit table and 64-bit
+  // divisions in each of its many workgroups); unit u goes to lane
+  // u / n_blocks of block u % n_blocks, before any wave leaves.
   for (int u = (int)threadIdx.x * a.n_blocks + (int)blockIdx.x; u < a.n_units;
        u += 256 * a.n_blocks) {
     const int ub = ut.pref[u], ue = ut.pref[u + 1];
-    if (ue > ub) {
-      a.ws_cols[2 * u] = L.of_tile(ub);
-      a.ws_cols[2 * u + 1] = L.of_tile(ue - 1);
-    }
+    *reinterpret_cast<int2*>(&a.ws_cols[2 * u]) =
+        ue > ub ? make_int2(L.of_tile(ub), L.of_tile(ue - 1)) : make_int2(1, 0);
   }
   if (lk >= L.Wc) return;
   const int x_end = uniform_i32(L.first(lk + 1));
@@ -1359,14 +1355,15 @@ __global__ __launch_bounds__(32 * ROWS) void decode_balanced_merge_kernel(AttnAr
   const int b = p / a.Hkv, g = p % a.Hkv;
   const int LH = line_heads<SRC>(a);
   const int u = kPairUnits<SRC> ? p : b, h = kPairUnits<SRC> ? 0 : g;
-  const int ubase = a.ws_pref[u], uend = a.ws_pref[u + 1];
+  // first and last column, each non-empty; (1, 0) for an empty unit
+  const int2 kc = *reinterpret_cast<const int2*>(&a.ws_cols[2 * u]);
+  const int k0 = kc.x, k1 = kc.y;
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
-  if (uend == ubase) {
+  if (k1 < k0) {
     if (threadIdx.x < kHeadDim) a.out[(head0 + j) * kHeadDim + threadIdx.x] = 0;
     if (threadIdx.x == 0 && a.lse) a.lse[head0 + j] = -INFINITY;
     return;
   }
-  const int k0 = a.ws_cols[2 * u], k1 = a.ws_cols[2 * u + 1];  // columns, each non-empty
   if (k0 == k1) return;  // one item covered the pair and wrote the output
   merge_head<KIND, G, ROWS>(a, head0, j, (int64_t)(k0 + u) * LH + h, LH, k1 - k0 + 1);
 }
@@ -1516,23 +1513,21 @@ int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles) {
   return (int)std::max<int64_t>(1, std::min(cap, need));
 }
 
-size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_pref) {
+size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_cols) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  return up((size_t)slots * G * kHeadDim * 4) + up((size_t)slots * G * 2 * 4) + up((size_t)n_pref * 4);
+  return up((size_t)slots * G * kHeadDim * 4) + up((size_t)slots * G * 2 * 4) + up((size_t)n_cols * 4);
 }
 
-bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_pref,
+bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_cols,
                           AttnArgs* a) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  if (ws_bytes < attn_workspace_bytes(slots, G, n_pref) || ws == nullptr) return false;
+  if (ws_bytes < attn_workspace_bytes(slots, G, n_cols) || ws == nullptr) return false;
   char* p = static_cast<char*>(ws);
   a->ws_o = reinterpret_cast<float*>(p);
   p += up((size_t)slots * G * kHeadDim * 4);
   a->ws_ml = reinterpret_cast<float*>(p);
   p += up((size_t)slots * G * 2 * 4);
-  a->ws_pref = n_pref > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;
-  // balanced: the units' column ranges follow the prefix (n_pref = 3 n_units + 1)
-  a->ws_cols = n_pref > 0 ? a->ws_pref + (n_pref - 1) / 3 + 1 : nullptr;
+  a->ws_cols = n_cols > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;  // 256-byte aligned
   return true;
 }
 

@@ -46,8 +46,8 @@ struct AttnArgs {
   float* lse;
   float* ws_o;                  // [slots, G, 128] unnormalised partial outputs
   float* ws_ml;                 // [slots, G, 2] partial (max, sum) in log2 units
-  int32_t* ws_pref;             // balanced: [n_units + 1] first tile of each unit
   int32_t* ws_cols;             // balanced: [n_units][2] first and last column of each unit
+                                // ((1, 0) for an empty unit), written by the main kernel
   int B, Hq, Hkv, G;
   int S;                        // dense: rows per sequence; ragged: token rows T;
                                 // paged: pages P in the pool
@@ -69,11 +69,11 @@ struct AttnArgs {
   int kv8;                      // K and V are e4m3 codes, one byte per element
 };
 
-// Bytes of workspace for `slots` partials of group size G plus n_pref ints.
-size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_pref);
-// Carves ws into the partial-output, partial-(max, sum) and prefix regions;
-// returns false if ws_bytes is too small.
-bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_pref,
+// Bytes of workspace for `slots` partials of group size G plus n_cols ints.
+size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_cols);
+// Carves ws into the partial-output, partial-(max, sum) and column-range
+// regions; returns false if ws_bytes is too small.
+bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_cols,
                           AttnArgs* a);
 // Whether the balanced schedule puts each column's workgroups on one XCD:
 // line_heads = 4m with m >= 4, n_blocks <= n_cu and a multiple of 8m.
