@@ -121,6 +121,22 @@ def test_wide_tiles_shortest_k(w_layout):
     _check_rows(d, kc, vc, rows=rows)
 
 
+@pytest.mark.parametrize("w_layout", LAYOUTS)
+def test_wide_tiles_beyond_one_round(w_layout):
+    """b*l = 40000 rows and h = 256: 157 x 2 tiles of 256 x 256 (the last row
+    tile holds 64 rows), more than one round of one workgroup per CU, with
+    four K steps.  Two rows of every row tile are checked, all columns."""
+    d = kvgen.kvpr_layer(seed=19, b=5, h=256, H=2, s=8008, l=8000)
+    say(f"[recompute] b=5 l=8000 h=256 (314 tiles, 4 K steps) w_layout={w_layout}")
+    kc, vc = recompute_on_gpu(d, w_layout)
+    rng = np.random.default_rng(20)
+    band = np.arange(0, 40000, 256)
+    inside = np.concatenate([band + rng.integers(0, 256, band.size), band + 255])
+    edges = [0, 7999, 8000, 39935, 39936, 39999]
+    rows = np.unique(np.concatenate([edges, np.minimum(inside, 39999)])).astype(np.int32)
+    _check_rows(d, kc, vc, rows=rows)
+
+
 def test_end_to_end_against_fp64_recompute():
     d = kvgen.kvpr_layer(seed=4, b=2, h=1024, H=8, s=200, l=120)
     say("[recompute] end to end vs fp64 X.W")
