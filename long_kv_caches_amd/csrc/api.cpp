@@ -183,6 +183,7 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->n_units = p.n_units;
   a->n_cu = p.n_cu;
   a->xcd_cols = p.mode == MODE_BALANCED && balanced_xcd_cols(p.line_heads, p.n_blocks, p.n_cu);
+  a->xcd_w = a->xcd_cols ? balanced_odd_xcd_weight(p.line_heads) : 100;
   a->kv8 = d->kv_format == KVDEC_KV_E4M3;
   // e4m3 K: scale * q . (k_scale * code) = (scale * k_scale) * q . code
   a->scale_log2 = (float)((double)d->softmax_scale * (a->kv8 ? (double)d->k_scale : 1.0) *

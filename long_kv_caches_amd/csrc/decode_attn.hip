@@ -1110,15 +1110,14 @@ struct ItemLine {
 };
 
 // Which column and line head a wave runs.  With a.xcd_cols set (the host sets
-// it when a column's LH waves fill m >= 4 whole workgroups, LH = 4m as with
-// 32 KV heads, and the grid is one dispatch round, at most one workgroup per
-// CU, of whole groups of 8m workgroups) the m workgroups of a column are on
-// one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs column
-// 8 (t / m) + x for heads 4 (t % m) ...  Otherwise wave w = 4b + i runs
-// column w / LH for head w % LH.  (Measured on MI355X: on the paged 1024 x
-// 32-head batch, one XCD per column 3376 -> 3361 us, and with odd XCDs
-// weighted 0.90, 3312 us; the 8-head headline gained nothing from either,
-// and e4m3, at three workgroups per CU, lost 1-2 us.)
+// it when a column's LH waves fill m >= 2 whole workgroups, LH = 4m as with 8
+// or 32 KV heads, and the grid is one dispatch round, at most one workgroup
+// per CU, of whole groups of 8m workgroups) the m workgroups of a column are
+// on one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs
+// column 8 (t / m) + x for heads 4 (t % m) ...  Otherwise wave w = 4b + i
+// runs column w / LH for head w % LH.  (Measured on MI355X: on the paged
+// 1024 x 32-head batch, one XCD per column 3376 -> 3361 us, and with odd XCDs
+// weighted 0.90, 3312 us; e4m3, at three workgroups per CU, lost 1-2 us.)
 struct ColumnOf {
   int col, head;
 };
@@ -1146,8 +1145,9 @@ __device__ __forceinline__ ColumnOf column_of(const AttnArgs& a, int LH) {
 // simulation on the measured per-wave rates).  Waves on odd-numbered XCDs
 // stream slower than those on even ones (measured on MI355X with one
 // workgroup per CU: 0.94-0.98 against 1.00-1.06 of the mean on the CLO
-// hybrid), so where a column's waves share one XCD (a.xcd_cols, column_of),
-// columns on odd XCDs get kOddXcdWeight / 100 as much.  At
+// hybrid, and on the 16 x 16K-32K batch whatever heads they run), so where a
+// column's waves share one XCD (a.xcd_cols, column_of), columns on odd XCDs
+// get a.xcd_w / 100 as much.  At
 // most N columns, and equal weights below 2 tiles per column, so that no
 // column is empty.
 __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) {
@@ -1161,7 +1161,7 @@ __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) 
   // the XCD weight where a column's waves share one XCD and every column
   // runs in the first dispatch round
   L.xcd_cols = a.xcd_cols != 0;  // column c on XCD c % 8
-  L.wo = weighted && L.xcd_cols ? kOddXcdWeight : 100;
+  L.wo = weighted && L.xcd_cols ? a.xcd_w : 100;
   L.total = L.cum(L.Wc);
   return L;
 }

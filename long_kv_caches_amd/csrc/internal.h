@@ -20,7 +20,6 @@ constexpr int kMaxGroup = 8;      // query heads per KV head handled by one work
 constexpr int kMaxUnits = 4096;   // tile-line units (sequences, or hybrid pairs) of the balanced schedule
 constexpr int kMinTilesPerWave = 8;
 constexpr int kFirstRoundWeight = 113;  // balanced: per 100, share of a first-round column
-constexpr int kOddXcdWeight = 90;       // balanced: per 100, share of a column on an odd XCD
 
 // Tile schedules of the attention kernels.
 enum Mode : int { MODE_CHUNKS = 0, MODE_BALANCED = 1 };
@@ -62,6 +61,7 @@ struct AttnArgs {
   int n_cu;                     // balanced: CUs of the device (workgroups of the first round)
   int n_units;                  // balanced: units of the tile line
   int xcd_cols;                 // balanced: each column's workgroups on one XCD (column c on XCD c % 8)
+  int xcd_w;                    // balanced, xcd_cols: per 100, the share of a column on an odd XCD
   float scale_log2;             // softmax_scale * log2(e) (* k_scale for e4m3 K)
   float out_scale;              // e4m3 V: v_scale, applied with the final normalisation
   int src;
@@ -76,11 +76,19 @@ size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_cols);
 bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_cols,
                           AttnArgs* a);
 // Whether the balanced schedule puts each column's workgroups on one XCD:
-// line_heads = 4m with m >= 4, n_blocks <= n_cu and a multiple of 8m.
+// line_heads = 4m with m >= 2, n_blocks <= n_cu and a multiple of 8m.
 inline bool balanced_xcd_cols(int line_heads, int n_blocks, int n_cu) {
   const int m = line_heads / kWaves;
-  return line_heads % kWaves == 0 && m >= 4 && n_blocks % (8 * m) == 0 && n_blocks <= n_cu;
+  return line_heads % kWaves == 0 && m >= 2 && n_blocks % (8 * m) == 0 && n_blocks <= n_cu;
 }
+// With columns on one XCD, per 100, the share of a column on an odd XCD:
+// 0.90 for columns of eight or more workgroups (32 KV heads), 0.95 for two
+// (8 KV heads).  Measured on MI355X, one process, interleaved, main kernel:
+// the paged 1024 x 32-head batch 3342 / 3326 / 3312 us at 0.96 / 0.93 / 0.90;
+// the 16 x 16K-32K batch with 8 KV heads 1.9-2.6 us shorter at 0.95 than
+// with columns across XCDs, on three boxes, and 0.3 us longer to 0.3 us
+// shorter with one XCD per column and equal weights.
+inline int balanced_odd_xcd_weight(int line_heads) { return line_heads / kWaves >= 4 ? 90 : 95; }
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
 int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);

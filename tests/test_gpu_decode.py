@@ -146,6 +146,14 @@ def test_ragged_mha_columns_on_one_xcd():
     _parity(d, "ragged MHA 8 sequences x 32 heads")
 
 
+@pytest.mark.parametrize("hq", [8, 32, 64])  # G = 1, 4 (vector path) and 8 (matrix cores)
+def test_ragged_gqa_columns_on_one_xcd(hq):
+    # 8 KV heads with enough tiles for a full one-workgroup-per-CU grid: each
+    # column's two workgroups run on one XCD, with odd XCDs' columns weighted
+    d = kvgen.ragged_llama(seed=25, lens=[4100, 3000, 17, 2222], Hq=hq, Hkv=8)
+    _parity(d, f"ragged 4 sequences x {hq}/8 heads")
+
+
 @pytest.mark.parametrize("hq,hkv,layout,bf16", [
     (40, 40, "dense", False),   # OPT-13B's 40 heads: 25 columns of 40 on 1024 waves
     (40, 40, "paged", False),
