@@ -1114,7 +1114,9 @@ struct ItemLine {
 // or 32 KV heads, and the grid is one dispatch round, at most one workgroup
 // per CU, of whole groups of 8m workgroups) the m workgroups of a column are
 // on one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs
-// column 8 (t / m) + x for heads 4 (t % m) ...  Otherwise wave w = 4b + i
+// column 8 (t / m) + x for heads 4 (t % m) ...; with one head per column
+// (LH = 1: the hybrid and gather sources, or a single KV head) wave i of
+// block b = 8t + x runs column 8 (4t + i) + x.  Otherwise wave w = 4b + i
 // runs column w / LH for head w % LH.  (Measured on MI355X: on the paged
 // 1024 x 32-head batch, one XCD per column 3376 -> 3361 us, and with odd XCDs
 // weighted 0.90, 3312 us; e4m3, at three workgroups per CU, lost 1-2 us.)
@@ -1124,7 +1126,11 @@ struct ColumnOf {
 __device__ __forceinline__ ColumnOf column_of(const AttnArgs& a, int LH) {
   ColumnOf c;
   const int b = (int)blockIdx.x, wave = (int)(threadIdx.x >> 6);
-  if (a.xcd_cols) {
+  if (a.xcd_cols && LH == 1) {  // four columns per workgroup: 8 (4t + i) + x
+    const int x = b % 8, t = b / 8;
+    c.col = (t * kWaves + wave) * 8 + x;
+    c.head = 0;
+  } else if (a.xcd_cols) {
     const int m = LH / kWaves, x = b % 8, t = b / 8;
     c.col = (t / m) * 8 + x;
     c.head = (t % m) * kWaves + wave;

@@ -75,20 +75,26 @@ size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_cols);
 // regions; returns false if ws_bytes is too small.
 bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_cols,
                           AttnArgs* a);
-// Whether the balanced schedule puts each column's workgroups on one XCD:
-// line_heads = 4m with m >= 2, n_blocks <= n_cu and a multiple of 8m.
+// Whether the balanced schedule puts each column's waves on one XCD, with
+// column c on XCD c % 8: a one-round grid (n_blocks <= n_cu) and either
+// line_heads = 4m, m >= 2, with n_blocks a multiple of 8m, or line_heads 1
+// (a column per wave) with n_blocks a multiple of 8.
 inline bool balanced_xcd_cols(int line_heads, int n_blocks, int n_cu) {
+  if (n_blocks > n_cu) return false;
+  if (line_heads == 1) return n_blocks % 8 == 0;
   const int m = line_heads / kWaves;
-  return line_heads % kWaves == 0 && m >= 2 && n_blocks % (8 * m) == 0 && n_blocks <= n_cu;
+  return line_heads % kWaves == 0 && m >= 2 && n_blocks % (8 * m) == 0;
 }
 // With columns on one XCD, per 100, the share of a column on an odd XCD:
-// 0.90 for columns of eight or more workgroups (32 KV heads), 0.95 for two
-// (8 KV heads).  Measured on MI355X, one process, interleaved, main kernel:
-// the paged 1024 x 32-head batch 3342 / 3326 / 3312 us at 0.96 / 0.93 / 0.90;
-// the 16 x 16K-32K batch with 8 KV heads 1.9-2.6 us shorter at 0.95 than
-// with columns across XCDs, on three boxes, and 0.3 us longer to 0.3 us
-// shorter with one XCD per column and equal weights.
-inline int balanced_odd_xcd_weight(int line_heads) { return line_heads / kWaves >= 4 ? 90 : 95; }
+// 0.95 for columns of two workgroups (8 KV heads), else 0.90 (eight or more
+// workgroups, or one wave).  Measured on MI355X, one process, interleaved,
+// main kernel: the paged 1024 x 32-head batch 3342 / 3326 / 3312 us at
+// 0.96 / 0.93 / 0.90; the 16 x 16K-32K batch with 8 KV heads 1.9-2.6 us
+// shorter at 0.95 than with columns across XCDs, on three boxes, and 0.3 us
+// longer to 0.3 us shorter with one XCD per column and equal weights; the CLO
+// hybrids (a column per wave) 0.2-1.4 us shorter at 0.90 (whole calls
+// 0.7-1.1 us) on three boxes, and about 0.5 us longer with equal weights.
+inline int balanced_odd_xcd_weight(int line_heads) { return line_heads == 2 * kWaves ? 95 : 90; }
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
 int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);

@@ -154,6 +154,17 @@ def test_ragged_gqa_columns_on_one_xcd(hq):
     _parity(d, f"ragged 4 sequences x {hq}/8 heads")
 
 
+@pytest.mark.parametrize("layout", ["ragged", "dense"])
+def test_one_kv_head_columns_on_one_xcd(layout):
+    # one KV head (a column per wave) with enough tiles for a full
+    # one-workgroup-per-CU grid: wave i of block 8t + x runs column
+    # 8 (4t + i) + x, with odd XCDs' columns weighted
+    d = kvgen.ragged_llama(seed=26, lens=[32768, 20000, 1, 31000], Hq=4, Hkv=1)
+    if layout == "dense":
+        d = kvgen.ragged_to_dense(d)
+    _parity(d, f"{layout} 4 sequences x 4/1 heads, up to 32K")
+
+
 @pytest.mark.parametrize("hq,hkv,layout,bf16", [
     (40, 40, "dense", False),   # OPT-13B's 40 heads: 25 columns of 40 on 1024 waves
     (40, 40, "paged", False),
