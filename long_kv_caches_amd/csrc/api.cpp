@@ -49,6 +49,7 @@ struct Plan {
   int chunk, n_chunks;    // chunks
   int n_blocks, n_units;  // balanced
   int n_cu;               // balanced
+  int xcd_rounds;         // balanced: dispatch rounds (workgroups per CU) that allow XCD-local columns
   int64_t max_items;      // balanced: columns of the line
   int line_heads;         // balanced: heads run per line item
 };
@@ -73,6 +74,11 @@ static Plan plan_attn(int dtype, int kv8, int G, int src, int64_t pairs, int64_t
     p.n_blocks = (int)std::max<int64_t>(balanced_blocks(dtype, kv8, G, src, est_tiles),
                                         (LH + kWaves - 1) / kWaves);
     p.n_cu = device_cu_count();
+    // XCD-local columns with one workgroup per CU, and with two for bf16 K/V
+    // read from runs (measured on MI355X, one process, interleaved: the
+    // 16 x 16K-32K batch in bf16, two workgroups per CU, 2.4-2.9 us shorter;
+    // e4m3 and gathered rows, also at two, 0.7-1.5 us longer)
+    p.xcd_rounds = dtype == KVDEC_BF16 && !kv8 && src != SRC_GATHER ? 2 : 1;
     // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
     p.max_items = (int64_t)p.n_blocks * kWaves / std::max<int64_t>(LH, 1);
     p.line_heads = (int)LH;
@@ -182,7 +188,8 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->n_blocks = p.n_blocks;
   a->n_units = p.n_units;
   a->n_cu = p.n_cu;
-  a->xcd_cols = p.mode == MODE_BALANCED && balanced_xcd_cols(p.line_heads, p.n_blocks, p.n_cu);
+  a->xcd_cols = p.mode == MODE_BALANCED &&
+                balanced_xcd_cols(p.line_heads, p.n_blocks, p.n_cu * p.xcd_rounds);
   a->xcd_w = a->xcd_cols ? balanced_odd_xcd_weight(p.line_heads) : 100;
   a->kv8 = d->kv_format == KVDEC_KV_E4M3;
   // e4m3 K: scale * q . (k_scale * code) = (scale * k_scale) * q . code

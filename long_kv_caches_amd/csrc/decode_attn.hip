@@ -1164,8 +1164,8 @@ __device__ __forceinline__ ItemLine item_line(const AttnArgs& a, int N, int LH) 
   const bool weighted = N >= 2 * L.Wc;
   L.w0 = weighted ? kFirstRoundWeight : 100;
   L.w1 = 100;
-  // the XCD weight where a column's waves share one XCD and every column
-  // runs in the first dispatch round
+  // the XCD weight where a column's waves share one XCD (with more than one
+  // dispatch round it multiplies the first-round weight)
   L.xcd_cols = a.xcd_cols != 0;  // column c on XCD c % 8
   L.wo = weighted && L.xcd_cols ? a.xcd_w : 100;
   L.total = L.cum(L.Wc);

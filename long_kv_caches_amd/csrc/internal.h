@@ -76,11 +76,12 @@ size_t attn_workspace_bytes(int64_t slots, int G, int64_t n_cols);
 bool attn_workspace_carve(void* ws, size_t ws_bytes, int64_t slots, int G, int64_t n_cols,
                           AttnArgs* a);
 // Whether the balanced schedule puts each column's waves on one XCD, with
-// column c on XCD c % 8: a one-round grid (n_blocks <= n_cu) and either
+// column c on XCD c % 8: n_blocks <= max_blocks (the CUs times the dispatch
+// rounds allowed) and either
 // line_heads = 4m, m >= 2, with n_blocks a multiple of 8m, or line_heads 1
 // (a column per wave) with n_blocks a multiple of 8.
-inline bool balanced_xcd_cols(int line_heads, int n_blocks, int n_cu) {
-  if (n_blocks > n_cu) return false;
+inline bool balanced_xcd_cols(int line_heads, int n_blocks, int max_blocks) {
+  if (n_blocks > max_blocks) return false;
   if (line_heads == 1) return n_blocks % 8 == 0;
   const int m = line_heads / kWaves;
   return line_heads % kWaves == 0 && m >= 2 && n_blocks % (8 * m) == 0;

@@ -154,6 +154,14 @@ def test_ragged_gqa_columns_on_one_xcd(hq):
     _parity(d, f"ragged 4 sequences x {hq}/8 heads")
 
 
+@pytest.mark.parametrize("hq", [8, 32])
+def test_bf16_columns_on_one_xcd_two_workgroups_per_cu(hq):
+    # bf16 K/V with enough tiles for two workgroups per CU: XCD-local columns
+    # with the first-round and odd-XCD weights together
+    d = kvgen.ragged_llama(seed=27, lens=[8200, 5000, 17, 3000], Hq=hq, Hkv=8)
+    _parity(d, f"ragged bf16 4 sequences x {hq}/8 heads", bf16=True)
+
+
 @pytest.mark.parametrize("layout", ["ragged", "dense"])
 def test_one_kv_head_columns_on_one_xcd(layout):
     # one KV head (a column per wave) with enough tiles for a full
