@@ -7,7 +7,9 @@ heads per KV head (1 to 8, so both the vector and the matrix-core tile paths),
 the batch (1 to 6 sequences) and each sequence's length (empty, one token,
 tile edges, or up to 2500 tokens), and the schedule (the persistent default
 or fixed chunks of 64 to 320 tokens).  The case is printed before it runs.
-The tolerances are those of every other parity test (tests/gpu_util.py).
+A second sweep draws batches large enough for a full persistent grid, where
+the columns are placed by XCD (1, 8 or 32 KV heads, fp16 or bf16).  The
+tolerances are those of every other parity test (tests/gpu_util.py).
 """
 import numpy as np
 import pytest
@@ -163,3 +165,42 @@ def test_gather_sweep(i):
                                 scale=d["scale"], kind=oracle.BF16 if bf16 else oracle.F16)
     check_close(go, ro, f"gather sweep {i}", bf16_out=bf16)
     check_lse(gl, rl, f"gather sweep {i} lse")
+
+
+# ---------------------------------------------------------------------------
+# Grids of one or two workgroups per CU whose columns are placed by XCD
+# ---------------------------------------------------------------------------
+
+N_XCD = 10
+
+
+def draw_xcd_case(i):
+    """Batches with enough tiles that the default plan fills a full grid
+    (est. tiles >= 32 per persistent workgroup): 1, 8 or 32 KV heads (a column
+    of one wave, two or eight workgroups), fp16 or bf16, any layout."""
+    rng = np.random.default_rng(90_000 + i)
+    hkv = int(rng.choice([1, 8, 32]))
+    g = int(rng.integers(1, 9 if hkv < 32 else 3))
+    bf16 = bool(rng.random() < 0.3)
+    b = int(rng.integers(2, 6))
+    need = (16384 if bf16 else 8192) * 16 // (b * hkv)  # tokens of the longest sequence
+    top = int(need + rng.integers(0, need // 4 + 1))
+    lens = [top] + [int(x) if rng.random() > 0.3 else int(rng.choice([0, 1, 17, top]))
+                    for x in rng.integers(0, top + 1, size=b - 1)]
+    layout = str(rng.choice(["ragged", "dense", "paged"]))
+    return dict(hkv=hkv, g=g, bf16=bf16, lens=lens, layout=layout, seed=91_000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_XCD))
+def test_xcd_columns_sweep(i):
+    c = draw_xcd_case(i)
+    say(f"[xcd sweep {i}] {c}")
+    d = kvgen.ragged_llama(seed=c["seed"], lens=c["lens"], Hq=c["g"] * c["hkv"], Hkv=c["hkv"])
+    if c["layout"] == "dense":
+        d = kvgen.ragged_to_dense(d)
+    elif c["layout"] == "paged":
+        d = kvgen.ragged_to_paged(d, seed=c["seed"] + 1)
+    out, lse = decode_on_gpu(d, split_tokens=0, bf16=c["bf16"])
+    ref_o, ref_l = reference(d, c["bf16"])
+    check_close(host_f64(out), ref_o, f"xcd sweep {i}", bf16_out=c["bf16"])
+    check_lse(lse, ref_l, f"xcd sweep {i} lse")
