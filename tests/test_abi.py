@@ -101,7 +101,7 @@ def test_workspace_sizes():
     # fixed chunks covering each sequence in one item need no partials
     small = _desc(max_seqlen=100, split_tokens=128)
     assert K.kvdec_decode_attn_workspace(small) == 0
-    # the balanced schedule always keeps its tile-line prefix and partial slots
+    # the balanced schedule always keeps its per-unit column table and partial slots
     assert K.kvdec_decode_attn_workspace(_desc(max_seqlen=100)) > 0
     d = _desc(batch=16, num_q_heads=32, num_kv_heads=8, max_seqlen=32768, kv_rows=393216,
               split_tokens=512)
