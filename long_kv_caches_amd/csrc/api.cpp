@@ -50,6 +50,7 @@ struct Plan {
   int n_blocks, n_units;  // balanced
   int n_cu;               // balanced
   int xcd_rounds;         // balanced: dispatch rounds (workgroups per CU) that allow XCD-local columns
+  int xcd_w;              // balanced: per 100, the share of a column on an odd XCD, if XCD-local
   int64_t max_items;      // balanced: columns of the line
   int line_heads;         // balanced: heads run per line item
 };
@@ -82,6 +83,7 @@ static Plan plan_attn(int dtype, int kv8, int G, int src, int64_t pairs, int64_t
     // Wc = W / LH columns of the line, slots (column + unit) * LH + h.
     p.max_items = (int64_t)p.n_blocks * kWaves / std::max<int64_t>(LH, 1);
     p.line_heads = (int)LH;
+    p.xcd_w = balanced_odd_xcd_weight(p.line_heads, src);
     return p;
   }
   p.mode = MODE_CHUNKS;
@@ -190,7 +192,7 @@ static void fill_common(const kvdec_attn_desc* d, const Plan& p, AttnArgs* a) {
   a->n_cu = p.n_cu;
   a->xcd_cols = p.mode == MODE_BALANCED &&
                 balanced_xcd_cols(p.line_heads, p.n_blocks, p.n_cu * p.xcd_rounds);
-  a->xcd_w = a->xcd_cols ? balanced_odd_xcd_weight(p.line_heads) : 100;
+  a->xcd_w = a->xcd_cols ? p.xcd_w : 100;
   a->kv8 = d->kv_format == KVDEC_KV_E4M3;
   // e4m3 K: scale * q . (k_scale * code) = (scale * k_scale) * q . code
   a->scale_log2 = (float)((double)d->softmax_scale * (a->kv8 ? (double)d->k_scale : 1.0) *

@@ -87,15 +87,22 @@ inline bool balanced_xcd_cols(int line_heads, int n_blocks, int max_blocks) {
   return line_heads % kWaves == 0 && m >= 2 && n_blocks % (8 * m) == 0;
 }
 // With columns on one XCD, per 100, the share of a column on an odd XCD:
-// 0.95 for columns of two workgroups (8 KV heads), else 0.90 (eight or more
-// workgroups, or one wave).  Measured on MI355X, one process, interleaved,
-// main kernel: the paged 1024 x 32-head batch 3342 / 3326 / 3312 us at
-// 0.96 / 0.93 / 0.90; the 16 x 16K-32K batch with 8 KV heads 1.9-2.6 us
+// 0.95 for columns of two workgroups (8 KV heads), 0.87 for eight or more
+// workgroups reading pages (32 KV heads, paged), else 0.90 (eight or more
+// workgroups reading runs, or one wave).  Measured on MI355X, one process,
+// interleaved, main kernel: the paged 1024 x 32-head batch 3342 / 3326 /
+// 3312 us at 0.96 / 0.93 / 0.90, and at 0.88 / 0.87 / 0.86 / 0.84 10 / 15 /
+// 19 / 12 us shorter than at 0.90 (whole calls at 0.87: 18 us), where the
+// same batch laid out ragged was 3 / 8-12 / 23 us longer at 0.88 / 0.87 /
+// 0.86; the 16 x 16K-32K batch with 8 KV heads 1.9-2.6 us
 // shorter at 0.95 than with columns across XCDs, on three boxes, and 0.3 us
 // longer to 0.3 us shorter with one XCD per column and equal weights; the CLO
 // hybrids (a column per wave) 0.2-1.4 us shorter at 0.90 (whole calls
 // 0.7-1.1 us) on three boxes, and about 0.5 us longer with equal weights.
-inline int balanced_odd_xcd_weight(int line_heads) { return line_heads == 2 * kWaves ? 95 : 90; }
+inline int balanced_odd_xcd_weight(int line_heads, int src) {
+  if (line_heads == 2 * kWaves) return 95;
+  return line_heads >= 4 * kWaves && src == SRC_PAGED ? 87 : 90;
+}
 // Persistent workgroups for the balanced schedule on the current device:
 // CUs x resident workgroups per CU, fewer when est_tiles is small.
 int balanced_blocks(int dtype, int kv8, int G, int src, int64_t est_tiles);
