@@ -51,8 +51,12 @@ __device__ __forceinline__ u32x2 buffer_load_b64_nt(__amdgpu_buffer_rsrc_t r, ui
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2);
 }
 
+// 16-byte global store.  `nt` marks data no kernel of the call reads back
+// as non-temporal.
+template <bool NT = false>
 __device__ __forceinline__ void store_b128(void* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = v;
 }
 
 // Low / high 16-bit element of a packed pair, widened to fp32.
