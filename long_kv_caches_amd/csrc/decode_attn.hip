@@ -29,9 +29,11 @@
 //
 // Two schedules distribute the tiles:
 //   balanced (default) -- a persistent grid of CUs x occupancy workgroups.
-//     The tile line (one KV head of every sequence) is cut into equal
-//     columns; wave k * Hkv + h runs column k for head h, so waves that run
-//     together read all heads of the same token rows.  A wave streams its
+//     The tile line (one KV head of every sequence) is cut into columns;
+//     column k is run for every head h by one wave each, so waves that run
+//     together read all heads of the same token rows.  On a full grid a
+//     column's waves share one XCD, and columns on the slower odd XCDs get
+//     fewer tiles (column_of, item_line).  A wave streams its
 //     column as one sequence of tiles (the next tile's loads are issued
 //     across pair boundaries) and writes one partial per pair it touches, or
 //     the final output when it covers a whole pair.  Its priority steps down
@@ -1111,9 +1113,9 @@ struct ItemLine {
 
 // Which column and line head a wave runs.  With a.xcd_cols set (the host sets
 // it when a column's LH waves fill m >= 2 whole workgroups, LH = 4m as with 8
-// or 32 KV heads, and the grid is one dispatch round, at most one workgroup
-// per CU, of whole groups of 8m workgroups) the m workgroups of a column are
-// on one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs
+// or 32 KV heads, and the grid holds at most one workgroup per CU, two for
+// bf16 K/V read from runs, in whole groups of 8m workgroups) the m workgroups
+// of a column are on one XCD (workgroups go to the 8 XCDs in turn): block b = 8t + x runs
 // column 8 (t / m) + x for heads 4 (t % m) ...; with one head per column
 // (LH = 1: the hybrid and gather sources, or a single KV head) wave i of
 // block b = 8t + x runs column 8 (4t + i) + x.  Otherwise wave w = 4b + i
