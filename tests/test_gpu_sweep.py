@@ -21,7 +21,7 @@ from test_gpu_decode import ORC_LAYOUT
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 80
 EDGE_LENGTHS = [0, 1, 15, 16, 17, 63, 64, 65]
 
 
@@ -83,7 +83,7 @@ def test_decode_sweep(i):
 # CLO hybrid attention: persistent slots and cache-buffer heads
 # ---------------------------------------------------------------------------
 
-N_HYBRID = 24
+N_HYBRID = 40
 
 
 def draw_hybrid(i):
@@ -139,7 +139,7 @@ def test_hybrid_sweep(i):
 # Index-gather attention over a dense cache
 # ---------------------------------------------------------------------------
 
-N_GATHER = 16
+N_GATHER = 24
 
 
 @pytest.mark.parametrize("i", range(N_GATHER))
@@ -171,7 +171,7 @@ def test_gather_sweep(i):
 # Grids of one or two workgroups per CU whose columns are placed by XCD
 # ---------------------------------------------------------------------------
 
-N_XCD = 10
+N_XCD = 24
 
 
 def draw_xcd_case(i):
